@@ -1,0 +1,175 @@
+"""CPU oracle for the per-rank ZeRO shard step.
+
+TEST INFRASTRUCTURE ONLY.  This package is the plain, slow, obviously correct
+definition the GPU path is checked against: ``zo.c`` (the step, the M-way
+reduce, the fp64 norm, bf16 conversion) and ``layout.py`` (the flat bucket /
+shard layout).  Only the test suite, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import it.  The product library never
+imports, links or calls anything here, and nothing here imports the product.
+
+Every function here is pinned by tests under ``tests/`` against closed forms,
+invariants, library routines (torch AdamW, clip_grad_norm_, torch bf16
+conversion) and the pages' worked numbers; see the test modules named
+``test_oracle_*``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import layout  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(_HERE, "libzo.so")
+SOURCES = [os.path.join(_HERE, "zo.c")]
+CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+          "-fno-fast-math", "-Wall", "-Wextra"]
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile zo.c into libzo.so with gcc (no FMA contraction, no fast-math)."""
+    import subprocess
+    cmd = ["gcc", *CFLAGS, "-o", LIB + ".tmp", *SOURCES, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            raise RuntimeError(f"{LIB} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB)
+        vp, i64, i32, f32, f64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                  ctypes.c_float, ctypes.c_double)
+        L.zo_bf16_to_f32_array.argtypes = [i64, vp, vp]
+        L.zo_bf16_to_f32_array.restype = None
+        L.zo_f32_to_bf16_array.argtypes = [i64, vp, vp]
+        L.zo_f32_to_bf16_array.restype = None
+        L.zo_set_threads.argtypes = [i32]
+        L.zo_set_threads.restype = None
+        L.zo_get_threads.argtypes = []
+        L.zo_get_threads.restype = i32
+        L.zo_scalars_f32_get.argtypes = [f32, f32, f32, f32, f32, i64, vp]
+        L.zo_scalars_f32_get.restype = None
+        L.zo_reduce_mean_f32.argtypes = [i64, i32, vp, vp]
+        L.zo_reduce_mean_f32.restype = None
+        L.zo_grad_sumsq.argtypes = [i64, i32, vp]
+        L.zo_grad_sumsq.restype = f64
+        L.zo_clip_coef.argtypes = [f64, f32]
+        L.zo_clip_coef.restype = f32
+        L.zo_step_f32.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, f32, f32, f32, f32, f32,
+                                  i64, i32, f32]
+        L.zo_step_f32.restype = i32
+        L.zo_step_f64.argtypes = [i64, i32, vp, vp, vp, vp, vp, f64, f64, f64, f64, f64, i64,
+                                  i32, f64]
+        L.zo_step_f64.restype = i32
+        _lib = L
+    return _lib
+
+
+def set_threads(n: int) -> None:
+    lib().zo_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().zo_get_threads())
+
+
+def _ptr_array(arrays):
+    arr = (ctypes.c_void_p * len(arrays))(*[a.ctypes.data for a in arrays])
+    return arr
+
+
+def _grads_u16(grads):
+    gs = [np.ascontiguousarray(g, dtype=np.uint16) for g in grads]
+    n = gs[0].size
+    if any(g.size != n for g in gs):
+        raise ValueError("gradient contributions differ in length")
+    return gs, n
+
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.size, dtype=np.float32)
+    lib().zo_bf16_to_f32_array(h.size, h.ctypes.data, out.ctypes.data)
+    return out.reshape(h.shape)
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.size, dtype=np.uint16)
+    lib().zo_f32_to_bf16_array(x.size, x.ctypes.data, out.ctypes.data)
+    return out.reshape(x.shape)
+
+
+def step_scalars_f32(lr, beta1, beta2, eps, wd, t) -> dict:
+    out = np.empty(8, dtype=np.float32)
+    lib().zo_scalars_f32_get(lr, beta1, beta2, eps, wd, int(t), out.ctypes.data)
+    names = ["beta1", "beta2", "c1", "c2", "alpha", "bhat", "eps", "decay_mul"]
+    return dict(zip(names, out.tolist()))
+
+
+def reduce_mean_f32(grads) -> np.ndarray:
+    gs, n = _grads_u16(grads)
+    out = np.empty(n, dtype=np.float32)
+    lib().zo_reduce_mean_f32(n, len(gs), _ptr_array(gs), out.ctypes.data)
+    return out
+
+
+def grad_sumsq(grads) -> float:
+    gs, n = _grads_u16(grads)
+    return float(lib().zo_grad_sumsq(n, len(gs), _ptr_array(gs)))
+
+
+def clip_coef(sumsq: float, max_norm: float) -> np.float32:
+    return np.float32(lib().zo_clip_coef(float(sumsq), float(max_norm)))
+
+
+def step_f32(grads, master, m, v, param=None, decay=None, *, lr, beta1, beta2, eps,
+             weight_decay, step, coef=None):
+    """One fp32 oracle step, in place on master/m/v (float32 arrays); writes param
+    (uint16 bf16 patterns) when given.  coef: clip coefficient applied to g."""
+    gs, n = _grads_u16(grads)
+    for a in (master, m, v):
+        if a.dtype != np.float32 or not a.flags.c_contiguous or a.size != n:
+            raise ValueError("master/m/v must be contiguous float32 of the shard length")
+    if param is not None and (param.dtype != np.uint16 or param.size != n
+                              or not param.flags.c_contiguous):
+        raise ValueError("param must be contiguous uint16 of the shard length")
+    if decay is not None:
+        decay = np.ascontiguousarray(decay, dtype=np.uint8)
+        if decay.size != n:
+            raise ValueError("decay mask length")
+    rc = lib().zo_step_f32(n, len(gs), _ptr_array(gs), master.ctypes.data, m.ctypes.data,
+                           v.ctypes.data, None if param is None else param.ctypes.data,
+                           None if decay is None else decay.ctypes.data, lr, beta1, beta2, eps,
+                           weight_decay, int(step), 0 if coef is None else 1,
+                           0.0 if coef is None else float(coef))
+    if rc != 0:
+        raise ValueError("zo_step_f32 rejected its arguments")
+
+
+def step_f64(grads, master, m, v, decay=None, *, lr, beta1, beta2, eps, weight_decay, step,
+             coef=None):
+    """The same formula in fp64 (grads: list of float64 arrays), in place."""
+    gs = [np.ascontiguousarray(g, dtype=np.float64) for g in grads]
+    n = gs[0].size
+    for a in (master, m, v):
+        if a.dtype != np.float64 or not a.flags.c_contiguous or a.size != n:
+            raise ValueError("master/m/v must be contiguous float64")
+    if decay is not None:
+        decay = np.ascontiguousarray(decay, dtype=np.uint8)
+    rc = lib().zo_step_f64(n, len(gs), _ptr_array(gs), master.ctypes.data, m.ctypes.data,
+                           v.ctypes.data, None if decay is None else decay.ctypes.data, lr,
+                           beta1, beta2, eps, weight_decay, int(step),
+                           0 if coef is None else 1, 0.0 if coef is None else float(coef))
+    if rc != 0:
+        raise ValueError("zo_step_f64 rejected its arguments")
