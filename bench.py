@@ -1,0 +1,225 @@
+"""Benchmark of the fused per-rank ZeRO shard step on one MI355X.
+
+One "step" is one call of zero_shard_step over the rank's whole shard: the
+M-way bf16 gradient reduce, (optional clip,) the AdamW update of the fp32
+master and moments, and the bf16 re-cast -- every row of the hot path.  Inputs
+are seeded synthetic values already resident in HBM when timing starts; the
+gradient contributions of one batch are reused for every timed step.
+
+Prints one JSON line.  `value` is params/s over the shard (the whole job on
+one GPU); `roofline` prices the step kernel against MI355X's 8 TB/s HBM peak
+using the algorithmic bytes 2M+12 read + 14 written per parameter;
+`cpu_baseline` times the CPU oracle on a bounded slab of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload 1..5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused reduce+AdamW shard step: params/s and HBM GB/s as % of MI355X peak"
+PEAK_HBM_GBS = 8000.0
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "internal.h"):
+        with open(os.path.join(ROOT, "sharded_optimizer_step_zero_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(S: int, M: int, clip: bool) -> dict:
+    step = S * (2 * M + 12 + 14)
+    norm = S * 2 * M if clip else 0
+    return {"step_kernel": step, "norm_pass": norm, "total": step + norm}
+
+
+def traffic_for(workload_name: str):
+    """HBM bytes per launch of the step kernel from the committed counter summary,
+    or None when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"step_kernel_traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, slab: int, min_seconds: float = 10.0) -> dict:
+    """The CPU oracle, as it stands, on a slab of `slab` elements of the workload."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    threads = oracle.get_threads()
+    keys = w.grad_keys(0)
+    grads = [synth.host_grad_bf16(slab, k, ks, w.sigma_grad, w.kinds) for k, ks in keys]
+    p = synth.host_normal_f32(slab, w.master_key(), w.sigma_master)
+    m = np.zeros(slab, np.float32)
+    v = np.zeros(slab, np.float32)
+    b = np.zeros(slab, np.uint16)
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+    clip = w.max_grad_norm > 0
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        coef = oracle.clip_coef(oracle.grad_sumsq(grads), w.max_grad_norm) if clip else None
+        oracle.step_f32(grads, p, m, v, b, None, step=steps + 1, coef=coef, **hp)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": slab * steps / el, "unit": "params/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{steps} oracle steps over a {slab:,}-element slab of the shard "
+                      f"(M={w.M}{', with the norm pass' if clip else ''}), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2,
+                    help="1 tiny, 2 GPT-1.3B 1/8 shard (default), 3 Llama-6.7B, "
+                         "4 Llama-70B 1/16 shard, 5 stress with clip")
+    ap.add_argument("--chunk", type=int, default=0, help="chunk_elems of the plan (0: default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-slab", type=int, default=1 << 25)
+    ap.add_argument("--calibrate-copy-gib", type=float, default=1.0,
+                    help="size of the plain copy run once before timing (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the multi-GPU "
+                                   "exchange (reduce-scatter / all-gather) is not built",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from sharded_optimizer_step_zero_amd import ZeroShard
+    from synth.device_case import DeviceCase
+    from synth.workloads import workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = workload(args.workload)
+    t_setup = time.time()
+    zs = ZeroShard(w.numel, w.decay, w.world_size, w.rank, w.M, device=dev,
+                   bucket_cap=w.bucket_cap, align=w.align, chunk_elems=args.chunk)
+    pad = [(o, n) for o, n, t, _, _ in zs.segments() if t < 0]
+    case = DeviceCase(w, zs.shard_len, pad, dev)
+    case.fill_master(zs.master)
+    grads = case.fill_grads(0)
+    stream = torch.cuda.current_stream(dev)
+    zs.set_stream(stream.cuda_stream)
+
+    if args.calibrate_copy_gib > 0:
+        n = int(args.calibrate_copy_gib * (1 << 30)) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        synth.dev_copy(b, a)
+        del a, b
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+    clip = w.max_grad_norm > 0
+    for s in range(args.warmup):
+        zs.step(grads, step=s + 1, max_grad_norm=w.max_grad_norm, **hp)
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for s in range(args.steps):
+        zs.step(grads, step=args.warmup + s + 1, max_grad_norm=w.max_grad_norm, **hp)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+
+    # the step kernel alone (per-launch average): when clipping, the norm pass is
+    # timed separately and removed
+    step_kernel_ms = ms_per_step
+    if clip:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(args.steps):
+            zs.step(grads, step=s + 1, max_grad_norm=0.0, **hp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        step_kernel_ms = e0.elapsed_time(e1) / args.steps
+
+    S = zs.shard_len
+    by = algorithmic_bytes(S, w.M, clip)
+    achieved = by["step_kernel"] / (step_kernel_ms * 1e-3) / 1e9
+    traffic = traffic_for(w.name)
+
+    out = {
+        "metric": METRIC,
+        "value": S / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "description": w.description,
+            "shard_params": S,
+            "M": w.M,
+            "world_size": w.world_size,
+            "rank": w.rank,
+            "tensors": len(w.numel),
+            "clip": w.max_grad_norm if clip else None,
+            "bytes_per_param": 2 * w.M + 12 + 14 + (2 * w.M if clip else 0),
+            "hbm_gbs_whole_step": by["total"] / (ms_per_step * 1e-3) / 1e9,
+            "pct_of_peak_whole_step": 100.0 * by["total"] / (ms_per_step * 1e-3) / 1e9
+                                      / PEAK_HBM_GBS,
+            "wall_s_timed": wall,
+            "setup_s": setup_s,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "zs::step_kernel<M=%d>" % w.M,
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": by["step_kernel"],
+            "avg_launch_ms": step_kernel_ms,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_slab, S))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

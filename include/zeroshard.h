@@ -1,0 +1,207 @@
+/*
+ * zeroshard.h -- C ABI of the fused per-rank ZeRO shard step for MI355X (gfx950).
+ *
+ * What the library computes.  One data-parallel rank owns 1/N of the flat
+ * parameter space.  Per optimizer step it
+ *   (a) reduces M bf16 gradient contributions of its shard into their fp32
+ *       average g = (1/M) sum_j grad_j, summed in the fixed order j = 0..M-1
+ *       -- the gradient-accumulation identity (Lecture04 notes, section
+ *       "单卡 baseline 与 gradient accumulation 的隐藏假设", equation for g)
+ *       and the reduce half of a reduce-scatter, after which each rank holds
+ *       the reduced gradient of exactly the slice it owns (Lecture04 notes,
+ *       "ZeRO-1"; CS324 notes §3.4; CS336 第七讲 summary, Q2);
+ *   (b) optionally scales g by min(1, max_norm / (||g|| + 1e-6)), the norm
+ *       accumulated in fp64 (gradient clipping of the AdamW recipe, CS324
+ *       notes §7.4);
+ *   (c) applies AdamW to the fp32 master weight and fp32 moments m, v of its
+ *       shard -- m and v follow the Adam formula, only their ownership is
+ *       sharded (Lecture04 notes, "ZeRO-1"), under the 16-bytes-per-parameter
+ *       layout bf16 param + bf16 grad + fp32 master, m, v (CS324 notes §2.1;
+ *       CS336 第七讲 summary, Q3);
+ *   (d) writes the bf16 re-cast of the new master (round to nearest even),
+ *       the buffer the all-gather then distributes (Lecture04 notes, "ZeRO-1").
+ * Per element, every operation is one IEEE fp32 operation rounded to nearest:
+ *   g   = (sum_j grad_j) / M            [* coef]
+ *   m'  = beta1*m + (1-beta1)*g
+ *   v'  = beta2*v + (1-beta2)*(g*g)
+ *   den = sqrt(v') / sqrt(1-beta2^t) + eps
+ *   p'  = p*(1 - lr*wd) - (lr/(1-beta1^t)) * (m'/den)
+ *   param = bf16_rne(p')
+ * with the per-step constants computed in fp64 on the host and rounded once
+ * to fp32.  Division and square root are correctly rounded; nothing is
+ * contracted into FMAs; subnormals are kept.
+ *
+ * Layout.  A plan flattens an ordered tensor list into buckets (tensors at
+ * multiples of `align` elements, a bucket closed when the next tensor would
+ * pass `bucket_cap` elements, a larger tensor alone), pads every bucket to a
+ * multiple of world_size*align, and gives rank r slice r of every bucket
+ * (大模型基础设施工程 06, §6.1 gradient buckets and §11.3 contiguous
+ * gradients; cutting flat buffers is legal because AdamW is elementwise,
+ * CS324 notes §3.4).  Every per-element array of the rank -- param, master,
+ * m, v and each grads[j] -- is one flat array of shard_len elements in that
+ * same order.  Padding elements must be zero in every array; the step keeps
+ * them zero.
+ *
+ * Conventions.
+ *   - Pointers named *_dev or taking buffers are device pointers; the caller
+ *     allocates and owns every device buffer (grads, param, master, moments,
+ *     workspace).  The library never allocates or frees device memory.
+ *     zs_plan and zs_ctx are host objects owned by the library, released by
+ *     their destroy calls.
+ *   - Device buffers must be 16-byte aligned; the workspace 256-byte aligned.
+ *   - `stream` is a hipStream_t handle (NULL: the null stream).  Calls
+ *     enqueue work and return without waiting, except where stated.
+ *   - Return value: 0 = ZS_OK; negative = error, nothing enqueued, state
+ *     unchanged, message in zero_shard_last_error(); positive = warning.
+ *   - A context is used by one host thread at a time.
+ */
+#ifndef ZEROSHARD_H
+#define ZEROSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct zs_plan zs_plan; /* host-side layout plan */
+typedef struct zs_ctx zs_ctx;   /* one rank's shard state bound to device buffers */
+
+enum {
+    ZS_OK = 0,
+    ZS_NONFINITE = 1,  /* warning: the gradient norm is NaN or Inf */
+    ZS_EINVAL = -1,    /* invalid argument */
+    ZS_ENOMEM = -2,    /* host allocation failed */
+    ZS_EHIP = -3,      /* a HIP runtime call failed */
+    ZS_ESTATE = -4     /* object in the wrong state for the call */
+};
+
+/* zero_shard_init flags */
+#define ZS_SKIP_NONFINITE 1u /* non-finite norm: the step leaves every array untouched */
+
+#define ZS_MAX_M 16
+
+/* ------------------------------------------------------------------ plan */
+
+/*
+ * Builds the layout of rank `rank` of `world_size` for tensors numel[0..n_tensors)
+ * (element counts, forward order; 0 allowed) with weight-decay flags decay[]
+ * (nonzero: decayed).  bucket_cap >= 1 elements; align a multiple of 8 (64 in
+ * the reference workloads: 128 B of bf16, 256 B of fp32); chunk_elems a
+ * multiple of 2048, or 0 for the default: the largest piece of the shard one
+ * workgroup of the step kernel processes.
+ * On success *out owns a new plan.  Errors: ZS_EINVAL (bad sizes, flags array
+ * missing, geometry), ZS_ENOMEM.
+ */
+int zs_plan_create(const int64_t *numel, const uint8_t *decay, int64_t n_tensors,
+                   int32_t world_size, int32_t rank, int64_t bucket_cap, int32_t align,
+                   int64_t chunk_elems, zs_plan **out);
+
+/* Sizes of the plan.  Any output pointer may be NULL.
+ *   shard_len    elements of this rank's flat shard (a multiple of align)
+ *   n_segments   maximal runs of one tensor, or of padding, in the shard
+ *   n_chunks     entries of the step kernel's chunk table
+ *   padded_total elements of all buckets together (shard_len * world_size)
+ *   n_buckets    number of buckets */
+int zs_plan_query(const zs_plan *plan, int64_t *shard_len, int64_t *n_segments,
+                  int64_t *n_chunks, int64_t *padded_total, int64_t *n_buckets);
+
+/* Where tensor `tensor` lies in this rank's shard: elements
+ * [tensor_off, tensor_off + len) of the tensor sit at [shard_off, shard_off + len).
+ * len = 0 when this rank owns none of it. */
+int zs_plan_tensor_slice(const zs_plan *plan, int64_t tensor, int64_t *shard_off,
+                         int64_t *tensor_off, int64_t *len);
+
+/* Segment i in shard order.  tensor = -1 for padding (tensor_off 0, decay 0). */
+int zs_plan_segment(const zs_plan *plan, int64_t i, int64_t *shard_off, int64_t *len,
+                    int64_t *tensor, int64_t *tensor_off, int32_t *decay);
+
+/* Bucket b: its start in the flat (all-ranks) order and its padded length. */
+int zs_plan_bucket(const zs_plan *plan, int64_t b, int64_t *flat_off, int64_t *len);
+
+/* Chunk i of the step kernel: shard offset, length, decay flag. */
+int zs_plan_chunk(const zs_plan *plan, int64_t i, int64_t *shard_off, int32_t *len,
+                  int32_t *decay);
+
+/* Resident model-state bytes of this rank at ZeRO stage 0..3 under 16 B/param
+ * (CS324 notes §2.1, exercise 1; Lecture04 notes, ZeRO-1/ZeRO-2 formulas):
+ * stage 0: 16*Psi; 1: 4*Psi + 12*S; 2: 2*Psi + 14*S; 3: 16*S,
+ * Psi = sum of numel, S = shard_len. */
+int zs_plan_state_bytes(const zs_plan *plan, int32_t stage, int64_t *bytes);
+
+void zs_plan_destroy(zs_plan *plan);
+
+/* Device workspace a context of this plan needs (chunk table, norm partials,
+ * clip coefficient), in bytes; 0 if plan is NULL.  M is accepted for forward
+ * compatibility and does not change the size. */
+size_t zs_workspace_bytes(const zs_plan *plan, int32_t M);
+
+/* ------------------------------------------------------------ the step */
+
+/*
+ * Binds a context to one rank's device buffers (each shard_len elements):
+ * param_bf16 (bf16, written by every step), master, exp_avg, exp_avg_sq
+ * (fp32, read and written), and a workspace of zs_workspace_bytes(plan, M).
+ * The caller initialises master, sets exp_avg = exp_avg_sq = 0 and zeroes
+ * the padding; param_bf16 is output only.  M in [1, ZS_MAX_M] is the number of
+ * gradient contributions each step reduces.  flags: ZS_SKIP_NONFINITE or 0.
+ * Uploads the chunk table on `stream` and waits for that copy.  The plan may
+ * be destroyed afterwards.  Errors: ZS_EINVAL, ZS_ENOMEM, ZS_EHIP.
+ */
+int zero_shard_init(zs_ctx **out, const zs_plan *plan, int32_t M, void *param_bf16,
+                    float *master, float *exp_avg, float *exp_avg_sq, void *workspace,
+                    size_t workspace_bytes, void *stream, uint32_t flags);
+
+/*
+ * Enqueues one optimizer step.  grads: host array of M device pointers, each
+ * to shard_len bf16 values (this rank's slice of contribution j).
+ * Hyper-parameters: lr >= 0, beta1 and beta2 in [0, 1), eps > 0,
+ * weight_decay >= 0, all finite; step >= 1 is the 1-based step number.
+ * max_grad_norm > 0 enables the global-norm clip of this shard (for N > 1 the
+ * caller uses zero_shard_grad_sumsq + zero_shard_step_global_norm instead);
+ * <= 0 disables it.  grad_norm_out: optional host pointer; when non-NULL the
+ * call waits for the stream and stores ||g||_2 of this shard (fp64).
+ * Returns ZS_OK, ZS_NONFINITE (only when grad_norm_out is given and the norm
+ * is not finite), or an error.  With ZS_SKIP_NONFINITE and a norm computed
+ * (clip on, or grad_norm_out given), a non-finite norm turns the update into
+ * a no-op on the device; otherwise NaN/Inf propagate as in torch.
+ */
+int zero_shard_step(zs_ctx *ctx, const void *const *grads, float lr, float beta1, float beta2,
+                    float eps, float weight_decay, int64_t step, float max_grad_norm,
+                    double *grad_norm_out);
+
+/*
+ * Multi-rank clip, part 1: enqueues sum_i g_i^2 (fp64) of this shard into the
+ * device double *sumsq_dev (g as in the step, before clipping).  The caller
+ * sums these partials over ranks (a scalar all-reduce) and passes the global
+ * value to part 2.  Errors: ZS_EINVAL, ZS_EHIP.
+ */
+int zero_shard_grad_sumsq(zs_ctx *ctx, const void *const *grads, double *sumsq_dev);
+
+/*
+ * Multi-rank clip, part 2: the step of zero_shard_step with the clip
+ * coefficient min(1, max_grad_norm / (sqrt(*global_sumsq_dev) + 1e-6)) taken
+ * from a device double.  max_grad_norm must be > 0.  Never waits.
+ */
+int zero_shard_step_global_norm(zs_ctx *ctx, const void *const *grads, float lr, float beta1,
+                                float beta2, float eps, float weight_decay, int64_t step,
+                                float max_grad_norm, const double *global_sumsq_dev);
+
+/* The bf16 parameter shard (the all-gather send buffer) and its length. */
+int zero_shard_params(zs_ctx *ctx, const void **param_bf16, int64_t *shard_len);
+
+/* Later calls enqueue on `stream`. */
+int zero_shard_set_stream(zs_ctx *ctx, void *stream);
+
+/* Releases the context (host memory only; device buffers stay the caller's). */
+void zero_shard_destroy(zs_ctx *ctx);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *zero_shard_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZEROSHARD_H */

@@ -65,6 +65,8 @@ def lib():
         L.zo_grad_sumsq.restype = f64
         L.zo_clip_coef.argtypes = [f64, f32]
         L.zo_clip_coef.restype = f32
+        L.zo_coef_from_norm.argtypes = [f64, f32]
+        L.zo_coef_from_norm.restype = f32
         L.zo_step_f32.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, f32, f32, f32, f32, f32,
                                   i64, i32, f32]
         L.zo_step_f32.restype = i32
@@ -131,6 +133,10 @@ def grad_sumsq(grads) -> float:
 
 def clip_coef(sumsq: float, max_norm: float) -> np.float32:
     return np.float32(lib().zo_clip_coef(float(sumsq), float(max_norm)))
+
+
+def coef_from_norm(norm: float, max_norm: float) -> np.float32:
+    return np.float32(lib().zo_coef_from_norm(float(norm), float(max_norm)))
 
 
 def step_f32(grads, master, m, v, param=None, decay=None, *, lr, beta1, beta2, eps,

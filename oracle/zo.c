@@ -234,13 +234,19 @@ double zo_grad_sumsq(int64_t n, int32_t M, const uint16_t *const *grads)
     return total;
 }
 
-/* coef = min(1, max_norm / (sqrt(sumsq) + 1e-6)) in fp64, rounded once. */
-float zo_clip_coef(double sumsq, float max_norm)
+/* coef = min(1, max_norm / (norm + 1e-6)) in fp64, rounded once. */
+float zo_coef_from_norm(double norm, float max_norm)
 {
-    double c = (double)max_norm / (sqrt(sumsq) + 1e-6);
+    double c = (double)max_norm / (norm + 1e-6);
     if (c > 1.0)
         c = 1.0;
     return (float)c;
+}
+
+/* the same from the sum of squares: norm = sqrt(sumsq). */
+float zo_clip_coef(double sumsq, float max_norm)
+{
+    return zo_coef_from_norm(sqrt(sumsq), max_norm);
 }
 
 /* ------------------------------------------------------- the steps */

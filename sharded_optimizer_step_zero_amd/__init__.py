@@ -1,0 +1,286 @@
+"""Python binding of libzeroshard.so: the fused per-rank ZeRO shard step on MI355X.
+
+Every C entry point of include/zeroshard.h is exposed under the same name; the
+functions here only marshal arguments (ints for device pointers, numpy/lists
+for host arrays) and turn negative return codes into ZeroShardError.  All the
+work of a step runs in the HIP kernels of the library.  There is no fallback:
+importing this package without the built library raises ImportError.
+
+``ZeroShard`` is a convenience owner for tests and benchmarks: it builds a
+plan, allocates the rank's buffers with torch on a device and binds a context
+to them.  PyTorch supplies device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzeroshard.so")
+
+ZS_OK = 0
+ZS_NONFINITE = 1
+ZS_EINVAL = -1
+ZS_ENOMEM = -2
+ZS_EHIP = -3
+ZS_ESTATE = -4
+ZS_SKIP_NONFINITE = 1
+ZS_MAX_M = 16
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                      "(there is no fallback implementation)")
+
+# A process must use one HIP runtime.  PyTorch bundles its own libamdhip64
+# (same soname, libamdhip64.so.7); loading torch first makes this library bind
+# to that copy instead of mapping a second runtime that then sees no device.
+try:
+    import torch  # noqa: F401
+except ImportError:  # no torch in the process: the system ROCm runtime is used
+    pass
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i64, _i32, _u32, _f32, _f64, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                          ctypes.c_uint32, ctypes.c_float, ctypes.c_double,
+                                          ctypes.c_size_t)
+_P = ctypes.POINTER
+
+
+def _sig(name, restype, *argtypes):
+    f = getattr(_lib, name)
+    f.restype = restype
+    f.argtypes = list(argtypes)
+    return f
+
+
+_sig("zs_plan_create", ctypes.c_int, _vp, _vp, _i64, _i32, _i32, _i64, _i32, _i64, _P(_vp))
+_sig("zs_plan_query", ctypes.c_int, _vp, _P(_i64), _P(_i64), _P(_i64), _P(_i64), _P(_i64))
+_sig("zs_plan_tensor_slice", ctypes.c_int, _vp, _i64, _P(_i64), _P(_i64), _P(_i64))
+_sig("zs_plan_segment", ctypes.c_int, _vp, _i64, _P(_i64), _P(_i64), _P(_i64), _P(_i64),
+     _P(_i32))
+_sig("zs_plan_bucket", ctypes.c_int, _vp, _i64, _P(_i64), _P(_i64))
+_sig("zs_plan_chunk", ctypes.c_int, _vp, _i64, _P(_i64), _P(_i32), _P(_i32))
+_sig("zs_plan_state_bytes", ctypes.c_int, _vp, _i32, _P(_i64))
+_sig("zs_plan_destroy", None, _vp)
+_sig("zs_workspace_bytes", _sz, _vp, _i32)
+_sig("zero_shard_init", ctypes.c_int, _P(_vp), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
+     _u32)
+_sig("zero_shard_step", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _i64, _f32,
+     _P(_f64))
+_sig("zero_shard_grad_sumsq", ctypes.c_int, _vp, _vp, _vp)
+_sig("zero_shard_step_global_norm", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _i64,
+     _f32, _vp)
+_sig("zero_shard_params", ctypes.c_int, _vp, _P(_vp), _P(_i64))
+_sig("zero_shard_set_stream", ctypes.c_int, _vp, _vp)
+_sig("zero_shard_destroy", None, _vp)
+_sig("zero_shard_last_error", ctypes.c_char_p)
+
+EXPORTED = ["zs_plan_create", "zs_plan_query", "zs_plan_tensor_slice", "zs_plan_segment",
+            "zs_plan_bucket", "zs_plan_chunk", "zs_plan_state_bytes", "zs_plan_destroy",
+            "zs_workspace_bytes", "zero_shard_init", "zero_shard_step", "zero_shard_grad_sumsq",
+            "zero_shard_step_global_norm", "zero_shard_params", "zero_shard_set_stream",
+            "zero_shard_destroy", "zero_shard_last_error"]
+
+
+class ZeroShardError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+def zero_shard_last_error() -> str:
+    return _lib.zero_shard_last_error().decode()
+
+
+def _check(rc):
+    if rc < 0:
+        raise ZeroShardError(rc, zero_shard_last_error())
+    return rc
+
+
+def _int64_array(xs):
+    return (ctypes.c_int64 * len(xs))(*[int(x) for x in xs])
+
+
+def _ptr_array(ptrs):
+    return (ctypes.c_void_p * max(1, len(ptrs)))(*[int(p) for p in ptrs])
+
+
+# ------------------------------------------------------------------ plan
+
+
+def zs_plan_create(numel: Sequence[int], decay: Sequence[int], world_size: int, rank: int,
+                   bucket_cap: int = 25_000_000, align: int = 64, chunk_elems: int = 0) -> int:
+    """Returns an opaque plan handle (int)."""
+    n = len(numel)
+    nb = _int64_array(numel)
+    db = (ctypes.c_uint8 * max(1, n))(*[1 if d else 0 for d in decay])
+    if len(decay) != n:
+        raise ValueError("numel and decay differ in length")
+    out = ctypes.c_void_p()
+    _check(_lib.zs_plan_create(nb if n else None, db if n else None, n, world_size, rank,
+                               bucket_cap, align, chunk_elems, ctypes.byref(out)))
+    return out.value
+
+
+def zs_plan_query(plan: int) -> dict:
+    v = [ctypes.c_int64() for _ in range(5)]
+    _check(_lib.zs_plan_query(plan, *[ctypes.byref(x) for x in v]))
+    keys = ["shard_len", "n_segments", "n_chunks", "padded_total", "n_buckets"]
+    return {k: x.value for k, x in zip(keys, v)}
+
+
+def zs_plan_tensor_slice(plan: int, tensor: int):
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.zs_plan_tensor_slice(plan, tensor, ctypes.byref(a), ctypes.byref(b),
+                                     ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def zs_plan_segment(plan: int, i: int):
+    a, b, c, d = (ctypes.c_int64() for _ in range(4))
+    e = ctypes.c_int32()
+    _check(_lib.zs_plan_segment(plan, i, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                ctypes.byref(d), ctypes.byref(e)))
+    return a.value, b.value, c.value, d.value, e.value
+
+
+def zs_plan_bucket(plan: int, b: int):
+    x, y = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.zs_plan_bucket(plan, b, ctypes.byref(x), ctypes.byref(y)))
+    return x.value, y.value
+
+
+def zs_plan_chunk(plan: int, i: int):
+    a, b, c = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.zs_plan_chunk(plan, i, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def zs_plan_state_bytes(plan: int, stage: int) -> int:
+    x = ctypes.c_int64()
+    _check(_lib.zs_plan_state_bytes(plan, stage, ctypes.byref(x)))
+    return x.value
+
+
+def zs_plan_destroy(plan: int) -> None:
+    _lib.zs_plan_destroy(plan)
+
+
+def zs_workspace_bytes(plan: int, M: int) -> int:
+    return int(_lib.zs_workspace_bytes(plan, M))
+
+
+# ------------------------------------------------------------------ step
+
+
+def zero_shard_init(plan: int, M: int, param_bf16: int, master: int, exp_avg: int,
+                    exp_avg_sq: int, workspace: int, workspace_bytes: int, stream: int = 0,
+                    flags: int = 0) -> int:
+    """Returns an opaque context handle (int).  Pointers are device addresses."""
+    out = ctypes.c_void_p()
+    _check(_lib.zero_shard_init(ctypes.byref(out), plan, M, param_bf16, master, exp_avg,
+                                exp_avg_sq, workspace, workspace_bytes, stream or None, flags))
+    return out.value
+
+
+def zero_shard_step(ctx: int, grads: Sequence[int], lr: float, beta1: float, beta2: float,
+                    eps: float, weight_decay: float, step: int, max_grad_norm: float = 0.0,
+                    want_norm: bool = False):
+    """Enqueues one step.  Returns the fp64 grad norm when want_norm (waits), else None."""
+    arr = _ptr_array(grads)
+    if want_norm:
+        nrm = ctypes.c_double()
+        _check(_lib.zero_shard_step(ctx, arr, lr, beta1, beta2, eps, weight_decay, step,
+                                    max_grad_norm, ctypes.byref(nrm)))
+        return nrm.value
+    _check(_lib.zero_shard_step(ctx, arr, lr, beta1, beta2, eps, weight_decay, step,
+                                max_grad_norm, None))
+    return None
+
+
+def zero_shard_grad_sumsq(ctx: int, grads: Sequence[int], sumsq_dev: int) -> None:
+    _check(_lib.zero_shard_grad_sumsq(ctx, _ptr_array(grads), sumsq_dev))
+
+
+def zero_shard_step_global_norm(ctx: int, grads: Sequence[int], lr: float, beta1: float,
+                                beta2: float, eps: float, weight_decay: float, step: int,
+                                max_grad_norm: float, global_sumsq_dev: int) -> None:
+    _check(_lib.zero_shard_step_global_norm(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
+                                            weight_decay, step, max_grad_norm,
+                                            global_sumsq_dev))
+
+
+def zero_shard_params(ctx: int):
+    p, n = ctypes.c_void_p(), ctypes.c_int64()
+    _check(_lib.zero_shard_params(ctx, ctypes.byref(p), ctypes.byref(n)))
+    return p.value or 0, n.value
+
+
+def zero_shard_set_stream(ctx: int, stream: int) -> None:
+    _check(_lib.zero_shard_set_stream(ctx, stream or None))
+
+
+def zero_shard_destroy(ctx: int) -> None:
+    _lib.zero_shard_destroy(ctx)
+
+
+# ----------------------------------------------------- convenience owner
+
+
+class ZeroShard:
+    """One rank's shard: plan + torch-allocated device buffers + bound context."""
+
+    def __init__(self, numel, decay, world_size=1, rank=0, M=1, device=None, bucket_cap=25_000_000,
+                 align=64, chunk_elems=0, flags=0, stream=None):
+        import torch
+        self.device = torch.device(device if device is not None else "cuda")
+        self.M = M
+        self.plan = zs_plan_create(numel, decay, world_size, rank, bucket_cap, align, chunk_elems)
+        q = zs_plan_query(self.plan)
+        self.shard_len = q["shard_len"]
+        self.n_chunks = q["n_chunks"]
+        S = max(self.shard_len, 8)
+        dev = self.device
+        self.master = torch.zeros(S, dtype=torch.float32, device=dev)
+        self.exp_avg = torch.zeros(S, dtype=torch.float32, device=dev)
+        self.exp_avg_sq = torch.zeros(S, dtype=torch.float32, device=dev)
+        self.param = torch.zeros(S, dtype=torch.bfloat16, device=dev)
+        self.ws_bytes = zs_workspace_bytes(self.plan, M)
+        # torch's caching allocator returns 512-byte aligned blocks
+        self.workspace = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self._stream = stream
+        s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+        self.ctx = zero_shard_init(self.plan, M, self.param.data_ptr(), self.master.data_ptr(),
+                                   self.exp_avg.data_ptr(), self.exp_avg_sq.data_ptr(),
+                                   self.workspace.data_ptr(), self.ws_bytes, s, flags)
+
+    def set_stream(self, stream: int):
+        zero_shard_set_stream(self.ctx, stream)
+
+    def step(self, grads, *, lr, beta1, beta2, eps, weight_decay, step, max_grad_norm=0.0,
+             want_norm=False):
+        ptrs = [g if isinstance(g, int) else g.data_ptr() for g in grads]
+        if len(ptrs) != self.M:
+            raise ValueError(f"expected {self.M} gradient contributions")
+        return zero_shard_step(self.ctx, ptrs, lr, beta1, beta2, eps, weight_decay, step,
+                               max_grad_norm, want_norm)
+
+    def segments(self):
+        n = zs_plan_query(self.plan)["n_segments"]
+        return [zs_plan_segment(self.plan, i) for i in range(n)]
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            zero_shard_destroy(self.ctx)
+            self.ctx = None
+        if getattr(self, "plan", None):
+            zs_plan_destroy(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

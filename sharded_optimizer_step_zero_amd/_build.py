@@ -1,0 +1,27 @@
+"""Compiles the product library libzeroshard.so in place (hipcc, gfx950)."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(_HERE, "libzeroshard.so")
+SOURCES = [os.path.join(_HERE, "csrc", f) for f in ("kernels.hip", "plan.cpp", "abi.cpp")]
+
+# -ffp-contract=off: no FMA contraction (each operation rounds once);
+# correctly rounded fp32 division / sqrt; fp32 subnormals kept;
+# packed-fp32 instructions disabled.
+HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+               "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+               "-fno-gpu-flush-denormals-to-zero",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-Wall"]
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    cmd = ["hipcc", *HIPCC_FLAGS, *(extra_flags or []), "-o", LIB + ".tmp", *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB

@@ -1,0 +1,271 @@
+// abi.cpp -- the extern "C" entry points of the shard step (see include/zeroshard.h).
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "../../include/zeroshard.h"
+#include "internal.h"
+
+namespace zs {
+
+thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+}  // namespace zs
+
+struct zs_ctx {
+  int32_t M = 0;
+  uint32_t flags = 0;
+  int64_t shard_len = 0, n_chunks = 0;
+  int32_t n_partials = 0;
+  uint16_t* param = nullptr;
+  float* master = nullptr;
+  float* m = nullptr;
+  float* v = nullptr;
+  char* ws = nullptr;
+  zs::WorkspaceLayout lay{};
+  hipStream_t stream = nullptr;
+};
+
+namespace {
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+zs::WorkspaceLayout workspace_layout(int64_t n_chunks, int32_t n_partials) {
+  zs::WorkspaceLayout l{};
+  l.chunks_off = 0;
+  l.chunks_bytes = (size_t)n_chunks * sizeof(zs::Chunk);
+  l.partials_off = round256(l.chunks_bytes);
+  l.scalars_off = l.partials_off + round256((size_t)n_partials * sizeof(double));
+  l.total = l.scalars_off + round256(sizeof(zs::ClipScalars));
+  return l;
+}
+
+int einval(const char* msg) {
+  zs::set_error(msg);
+  return ZS_EINVAL;
+}
+
+int ehip(const char* where, hipError_t e) {
+  zs::set_error(std::string(where) + ": " + hipGetErrorString(e));
+  return ZS_EHIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Per-step constants: fp64 from the fp32 hyper-parameters, rounded once to fp32.
+zs::StepConsts step_consts(float lr, float beta1, float beta2, float eps, float wd, int64_t t) {
+  const double b1 = beta1, b2 = beta2, l = lr;
+  const double bc1 = 1.0 - pow(b1, (double)t);
+  const double bc2 = 1.0 - pow(b2, (double)t);
+  zs::StepConsts k;
+  k.beta1 = beta1;
+  k.beta2 = beta2;
+  k.c1 = (float)(1.0 - b1);
+  k.c2 = (float)(1.0 - b2);
+  k.alpha = (float)(l / bc1);
+  k.bhat = (float)sqrt(bc2);
+  k.eps = eps;
+  k.decay_mul = (float)(1.0 - l * (double)wd);
+  return k;
+}
+
+int check_hparams(float lr, float beta1, float beta2, float eps, float wd, int64_t step) {
+  if (!(isfinite(lr) && isfinite(beta1) && isfinite(beta2) && isfinite(eps) && isfinite(wd)))
+    return einval("zero_shard_step: hyper-parameters must be finite");
+  if (lr < 0.0f) return einval("zero_shard_step: lr must be >= 0");
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return einval("zero_shard_step: beta1 and beta2 must lie in [0, 1)");
+  if (!(eps > 0.0f)) return einval("zero_shard_step: eps must be > 0");
+  if (wd < 0.0f) return einval("zero_shard_step: weight_decay must be >= 0");
+  if (step < 1) return einval("zero_shard_step: step is 1-based and must be >= 1");
+  return ZS_OK;
+}
+
+int gather_grads(const zs_ctx* ctx, const void* const* grads, zs::GradPtrs* out) {
+  if (!grads) return einval("zero_shard_step: grads is NULL");
+  memset(out, 0, sizeof(*out));
+  for (int j = 0; j < ctx->M; j++) {
+    if (!grads[j] || !aligned16(grads[j]))
+      return einval("zero_shard_step: every grads[j] must be a non-NULL 16-byte-aligned pointer");
+    out->p[j] = static_cast<const uint16_t*>(grads[j]);
+  }
+  return ZS_OK;
+}
+
+zs::ClipScalars* scalars(zs_ctx* ctx) {
+  return reinterpret_cast<zs::ClipScalars*>(ctx->ws + ctx->lay.scalars_off);
+}
+double* partials(zs_ctx* ctx) { return reinterpret_cast<double*>(ctx->ws + ctx->lay.partials_off); }
+const zs::Chunk* chunk_table(zs_ctx* ctx) {
+  return reinterpret_cast<const zs::Chunk*>(ctx->ws + ctx->lay.chunks_off);
+}
+
+}  // namespace
+
+extern "C" size_t zs_workspace_bytes(const zs_plan* plan, int32_t M) {
+  (void)M;
+  if (!plan) return 0;
+  return workspace_layout((int64_t)plan->chunks.size(), zs::sumsq_partials(plan->shard_len)).total;
+}
+
+extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, void* param_bf16,
+                               float* master, float* exp_avg, float* exp_avg_sq, void* workspace,
+                               size_t workspace_bytes, void* stream, uint32_t flags) {
+  if (!out) return einval("zero_shard_init: out is NULL");
+  *out = nullptr;
+  if (!plan) return einval("zero_shard_init: plan is NULL");
+  if (M < 1 || M > ZS_MAX_M) return einval("zero_shard_init: M must lie in [1, 16]");
+  if (flags & ~ZS_SKIP_NONFINITE) return einval("zero_shard_init: unknown flag");
+  if (!param_bf16 || !master || !exp_avg || !exp_avg_sq || !workspace)
+    return einval("zero_shard_init: NULL buffer");
+  if (!aligned16(param_bf16) || !aligned16(master) || !aligned16(exp_avg) ||
+      !aligned16(exp_avg_sq))
+    return einval("zero_shard_init: buffers must be 16-byte aligned");
+  if (((uintptr_t)workspace & 255u) != 0)
+    return einval("zero_shard_init: workspace must be 256-byte aligned");
+  const int32_t n_partials = zs::sumsq_partials(plan->shard_len);
+  const zs::WorkspaceLayout lay = workspace_layout((int64_t)plan->chunks.size(), n_partials);
+  if (workspace_bytes < lay.total) return einval("zero_shard_init: workspace too small");
+
+  zs_ctx* c = new (std::nothrow) zs_ctx;
+  if (!c) {
+    zs::set_error("zero_shard_init: out of host memory");
+    return ZS_ENOMEM;
+  }
+  c->M = M;
+  c->flags = flags;
+  c->shard_len = plan->shard_len;
+  c->n_chunks = (int64_t)plan->chunks.size();
+  c->n_partials = n_partials;
+  c->param = static_cast<uint16_t*>(param_bf16);
+  c->master = master;
+  c->m = exp_avg;
+  c->v = exp_avg_sq;
+  c->ws = static_cast<char*>(workspace);
+  c->lay = lay;
+  c->stream = static_cast<hipStream_t>(stream);
+  if (lay.chunks_bytes) {
+    hipError_t e = hipMemcpyAsync(c->ws + lay.chunks_off, plan->chunks.data(), lay.chunks_bytes,
+                                  hipMemcpyHostToDevice, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) {
+      delete c;
+      return ehip("zero_shard_init: chunk table upload", e);
+    }
+  }
+  *out = c;
+  return ZS_OK;
+}
+
+namespace {
+
+// The norm pass (when needed) and the fused step, enqueued on ctx->stream.
+int enqueue_step(zs_ctx* ctx, const zs::GradPtrs& g, const zs::StepConsts& k, bool need_norm,
+                 bool clip, float max_norm, const double* external_sumsq) {
+  hipError_t e;
+  zs::ClipScalars* sc = scalars(ctx);
+  if (need_norm) {
+    if (!external_sumsq) {
+      e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), ctx->n_partials,
+                           ctx->stream);
+      if (e != hipSuccess) return ehip("zero_shard_step: norm pass", e);
+    }
+    e = zs::launch_finalize(partials(ctx), ctx->n_partials, external_sumsq, max_norm, clip ? 1 : 0,
+                            (ctx->flags & ZS_SKIP_NONFINITE) ? 1 : 0, sc, ctx->stream);
+    if (e != hipSuccess) return ehip("zero_shard_step: norm finalize", e);
+  }
+  e = zs::launch_step(ctx->M, need_norm, g, ctx->master, ctx->m, ctx->v, ctx->param,
+                      chunk_table(ctx), ctx->n_chunks, sc, k, ctx->stream);
+  if (e != hipSuccess) return ehip("zero_shard_step: step kernel", e);
+  return ZS_OK;
+}
+
+}  // namespace
+
+extern "C" int zero_shard_step(zs_ctx* ctx, const void* const* grads, float lr, float beta1,
+                               float beta2, float eps, float weight_decay, int64_t step,
+                               float max_grad_norm, double* grad_norm_out) {
+  if (!ctx) return einval("zero_shard_step: ctx is NULL");
+  int rc = check_hparams(lr, beta1, beta2, eps, weight_decay, step);
+  if (rc) return rc;
+  if (isnan(max_grad_norm) || isinf(max_grad_norm))
+    return einval("zero_shard_step: max_grad_norm must be finite");
+  zs::GradPtrs g;
+  if ((rc = gather_grads(ctx, grads, &g))) return rc;
+  if (ctx->shard_len == 0) {
+    if (grad_norm_out) *grad_norm_out = 0.0;
+    return ZS_OK;
+  }
+  const bool clip = max_grad_norm > 0.0f;
+  const bool need_norm = clip || grad_norm_out || (ctx->flags & ZS_SKIP_NONFINITE);
+  const zs::StepConsts k = step_consts(lr, beta1, beta2, eps, weight_decay, step);
+  if ((rc = enqueue_step(ctx, g, k, need_norm, clip, max_grad_norm, nullptr))) return rc;
+  if (grad_norm_out) {
+    double norm = 0.0;
+    hipError_t e = hipMemcpyAsync(&norm, &scalars(ctx)->norm, sizeof(double),
+                                  hipMemcpyDeviceToHost, ctx->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+    if (e != hipSuccess) return ehip("zero_shard_step: reading the norm", e);
+    *grad_norm_out = norm;
+    if (!isfinite(norm)) return ZS_NONFINITE;
+  }
+  return ZS_OK;
+}
+
+extern "C" int zero_shard_grad_sumsq(zs_ctx* ctx, const void* const* grads, double* sumsq_dev) {
+  if (!ctx) return einval("zero_shard_grad_sumsq: ctx is NULL");
+  if (!sumsq_dev || ((uintptr_t)sumsq_dev & 7u))
+    return einval("zero_shard_grad_sumsq: sumsq_dev must be an 8-byte-aligned device pointer");
+  zs::GradPtrs g;
+  int rc = gather_grads(ctx, grads, &g);
+  if (rc) return rc;
+  // an empty shard sums zero partials, which writes 0 (no memset: capture-safe)
+  const int32_t n_partials = ctx->shard_len ? ctx->n_partials : 0;
+  hipError_t e = hipSuccess;
+  if (n_partials)
+    e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), n_partials, ctx->stream);
+  if (e == hipSuccess) e = zs::launch_sumsq_total(partials(ctx), n_partials, sumsq_dev,
+                                                  ctx->stream);
+  return e == hipSuccess ? ZS_OK : ehip("zero_shard_grad_sumsq", e);
+}
+
+extern "C" int zero_shard_step_global_norm(zs_ctx* ctx, const void* const* grads, float lr,
+                                           float beta1, float beta2, float eps,
+                                           float weight_decay, int64_t step, float max_grad_norm,
+                                           const double* global_sumsq_dev) {
+  if (!ctx) return einval("zero_shard_step_global_norm: ctx is NULL");
+  int rc = check_hparams(lr, beta1, beta2, eps, weight_decay, step);
+  if (rc) return rc;
+  if (!(max_grad_norm > 0.0f) || isinf(max_grad_norm))
+    return einval("zero_shard_step_global_norm: max_grad_norm must be finite and > 0");
+  if (!global_sumsq_dev || ((uintptr_t)global_sumsq_dev & 7u))
+    return einval("zero_shard_step_global_norm: global_sumsq_dev must be an aligned device pointer");
+  zs::GradPtrs g;
+  if ((rc = gather_grads(ctx, grads, &g))) return rc;
+  if (ctx->shard_len == 0) return ZS_OK;
+  const zs::StepConsts k = step_consts(lr, beta1, beta2, eps, weight_decay, step);
+  return enqueue_step(ctx, g, k, true, true, max_grad_norm, global_sumsq_dev);
+}
+
+extern "C" int zero_shard_params(zs_ctx* ctx, const void** param_bf16, int64_t* shard_len) {
+  if (!ctx) return einval("zero_shard_params: ctx is NULL");
+  if (param_bf16) *param_bf16 = ctx->param;
+  if (shard_len) *shard_len = ctx->shard_len;
+  return ZS_OK;
+}
+
+extern "C" int zero_shard_set_stream(zs_ctx* ctx, void* stream) {
+  if (!ctx) return einval("zero_shard_set_stream: ctx is NULL");
+  ctx->stream = static_cast<hipStream_t>(stream);
+  return ZS_OK;
+}
+
+extern "C" void zero_shard_destroy(zs_ctx* ctx) { delete ctx; }
+
+extern "C" const char* zero_shard_last_error(void) { return zs::g_last_error.c_str(); }

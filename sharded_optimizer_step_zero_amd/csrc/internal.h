@@ -1,0 +1,89 @@
+// internal.h -- types shared by the planner, the kernels and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+namespace zs {
+
+// One entry of the step kernel's chunk table: a piece of the shard with one
+// weight-decay flag, processed by one workgroup.  16 bytes.
+struct Chunk {
+  int64_t off;  // shard offset, a multiple of 8 elements
+  int32_t len;  // elements, a multiple of 8
+  int32_t flags;  // bit 0: weight decay applies
+};
+static_assert(sizeof(Chunk) == 16, "chunk descriptor is 16 bytes");
+
+struct Segment {
+  int64_t shard_off, len, tensor, tensor_off;
+  int32_t decay;
+};
+
+// Per-step constants, each computed in fp64 from the fp32 hyper-parameters
+// and rounded once to fp32.
+struct StepConsts {
+  float beta1, beta2;
+  float c1, c2;       // 1 - beta1, 1 - beta2
+  float alpha;        // lr / (1 - beta1^t)
+  float bhat;         // sqrt(1 - beta2^t)
+  float eps;
+  float decay_mul;    // 1 - lr * wd (decayed elements; others use 1)
+};
+
+constexpr int kMaxM = 16;
+
+struct GradPtrs {
+  const uint16_t* p[kMaxM];
+};
+
+// Device workspace layout (offsets in bytes from the workspace base).
+struct WorkspaceLayout {
+  size_t chunks_off, chunks_bytes;
+  size_t partials_off;  // n_partials doubles
+  size_t scalars_off;   // ClipScalars
+  size_t total;
+};
+
+// Written by the finalize kernel, read by the step kernel.
+struct ClipScalars {
+  double sumsq;    // sum of g^2 of the reduced gradient
+  double norm;     // sqrt(sumsq)
+  float coef;      // clip coefficient applied to g (1 when not clipping)
+  uint32_t skip;   // nonzero: leave the state untouched this step
+  uint32_t pad[2];
+};
+
+// Number of fp64 partial sums (= workgroups) of the norm pass for a shard.
+int32_t sumsq_partials(int64_t shard_len);
+
+// Kernel launchers (kernels.hip).  All enqueue on `stream`.
+hipError_t launch_sumsq(int M, const GradPtrs& g, int64_t shard_len, double* partials,
+                        int32_t n_partials, hipStream_t stream);
+// Reduces the partials (or takes *external_sumsq when non-null) into *out.
+hipError_t launch_finalize(const double* partials, int32_t n_partials,
+                           const double* external_sumsq, float max_norm, int clip,
+                           int skip_nonfinite, ClipScalars* out, hipStream_t stream);
+hipError_t launch_sumsq_total(const double* partials, int32_t n_partials, double* out,
+                              hipStream_t stream);
+hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, float* m,
+                       float* v, uint16_t* param, const Chunk* chunks, int64_t n_chunks,
+                       const ClipScalars* clip, const StepConsts& k, hipStream_t stream);
+
+}  // namespace zs
+
+struct zs_plan {
+  int32_t world_size = 1, rank = 0, align = 64;
+  int64_t bucket_cap = 0, chunk_elems = 0;
+  std::vector<int64_t> numel;
+  std::vector<uint8_t> decay;
+  std::vector<int64_t> tensor_flat_off;
+  std::vector<int64_t> tensor_segment;  // segment index of the tensor's piece, or -1
+  std::vector<int64_t> bucket_off, bucket_len;
+  std::vector<zs::Segment> segments;
+  std::vector<zs::Chunk> chunks;
+  int64_t shard_len = 0, padded_total = 0, total_params = 0;
+};

@@ -1,0 +1,301 @@
+// kernels.hip -- the fused ZeRO shard step for gfx950 (MI355X).
+//
+// The step is one streaming pass over HBM: per element it reads M bf16
+// gradient contributions and the fp32 master, m, v (2M + 12 bytes) and writes
+// master, m, v and the bf16 param (14 bytes).  At well under one flop per byte
+// it is bound by HBM bandwidth, far from the VALU and MFMA limits, so there is
+// no matrix-core work here: each lane moves 16-byte (dwordx4) words, holds the
+// M-way reduction in registers in a fixed order, and every element is read
+// and written exactly once.
+//
+// Arithmetic per element (each operation one fp32 rounding, the build uses
+// -ffp-contract=off and correctly rounded division and square root):
+//   s = grad_0 + grad_1 + ... + grad_{M-1}  (bf16 widened exactly, in order)
+//   g = s / M                               [ * coef when clipping ]
+//   m' = beta1*m + c1*g,  v' = beta2*v + c2*(g*g)
+//   den = sqrt(v') / bhat + eps
+//   p' = p*d - alpha*(m'/den),  param = bf16_rne(p')
+// The gradient-accumulation average is the g = (1/M) sum_j grad_j equation of
+// Lecture04 notes ("单卡 baseline 与 gradient accumulation 的隐藏假设"); the
+// update is AdamW with m and v following the Adam recursion (Lecture04 notes,
+// "ZeRO-1"); fp32 accumulation and update as 大模型基础设施工程 06 §9.1
+// prescribes.
+//
+// The optional clip needs the global norm before any update, so it is a
+// separate read pass: sumsq_kernel recomputes g and accumulates g^2 in fp64
+// per lane, reduces each workgroup in a fixed order, and finalize_kernel adds
+// the per-workgroup partials in index order -- run-to-run deterministic.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace zs {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;  // 4 wave64s per workgroup
+constexpr int kVec = 8;        // elements per lane per iteration (one dwordx4 of bf16)
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN is kept as a quiet NaN.
+__device__ __forceinline__ uint32_t to_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : r;
+}
+
+__device__ __forceinline__ void unpack(const u32x4 w, float s[kVec]) {
+  s[0] = bf16_lo(w.x); s[1] = bf16_hi(w.x);
+  s[2] = bf16_lo(w.y); s[3] = bf16_hi(w.y);
+  s[4] = bf16_lo(w.z); s[5] = bf16_hi(w.z);
+  s[6] = bf16_lo(w.w); s[7] = bf16_hi(w.w);
+}
+
+// The M-way reduce of 8 consecutive elements starting at e, divided by M.
+template <int M>
+__device__ __forceinline__ void reduce8(const GradPtrs& g, int64_t e, float s[kVec]) {
+  u32x4 w[M];
+#pragma unroll
+  for (int j = 0; j < M; j++) w[j] = *reinterpret_cast<const u32x4*>(g.p[j] + e);
+  unpack(w[0], s);
+#pragma unroll
+  for (int j = 1; j < M; j++) {
+    float t[kVec];
+    unpack(w[j], t);
+#pragma unroll
+    for (int q = 0; q < kVec; q++) s[q] = s[q] + t[q];
+  }
+#pragma unroll
+  for (int q = 0; q < kVec; q++) s[q] = s[q] / (float)M;
+}
+
+__device__ __forceinline__ void adamw(float g, float& p, float& m, float& v, const StepConsts& k,
+                                      float d) {
+  const float mN = k.beta1 * m;
+  const float mG = k.c1 * g;
+  const float m1 = mN + mG;
+  const float gg = g * g;
+  const float vN = k.beta2 * v;
+  const float vG = k.c2 * gg;
+  const float v1 = vN + vG;
+  const float r = __builtin_sqrtf(v1);
+  const float q = r / k.bhat;
+  const float den = q + k.eps;
+  const float p1 = p * d;
+  const float u = m1 / den;
+  const float w = k.alpha * u;
+  p = p1 - w;
+  m = m1;
+  v = v1;
+}
+
+template <int M, bool CLIP>
+__global__ __launch_bounds__(kThreads) void step_kernel(
+    GradPtrs g, float* __restrict__ master, float* __restrict__ mom1, float* __restrict__ mom2,
+    uint16_t* __restrict__ param, const Chunk* __restrict__ chunks,
+    const ClipScalars* __restrict__ clip, StepConsts k) {
+  const Chunk c = chunks[blockIdx.x];
+  float coef = 1.0f;
+  if (CLIP) {
+    if (clip->skip) return;  // uniform: the whole grid leaves the state untouched
+    coef = clip->coef;
+  }
+  const float d = (c.flags & 1) ? k.decay_mul : 1.0f;
+  for (int32_t i = (int32_t)threadIdx.x * kVec; i < c.len; i += kThreads * kVec) {
+    const int64_t e = c.off + i;
+    float s[kVec];
+    reduce8<M>(g, e, s);
+    f32x4* pp = reinterpret_cast<f32x4*>(master + e);
+    f32x4* mp = reinterpret_cast<f32x4*>(mom1 + e);
+    f32x4* vp = reinterpret_cast<f32x4*>(mom2 + e);
+    f32x4 p4[2] = {pp[0], pp[1]};
+    f32x4 m4[2] = {mp[0], mp[1]};
+    f32x4 v4[2] = {vp[0], vp[1]};
+    uint32_t b[kVec];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        float gq = s[4 * h + q];
+        if (CLIP) gq = gq * coef;
+        float p = p4[h][q], m = m4[h][q], v = v4[h][q];
+        adamw(gq, p, m, v, k, d);
+        p4[h][q] = p;
+        m4[h][q] = m;
+        v4[h][q] = v;
+        b[4 * h + q] = to_bf16(p);
+      }
+    }
+    pp[0] = p4[0]; pp[1] = p4[1];
+    mp[0] = m4[0]; mp[1] = m4[1];
+    vp[0] = v4[0]; vp[1] = v4[1];
+    u32x4 pb;
+    pb.x = b[0] | (b[1] << 16);
+    pb.y = b[2] | (b[3] << 16);
+    pb.z = b[4] | (b[5] << 16);
+    pb.w = b[6] | (b[7] << 16);
+    *reinterpret_cast<u32x4*>(param + e) = pb;
+  }
+}
+
+// Sum over the workgroup in a fixed order: butterfly inside each wave64, then
+// the four wave totals in wave order.  The result is valid in thread 0.
+__device__ __forceinline__ double block_sum(double x) {
+  __shared__ double wave_tot[kThreads / 64];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = x + __shfl_xor(x, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) wave_tot[wave] = x;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0) {
+    t = wave_tot[0];
+    for (int w = 1; w < kThreads / 64; w++) t = t + wave_tot[w];
+  }
+  return t;
+}
+
+template <int M>
+__global__ __launch_bounds__(kThreads) void sumsq_kernel(GradPtrs g, int64_t n_groups,
+                                                         double* __restrict__ partials) {
+  double acc = 0.0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t grp = (int64_t)blockIdx.x * kThreads + threadIdx.x; grp < n_groups;
+       grp += stride) {
+    float s[kVec];
+    reduce8<M>(g, grp * kVec, s);
+#pragma unroll
+    for (int q = 0; q < kVec; q++) {
+      const double x = (double)s[q];
+      acc = acc + x * x;  // the square of an fp32 value is exact in fp64
+    }
+  }
+  const double t = block_sum(acc);
+  if (threadIdx.x == 0) partials[blockIdx.x] = t;
+}
+
+__device__ __forceinline__ double sum_partials(const double* __restrict__ partials, int32_t n) {
+  double acc = 0.0;
+  for (int32_t i = threadIdx.x; i < n; i += kThreads) acc = acc + partials[i];
+  return block_sum(acc);
+}
+
+__global__ __launch_bounds__(kThreads) void finalize_kernel(
+    const double* __restrict__ partials, int32_t n, const double* __restrict__ external,
+    float max_norm, int clip, int skip_nonfinite, ClipScalars* __restrict__ out) {
+  const double part = external ? 0.0 : sum_partials(partials, n);
+  if (threadIdx.x != 0) return;
+  const double total = external ? *external : part;
+  const double norm = __builtin_sqrt(total);
+  float coef = 1.0f;
+  if (clip) {
+    double c = (double)max_norm / (norm + 1e-6);
+    if (c > 1.0) c = 1.0;
+    coef = (float)c;
+  }
+  ClipScalars r;
+  r.sumsq = total;
+  r.norm = norm;
+  r.coef = coef;
+  r.skip = (skip_nonfinite && !__builtin_isfinite(total)) ? 1u : 0u;
+  r.pad[0] = r.pad[1] = 0;
+  *out = r;
+}
+
+__global__ __launch_bounds__(kThreads) void sumsq_total_kernel(const double* __restrict__ partials,
+                                                               int32_t n, double* __restrict__ out) {
+  const double t = sum_partials(partials, n);
+  if (threadIdx.x == 0) *out = t;
+}
+
+template <int M>
+hipError_t launch_step_m(bool use_clip, const GradPtrs& g, float* master, float* m, float* v,
+                         uint16_t* param, const Chunk* chunks, int64_t n_chunks,
+                         const ClipScalars* clip, const StepConsts& k, hipStream_t stream) {
+  const dim3 grid((unsigned)n_chunks), block(kThreads);
+  if (use_clip)
+    hipLaunchKernelGGL((step_kernel<M, true>), grid, block, 0, stream, g, master, m, v, param,
+                       chunks, clip, k);
+  else
+    hipLaunchKernelGGL((step_kernel<M, false>), grid, block, 0, stream, g, master, m, v, param,
+                       chunks, clip, k);
+  return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_sumsq_m(const GradPtrs& g, int64_t shard_len, double* partials,
+                          int32_t n_partials, hipStream_t stream) {
+  hipLaunchKernelGGL((sumsq_kernel<M>), dim3((unsigned)n_partials), dim3(kThreads), 0, stream,
+                     g, shard_len / kVec, partials);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int32_t sumsq_partials(int64_t shard_len) {
+  int64_t groups = shard_len / kVec;
+  int64_t wg = (groups + kThreads - 1) / kThreads;
+  if (wg > 2048) wg = 2048;
+  if (wg < 1) wg = 1;
+  return (int32_t)wg;
+}
+
+#define ZS_DISPATCH_M(M_, CALL) \
+  switch (M_) {                 \
+    case 1: return CALL(1);     \
+    case 2: return CALL(2);     \
+    case 3: return CALL(3);     \
+    case 4: return CALL(4);     \
+    case 5: return CALL(5);     \
+    case 6: return CALL(6);     \
+    case 7: return CALL(7);     \
+    case 8: return CALL(8);     \
+    case 9: return CALL(9);     \
+    case 10: return CALL(10);   \
+    case 11: return CALL(11);   \
+    case 12: return CALL(12);   \
+    case 13: return CALL(13);   \
+    case 14: return CALL(14);   \
+    case 15: return CALL(15);   \
+    case 16: return CALL(16);   \
+    default: return hipErrorInvalidValue; \
+  }
+
+hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, float* m,
+                       float* v, uint16_t* param, const Chunk* chunks, int64_t n_chunks,
+                       const ClipScalars* clip, const StepConsts& k, hipStream_t stream) {
+  if (n_chunks <= 0) return hipSuccess;
+  if (n_chunks > 0x7fffffff) return hipErrorInvalidValue;
+#define ZS_CALL_STEP(X) \
+  launch_step_m<X>(use_clip, g, master, m, v, param, chunks, n_chunks, clip, k, stream)
+  ZS_DISPATCH_M(M, ZS_CALL_STEP)
+#undef ZS_CALL_STEP
+}
+
+hipError_t launch_sumsq(int M, const GradPtrs& g, int64_t shard_len, double* partials,
+                        int32_t n_partials, hipStream_t stream) {
+#define ZS_CALL_SUMSQ(X) launch_sumsq_m<X>(g, shard_len, partials, n_partials, stream)
+  ZS_DISPATCH_M(M, ZS_CALL_SUMSQ)
+#undef ZS_CALL_SUMSQ
+}
+
+hipError_t launch_finalize(const double* partials, int32_t n_partials,
+                           const double* external_sumsq, float max_norm, int clip,
+                           int skip_nonfinite, ClipScalars* out, hipStream_t stream) {
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kThreads), 0, stream, partials, n_partials,
+                     external_sumsq, max_norm, clip, skip_nonfinite, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sumsq_total(const double* partials, int32_t n_partials, double* out,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(sumsq_total_kernel, dim3(1), dim3(kThreads), 0, stream, partials,
+                     n_partials, out);
+  return hipGetLastError();
+}
+
+}  // namespace zs

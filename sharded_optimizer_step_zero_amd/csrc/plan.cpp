@@ -1,0 +1,264 @@
+// plan.cpp -- the flat bucket / shard layout and the step kernel's chunk table.
+//
+// Layout (integer work, once per model):
+//  1. Tensors are placed in forward order into buckets, each at the next
+//     multiple of `align` elements from its bucket's start; a bucket closes
+//     when the next tensor would end past `bucket_cap`; a larger tensor sits
+//     alone (gradient buckets: 大模型基础设施工程 06, §6.1; contiguous flat
+//     gradient buffers: same page, §11.3).
+//  2. A bucket's length is padded to a multiple of world_size * align, so
+//     its world_size slices are equal and aligned ("padded to the shard
+//     boundary").
+//  3. Rank r owns slice r of every bucket: the part of the reduced gradient a
+//     reduce-scatter leaves on it and the only part it updates (Lecture04
+//     notes, "ZeRO-1"; CS324 notes §3.4).  Its shard concatenates those
+//     slices in bucket order; flat cutting is legal because AdamW is
+//     elementwise (CS324 notes §3.4).
+//  4. Segments are maximal runs of one tensor or of padding in the shard.
+//  5. The chunk table cuts the shard into pieces of at most chunk_elems
+//     elements, each inside one run of equal weight-decay flag (padding joins
+//     the run it follows, or the next one at the shard's start; it is zero
+//     in every array and stays zero under either flag).  Every run boundary
+//     is a tensor start, hence a multiple of `align`.
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "../../include/zeroshard.h"
+#include "internal.h"
+
+namespace zs {
+void set_error(const std::string& msg);
+}
+
+namespace {
+
+constexpr int64_t kDefaultChunk = 16384;
+constexpr int64_t kMaxChunk = int64_t(1) << 30;
+constexpr int64_t kMaxElems = int64_t(1) << 52;
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int fail(const char* msg) {
+  zs::set_error(msg);
+  return ZS_EINVAL;
+}
+
+void build_chunks(zs_plan& p) {
+  // runs of equal decay flag over the segments
+  struct Run { int64_t off, len; int flag; };
+  std::vector<Run> runs;
+  for (const zs::Segment& s : p.segments) {
+    if (s.tensor < 0) {  // padding joins the current run
+      if (runs.empty()) runs.push_back({s.shard_off, 0, -1});
+      runs.back().len += s.len;
+      continue;
+    }
+    if (!runs.empty() && (runs.back().flag == -1 || runs.back().flag == s.decay)) {
+      runs.back().flag = s.decay;
+      runs.back().len += s.len;
+    } else {
+      runs.push_back({s.shard_off, s.len, s.decay});
+    }
+  }
+  p.chunks.clear();
+  for (const Run& r : runs) {
+    for (int64_t o = 0; o < r.len; o += p.chunk_elems) {
+      int64_t len = std::min(p.chunk_elems, r.len - o);
+      p.chunks.push_back({r.off + o, (int32_t)len, r.flag > 0 ? 1 : 0});
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" int zs_plan_create(const int64_t* numel, const uint8_t* decay, int64_t n_tensors,
+                              int32_t world_size, int32_t rank, int64_t bucket_cap,
+                              int32_t align, int64_t chunk_elems, zs_plan** out) {
+  if (!out) return fail("zs_plan_create: out is NULL");
+  *out = nullptr;
+  if (n_tensors < 0 || (n_tensors > 0 && (!numel || !decay)))
+    return fail("zs_plan_create: tensor arrays missing");
+  if (world_size < 1 || rank < 0 || rank >= world_size)
+    return fail("zs_plan_create: need 0 <= rank < world_size");
+  if (bucket_cap < 1) return fail("zs_plan_create: bucket_cap must be >= 1");
+  if (align < 8 || align % 8 != 0 || align > (1 << 20))
+    return fail("zs_plan_create: align must be a multiple of 8 (at most 2^20)");
+  if (chunk_elems == 0) chunk_elems = kDefaultChunk;
+  if (chunk_elems < 8 || chunk_elems % 8 != 0 || chunk_elems > kMaxChunk)
+    return fail("zs_plan_create: chunk_elems must be 0 or a multiple of 8 up to 2^30");
+  int64_t total = 0;
+  for (int64_t t = 0; t < n_tensors; t++) {
+    if (numel[t] < 0 || numel[t] > kMaxElems)
+      return fail("zs_plan_create: tensor size out of range");
+    total += numel[t];
+    if (total > kMaxElems) return fail("zs_plan_create: total size out of range");
+  }
+  if ((int64_t)world_size * align > (int64_t(1) << 30))
+    return fail("zs_plan_create: world_size * align too large");
+
+  zs_plan* p = new (std::nothrow) zs_plan;
+  if (!p) {
+    zs::set_error("zs_plan_create: out of host memory");
+    return ZS_ENOMEM;
+  }
+  try {
+    p->world_size = world_size;
+    p->rank = rank;
+    p->align = align;
+    p->bucket_cap = bucket_cap;
+    p->chunk_elems = chunk_elems;
+    p->numel.assign(numel, numel + n_tensors);
+    p->decay.resize(n_tensors);
+    for (int64_t t = 0; t < n_tensors; t++) p->decay[t] = decay[t] ? 1 : 0;
+    p->total_params = total;
+    p->tensor_flat_off.assign(n_tensors, 0);
+    p->tensor_segment.assign(n_tensors, -1);
+
+    // 1-2. buckets
+    std::vector<int64_t> first_of_bucket;
+    const int64_t pad_to = (int64_t)world_size * align;
+    int64_t start = 0, fill = 0;
+    bool open = false;
+    for (int64_t t = 0; t < n_tensors; t++) {
+      int64_t pos = align_up(fill, align);
+      if (open && pos + numel[t] > bucket_cap) {
+        int64_t len = align_up(fill, pad_to);
+        p->bucket_off.push_back(start);
+        p->bucket_len.push_back(len);
+        start += len;
+        fill = 0;
+        pos = 0;
+        open = false;
+      }
+      if (!open) {
+        first_of_bucket.push_back(t);
+        open = true;
+      }
+      p->tensor_flat_off[t] = start + pos;
+      fill = pos + numel[t];
+    }
+    if (open) {
+      p->bucket_off.push_back(start);
+      p->bucket_len.push_back(align_up(fill, pad_to));
+    }
+    const int64_t nb = (int64_t)p->bucket_off.size();
+    p->padded_total = nb ? p->bucket_off[nb - 1] + p->bucket_len[nb - 1] : 0;
+
+    // 3-4. this rank's slices, cut into segments
+    int64_t shard = 0;
+    for (int64_t b = 0; b < nb; b++) {
+      const int64_t part = p->bucket_len[b] / world_size;
+      const int64_t lo = p->bucket_off[b] + rank * part, hi = lo + part;
+      const int64_t t_end = b + 1 < nb ? first_of_bucket[b + 1] : n_tensors;
+      int64_t cursor = lo;
+      auto pad = [&](int64_t a, int64_t e) {
+        if (e <= a) return;
+        if (!p->segments.empty() && p->segments.back().tensor < 0 &&
+            p->segments.back().shard_off + p->segments.back().len == shard + (a - lo))
+          p->segments.back().len += e - a;
+        else
+          p->segments.push_back({shard + (a - lo), e - a, -1, 0, 0});
+      };
+      for (int64_t t = first_of_bucket[b]; t < t_end; t++) {
+        const int64_t a = std::max(p->tensor_flat_off[t], lo);
+        const int64_t e = std::min(p->tensor_flat_off[t] + numel[t], hi);
+        if (a >= e) continue;
+        pad(cursor, a);
+        p->tensor_segment[t] = (int64_t)p->segments.size();
+        p->segments.push_back(
+            {shard + (a - lo), e - a, t, a - p->tensor_flat_off[t], (int32_t)p->decay[t]});
+        cursor = e;
+      }
+      pad(cursor, hi);
+      shard += part;
+    }
+    p->shard_len = shard;
+
+    // 5. chunk table
+    build_chunks(*p);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    zs::set_error("zs_plan_create: out of host memory");
+    return ZS_ENOMEM;
+  }
+  *out = p;
+  return ZS_OK;
+}
+
+extern "C" int zs_plan_query(const zs_plan* p, int64_t* shard_len, int64_t* n_segments,
+                             int64_t* n_chunks, int64_t* padded_total, int64_t* n_buckets) {
+  if (!p) return fail("zs_plan_query: plan is NULL");
+  if (shard_len) *shard_len = p->shard_len;
+  if (n_segments) *n_segments = (int64_t)p->segments.size();
+  if (n_chunks) *n_chunks = (int64_t)p->chunks.size();
+  if (padded_total) *padded_total = p->padded_total;
+  if (n_buckets) *n_buckets = (int64_t)p->bucket_off.size();
+  return ZS_OK;
+}
+
+extern "C" int zs_plan_tensor_slice(const zs_plan* p, int64_t tensor, int64_t* shard_off,
+                                    int64_t* tensor_off, int64_t* len) {
+  if (!p || !shard_off || !tensor_off || !len) return fail("zs_plan_tensor_slice: NULL argument");
+  if (tensor < 0 || tensor >= (int64_t)p->numel.size())
+    return fail("zs_plan_tensor_slice: tensor index out of range");
+  int64_t s = p->tensor_segment[tensor];
+  if (s < 0) {
+    *shard_off = *tensor_off = *len = 0;
+  } else {
+    *shard_off = p->segments[s].shard_off;
+    *tensor_off = p->segments[s].tensor_off;
+    *len = p->segments[s].len;
+  }
+  return ZS_OK;
+}
+
+extern "C" int zs_plan_segment(const zs_plan* p, int64_t i, int64_t* shard_off, int64_t* len,
+                               int64_t* tensor, int64_t* tensor_off, int32_t* decay) {
+  if (!p || !shard_off || !len || !tensor || !tensor_off || !decay)
+    return fail("zs_plan_segment: NULL argument");
+  if (i < 0 || i >= (int64_t)p->segments.size())
+    return fail("zs_plan_segment: index out of range");
+  const zs::Segment& s = p->segments[i];
+  *shard_off = s.shard_off;
+  *len = s.len;
+  *tensor = s.tensor;
+  *tensor_off = s.tensor_off;
+  *decay = s.decay;
+  return ZS_OK;
+}
+
+extern "C" int zs_plan_bucket(const zs_plan* p, int64_t b, int64_t* flat_off, int64_t* len) {
+  if (!p || !flat_off || !len) return fail("zs_plan_bucket: NULL argument");
+  if (b < 0 || b >= (int64_t)p->bucket_off.size())
+    return fail("zs_plan_bucket: index out of range");
+  *flat_off = p->bucket_off[b];
+  *len = p->bucket_len[b];
+  return ZS_OK;
+}
+
+extern "C" int zs_plan_chunk(const zs_plan* p, int64_t i, int64_t* shard_off, int32_t* len,
+                             int32_t* decay) {
+  if (!p || !shard_off || !len || !decay) return fail("zs_plan_chunk: NULL argument");
+  if (i < 0 || i >= (int64_t)p->chunks.size()) return fail("zs_plan_chunk: index out of range");
+  *shard_off = p->chunks[i].off;
+  *len = p->chunks[i].len;
+  *decay = p->chunks[i].flags & 1;
+  return ZS_OK;
+}
+
+extern "C" int zs_plan_state_bytes(const zs_plan* p, int32_t stage, int64_t* bytes) {
+  if (!p || !bytes) return fail("zs_plan_state_bytes: NULL argument");
+  const int64_t psi = p->total_params, S = p->shard_len;
+  switch (stage) {
+    case 0: *bytes = 16 * psi; break;           // plain data parallelism
+    case 1: *bytes = 4 * psi + 12 * S; break;   // optimizer state sharded
+    case 2: *bytes = 2 * psi + 14 * S; break;   // + gradients sharded
+    case 3: *bytes = 16 * S; break;             // + parameters sharded
+    default: return fail("zs_plan_state_bytes: stage must be 0..3");
+  }
+  return ZS_OK;
+}
+
+extern "C" void zs_plan_destroy(zs_plan* p) { delete p; }

@@ -77,6 +77,7 @@ def host_lib():
 def dev_lib():
     global _dev
     if _dev is None:
+        import torch  # noqa: F401  (share torch's HIP runtime; see the product binding)
         if not os.path.exists(DEV_LIB):
             raise RuntimeError(f"{DEV_LIB} is not built; run __graft_entry__.build()")
         lib = ctypes.CDLL(DEV_LIB)

@@ -1,0 +1,85 @@
+"""Fills a rank's device buffers with a workload's seeded synthetic inputs.
+
+Input plumbing for the tests and the benchmark.  Values are addressed by shard
+offset (see synth/__init__.py); padding ranges -- given by the caller as
+(offset, length) pairs -- are zeroed in every array, as the layout requires.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import dev_grad_bf16, dev_normal_f32, dev_zero_ranges, host_grad_bf16, \
+    host_grad_bf16_at, host_normal_f32, host_normal_f32_at
+from .workloads import Workload
+
+
+def padding_mask_at(idx: np.ndarray, padding_ranges) -> np.ndarray:
+    """True where a sampled index falls in padding."""
+    if not padding_ranges:
+        return np.zeros(idx.size, bool)
+    r = np.asarray(padding_ranges, dtype=np.int64).reshape(-1, 2)
+    starts = r[:, 0]
+    ends = r[:, 0] + r[:, 1]
+    order = np.argsort(starts)
+    starts, ends = starts[order], ends[order]
+    k = np.searchsorted(starts, idx, side="right") - 1
+    ok = k >= 0
+    out = np.zeros(idx.size, bool)
+    out[ok] = idx[ok] < ends[k[ok]]
+    return out
+
+
+class DeviceCase:
+    """Device inputs of workload `w` for a shard of `shard_len` elements."""
+
+    def __init__(self, w: Workload, shard_len: int, padding_ranges, device):
+        import torch
+        self.w = w
+        self.S = shard_len
+        self.pad = [(int(o), int(n)) for o, n in padding_ranges if n > 0]
+        self.device = device
+        n = max(shard_len, 8)
+        self.grads = [torch.empty(n, dtype=torch.bfloat16, device=device) for _ in range(w.M)]
+        self._grads_step = None
+
+    # -------------------------------------------------------- device fills
+
+    def fill_master(self, master):
+        dev_normal_f32(master[:self.S], self.w.master_key(), self.w.sigma_master)
+        dev_zero_ranges(master, self.pad)
+
+    def fill_grads(self, step0: int):
+        """Generate the M contributions of 0-based step `step0` (cached for fixed grads)."""
+        s = self.w.grad_step_index(step0)
+        if self._grads_step == s:
+            return self.grads
+        for g, (k, ks) in zip(self.grads, self.w.grad_keys(step0)):
+            dev_grad_bf16(g[:self.S], k, ks, self.w.sigma_grad, self.w.kinds)
+            dev_zero_ranges(g, self.pad)
+        self._grads_step = s
+        return self.grads
+
+    # ---------------------------------------------------------- host twins
+
+    def host_master(self, idx=None) -> np.ndarray:
+        if idx is None:
+            x = host_normal_f32(self.S, self.w.master_key(), self.w.sigma_master)
+            for o, n in self.pad:
+                x[o:o + n] = 0
+            return x
+        x = host_normal_f32_at(idx, self.w.master_key(), self.w.sigma_master)
+        x[padding_mask_at(idx, self.pad)] = 0
+        return x
+
+    def host_grads(self, step0: int, idx=None):
+        out = []
+        for k, ks in self.w.grad_keys(step0):
+            if idx is None:
+                g = host_grad_bf16(self.S, k, ks, self.w.sigma_grad, self.w.kinds)
+                for o, n in self.pad:
+                    g[o:o + n] = 0
+            else:
+                g = host_grad_bf16_at(idx, k, ks, self.w.sigma_grad, self.w.kinds)
+                g[padding_mask_at(idx, self.pad)] = 0
+            out.append(g)
+        return out

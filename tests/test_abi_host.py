@@ -1,0 +1,89 @@
+"""Host-only checks of the C-ABI library: it loads, exports every entry point the
+header declares, and validates arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sharded_optimizer_step_zero_amd as zs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "zeroshard.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:zs|zero_shard)_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 17
+    lib = ctypes.CDLL(zs.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(zs.EXPORTED) == names
+    for n in names:  # the binding exposes the same names
+        assert callable(getattr(zs, n)), n
+
+
+def test_plan_argument_errors():
+    with pytest.raises(zs.ZeroShardError) as e:
+        zs.zs_plan_create([10], [1], 2, 2)
+    assert e.value.code == zs.ZS_EINVAL and "rank" in str(e.value)
+    with pytest.raises(zs.ZeroShardError):
+        zs.zs_plan_create([10], [1], 1, 0, align=12)
+    with pytest.raises(zs.ZeroShardError):
+        zs.zs_plan_create([10], [1], 1, 0, chunk_elems=100)
+    with pytest.raises(zs.ZeroShardError):
+        zs.zs_plan_create([-1], [1], 1, 0)
+    with pytest.raises(zs.ZeroShardError):
+        zs.zs_plan_create([10], [1], 1, 0, bucket_cap=0)
+    p = zs.zs_plan_create([10, 20], [1, 0], 1, 0)
+    try:
+        with pytest.raises(zs.ZeroShardError):
+            zs.zs_plan_tensor_slice(p, 2)
+        with pytest.raises(zs.ZeroShardError):
+            zs.zs_plan_segment(p, 99)
+        with pytest.raises(zs.ZeroShardError):
+            zs.zs_plan_state_bytes(p, 4)
+        with pytest.raises(zs.ZeroShardError):
+            zs.zs_plan_chunk(p, -1)
+    finally:
+        zs.zs_plan_destroy(p)
+
+
+def test_init_and_step_argument_errors_before_any_device_call():
+    p = zs.zs_plan_create([1000], [1], 1, 0)
+    ws = zs.zs_workspace_bytes(p, 4)
+    assert ws > 0 and ws % 256 == 0
+    try:
+        with pytest.raises(zs.ZeroShardError):
+            zs.zero_shard_init(p, 0, 16, 16, 16, 16, 256, ws)        # M = 0
+        with pytest.raises(zs.ZeroShardError):
+            zs.zero_shard_init(p, 17, 16, 16, 16, 16, 256, ws)       # M > 16
+        with pytest.raises(zs.ZeroShardError):
+            zs.zero_shard_init(p, 4, 0, 16, 16, 16, 256, ws)         # NULL param
+        with pytest.raises(zs.ZeroShardError):
+            zs.zero_shard_init(p, 4, 8, 16, 16, 16, 256, ws)         # misaligned
+        with pytest.raises(zs.ZeroShardError):
+            zs.zero_shard_init(p, 4, 16, 16, 16, 16, 128, ws)        # workspace alignment
+        with pytest.raises(zs.ZeroShardError):
+            zs.zero_shard_init(p, 4, 16, 16, 16, 16, 256, ws - 1)    # workspace size
+        with pytest.raises(zs.ZeroShardError):
+            zs.zero_shard_init(p, 4, 16, 16, 16, 16, 256, ws, flags=2)
+        with pytest.raises(zs.ZeroShardError):
+            zs.zero_shard_step(0, [16] * 4, 1e-3, 0.9, 0.95, 1e-8, 0.1, 1)
+    finally:
+        zs.zs_plan_destroy(p)
+    assert zs.zero_shard_last_error()
+
+
+def test_empty_plan():
+    p = zs.zs_plan_create([], [], 4, 3)
+    try:
+        q = zs.zs_plan_query(p)
+        assert q == dict(shard_len=0, n_segments=0, n_chunks=0, padded_total=0, n_buckets=0)
+    finally:
+        zs.zs_plan_destroy(p)

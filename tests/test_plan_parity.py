@@ -1,0 +1,80 @@
+"""The library's layout planner against the oracle layout, exactly (integer work):
+shard length, buckets, segments, tensor slices and per-stage bytes on the five
+workloads (several ranks) and on random tensor lists; plus the properties the
+step kernel relies on for the chunk table."""
+import numpy as np
+import pytest
+
+import sharded_optimizer_step_zero_amd as zs
+from oracle import layout as L
+from synth.workloads import workload
+
+
+def _compare(numel, decay, N, r, cap, align, chunk=0):
+    lay = L.plan(numel, decay, N, r, cap, align)
+    p = zs.zs_plan_create(numel, decay, N, r, cap, align, chunk)
+    try:
+        q = zs.zs_plan_query(p)
+        assert q["shard_len"] == lay.shard_len
+        assert q["padded_total"] == lay.padded_total
+        assert q["n_buckets"] == len(lay.buckets)
+        assert q["n_segments"] == len(lay.segments)
+        for b, (off, ln) in enumerate(lay.buckets):
+            assert zs.zs_plan_bucket(p, b) == (off, ln)
+        for i, s in enumerate(lay.segments):
+            assert zs.zs_plan_segment(p, i) == (s.shard_off, s.length, s.tensor, s.tensor_off,
+                                                s.decay), i
+        for t in range(len(numel)):
+            assert zs.zs_plan_tensor_slice(p, t) == lay.tensor_slice(t), t
+        for stage in range(4):
+            assert zs.zs_plan_state_bytes(p, stage) == lay.state_bytes(stage)
+        _check_chunks(p, q, lay, chunk or 16384, align)
+    finally:
+        zs.zs_plan_destroy(p)
+
+
+def _check_chunks(p, q, lay, chunk, align):
+    n = q["n_chunks"]
+    offs = np.empty(n, np.int64)
+    lens = np.empty(n, np.int64)
+    flags = np.empty(n, np.int64)
+    for i in range(n):
+        offs[i], lens[i], flags[i] = zs.zs_plan_chunk(p, i)
+    # an exact partition of [0, shard_len), in order: every element is written by one workgroup
+    assert offs[0] == 0 if n else lay.shard_len == 0
+    assert np.array_equal(offs[1:], offs[:-1] + lens[:-1])
+    assert offs[-1] + lens[-1] == lay.shard_len if n else True
+    assert (lens > 0).all() and (lens <= chunk).all()
+    assert (offs % 8 == 0).all() and (lens % 8 == 0).all()
+    # the chunk's decay flag equals every tensor element's flag inside it
+    seg_off = np.array([x.shard_off for x in lay.segments], np.int64)
+    seg_end = np.array([x.shard_off + x.length for x in lay.segments], np.int64)
+    seg_flag = np.array([x.decay for x in lay.segments], np.int64)
+    seg_tensor = np.array([x.tensor >= 0 for x in lay.segments], bool)
+    first = np.searchsorted(seg_end, offs, side="right")
+    last = np.searchsorted(seg_off, offs + lens, side="left")
+    for i in range(n):
+        sl = slice(first[i], last[i])
+        assert (seg_flag[sl][seg_tensor[sl]] == flags[i]).all(), i
+
+
+@pytest.mark.parametrize("index,ranks", [(1, [0]), (2, [0, 3, 7]), (3, [0]), (4, [0, 15]),
+                                         (5, [0])])
+def test_workloads(index, ranks):
+    w = workload(index)
+    for r in ranks:
+        _compare(w.numel, w.decay, w.world_size, r, w.bucket_cap, w.align)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_lists(seed):
+    rng = np.random.default_rng(1000 + seed)
+    T = int(rng.integers(0, 60))
+    numel = [int(x) for x in rng.integers(0, 9000, T)]
+    decay = [int(x) for x in rng.integers(0, 2, T)]
+    N = int(rng.choice([1, 2, 3, 5, 8, 16]))
+    align = int(rng.choice([8, 64, 128]))
+    cap = int(rng.choice([1000, 8192, 40_000]))
+    chunk = int(rng.choice([0, 8, 2048, 4096]))
+    for r in {0, N - 1, int(rng.integers(0, N))}:
+        _compare(numel, decay, N, r, cap, align, chunk)
