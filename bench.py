@@ -96,7 +96,6 @@ def main():
     ap.add_argument("--workload", type=int, default=2,
                     help="1 tiny, 2 GPT-1.3B 1/8 shard (default), 3 Llama-6.7B, "
                          "4 Llama-70B 1/16 shard, 5 stress with clip")
-    ap.add_argument("--chunk", type=int, default=0, help="chunk_elems of the plan (0: default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-slab", type=int, default=1 << 25)
     ap.add_argument("--calibrate-copy-gib", type=float, default=1.0,
@@ -121,7 +120,7 @@ def main():
     w = workload(args.workload)
     t_setup = time.time()
     zs = ZeroShard(w.numel, w.decay, w.world_size, w.rank, w.M, device=dev,
-                   bucket_cap=w.bucket_cap, align=w.align, chunk_elems=args.chunk)
+                   bucket_cap=w.bucket_cap, align=w.align)
     pad = [(o, n) for o, n, t, _, _ in zs.segments() if t < 0]
     case = DeviceCase(w, zs.shard_len, pad, dev)
     case.fill_master(zs.master)

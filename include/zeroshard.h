@@ -88,24 +88,23 @@ enum {
  * Builds the layout of rank `rank` of `world_size` for tensors numel[0..n_tensors)
  * (element counts, forward order; 0 allowed) with weight-decay flags decay[]
  * (nonzero: decayed).  bucket_cap >= 1 elements; align a multiple of 8 (64 in
- * the reference workloads: 128 B of bf16, 256 B of fp32); chunk_elems a
- * multiple of 2048, or 0 for the default: the largest piece of the shard one
- * workgroup of the step kernel processes.
+ * the reference workloads: 128 B of bf16, 256 B of fp32).
  * On success *out owns a new plan.  Errors: ZS_EINVAL (bad sizes, flags array
  * missing, geometry), ZS_ENOMEM.
  */
 int zs_plan_create(const int64_t *numel, const uint8_t *decay, int64_t n_tensors,
                    int32_t world_size, int32_t rank, int64_t bucket_cap, int32_t align,
-                   int64_t chunk_elems, zs_plan **out);
+                   zs_plan **out);
 
 /* Sizes of the plan.  Any output pointer may be NULL.
  *   shard_len    elements of this rank's flat shard (a multiple of align)
  *   n_segments   maximal runs of one tensor, or of padding, in the shard
- *   n_chunks     entries of the step kernel's chunk table
+ *   n_runs       maximal stretches of one weight-decay flag (padding joins a
+ *                neighbour); the step kernel looks each tile's flag up here
  *   padded_total elements of all buckets together (shard_len * world_size)
  *   n_buckets    number of buckets */
 int zs_plan_query(const zs_plan *plan, int64_t *shard_len, int64_t *n_segments,
-                  int64_t *n_chunks, int64_t *padded_total, int64_t *n_buckets);
+                  int64_t *n_runs, int64_t *padded_total, int64_t *n_buckets);
 
 /* Where tensor `tensor` lies in this rank's shard: elements
  * [tensor_off, tensor_off + len) of the tensor sit at [shard_off, shard_off + len).
@@ -120,9 +119,9 @@ int zs_plan_segment(const zs_plan *plan, int64_t i, int64_t *shard_off, int64_t 
 /* Bucket b: its start in the flat (all-ranks) order and its padded length. */
 int zs_plan_bucket(const zs_plan *plan, int64_t b, int64_t *flat_off, int64_t *len);
 
-/* Chunk i of the step kernel: shard offset, length, decay flag. */
-int zs_plan_chunk(const zs_plan *plan, int64_t i, int64_t *shard_off, int32_t *len,
-                  int32_t *decay);
+/* Weight-decay run i: shard offset, length, flag.  Runs partition the shard. */
+int zs_plan_run(const zs_plan *plan, int64_t i, int64_t *shard_off, int64_t *len,
+                int32_t *decay);
 
 /* Resident model-state bytes of this rank at ZeRO stage 0..3 under 16 B/param
  * (CS324 notes §2.1, exercise 1; Lecture04 notes, ZeRO-1/ZeRO-2 formulas):
@@ -132,7 +131,7 @@ int zs_plan_state_bytes(const zs_plan *plan, int32_t stage, int64_t *bytes);
 
 void zs_plan_destroy(zs_plan *plan);
 
-/* Device workspace a context of this plan needs (chunk table, norm partials,
+/* Device workspace a context of this plan needs (run table, norm partials,
  * clip coefficient), in bytes; 0 if plan is NULL.  M is accepted for forward
  * compatibility and does not change the size. */
 size_t zs_workspace_bytes(const zs_plan *plan, int32_t M);
@@ -146,7 +145,7 @@ size_t zs_workspace_bytes(const zs_plan *plan, int32_t M);
  * The caller initialises master, sets exp_avg = exp_avg_sq = 0 and zeroes
  * the padding; param_bf16 is output only.  M in [1, ZS_MAX_M] is the number of
  * gradient contributions each step reduces.  flags: ZS_SKIP_NONFINITE or 0.
- * Uploads the chunk table on `stream` and waits for that copy.  The plan may
+ * Uploads the run table on `stream` and waits for that copy.  The plan may
  * be destroyed afterwards.  Errors: ZS_EINVAL, ZS_ENOMEM, ZS_EHIP.
  */
 int zero_shard_init(zs_ctx **out, const zs_plan *plan, int32_t M, void *param_bf16,

@@ -54,13 +54,13 @@ def _sig(name, restype, *argtypes):
     return f
 
 
-_sig("zs_plan_create", ctypes.c_int, _vp, _vp, _i64, _i32, _i32, _i64, _i32, _i64, _P(_vp))
+_sig("zs_plan_create", ctypes.c_int, _vp, _vp, _i64, _i32, _i32, _i64, _i32, _P(_vp))
 _sig("zs_plan_query", ctypes.c_int, _vp, _P(_i64), _P(_i64), _P(_i64), _P(_i64), _P(_i64))
 _sig("zs_plan_tensor_slice", ctypes.c_int, _vp, _i64, _P(_i64), _P(_i64), _P(_i64))
 _sig("zs_plan_segment", ctypes.c_int, _vp, _i64, _P(_i64), _P(_i64), _P(_i64), _P(_i64),
      _P(_i32))
 _sig("zs_plan_bucket", ctypes.c_int, _vp, _i64, _P(_i64), _P(_i64))
-_sig("zs_plan_chunk", ctypes.c_int, _vp, _i64, _P(_i64), _P(_i32), _P(_i32))
+_sig("zs_plan_run", ctypes.c_int, _vp, _i64, _P(_i64), _P(_i64), _P(_i32))
 _sig("zs_plan_state_bytes", ctypes.c_int, _vp, _i32, _P(_i64))
 _sig("zs_plan_destroy", None, _vp)
 _sig("zs_workspace_bytes", _sz, _vp, _i32)
@@ -77,7 +77,7 @@ _sig("zero_shard_destroy", None, _vp)
 _sig("zero_shard_last_error", ctypes.c_char_p)
 
 EXPORTED = ["zs_plan_create", "zs_plan_query", "zs_plan_tensor_slice", "zs_plan_segment",
-            "zs_plan_bucket", "zs_plan_chunk", "zs_plan_state_bytes", "zs_plan_destroy",
+            "zs_plan_bucket", "zs_plan_run", "zs_plan_state_bytes", "zs_plan_destroy",
             "zs_workspace_bytes", "zero_shard_init", "zero_shard_step", "zero_shard_grad_sumsq",
             "zero_shard_step_global_norm", "zero_shard_params", "zero_shard_set_stream",
             "zero_shard_destroy", "zero_shard_last_error"]
@@ -111,7 +111,7 @@ def _ptr_array(ptrs):
 
 
 def zs_plan_create(numel: Sequence[int], decay: Sequence[int], world_size: int, rank: int,
-                   bucket_cap: int = 25_000_000, align: int = 64, chunk_elems: int = 0) -> int:
+                   bucket_cap: int = 25_000_000, align: int = 64) -> int:
     """Returns an opaque plan handle (int)."""
     n = len(numel)
     nb = _int64_array(numel)
@@ -120,14 +120,14 @@ def zs_plan_create(numel: Sequence[int], decay: Sequence[int], world_size: int, 
         raise ValueError("numel and decay differ in length")
     out = ctypes.c_void_p()
     _check(_lib.zs_plan_create(nb if n else None, db if n else None, n, world_size, rank,
-                               bucket_cap, align, chunk_elems, ctypes.byref(out)))
+                               bucket_cap, align, ctypes.byref(out)))
     return out.value
 
 
 def zs_plan_query(plan: int) -> dict:
     v = [ctypes.c_int64() for _ in range(5)]
     _check(_lib.zs_plan_query(plan, *[ctypes.byref(x) for x in v]))
-    keys = ["shard_len", "n_segments", "n_chunks", "padded_total", "n_buckets"]
+    keys = ["shard_len", "n_segments", "n_runs", "padded_total", "n_buckets"]
     return {k: x.value for k, x in zip(keys, v)}
 
 
@@ -152,9 +152,9 @@ def zs_plan_bucket(plan: int, b: int):
     return x.value, y.value
 
 
-def zs_plan_chunk(plan: int, i: int):
-    a, b, c = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
-    _check(_lib.zs_plan_chunk(plan, i, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+def zs_plan_run(plan: int, i: int):
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    _check(_lib.zs_plan_run(plan, i, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
     return a.value, b.value, c.value
 
 
@@ -233,14 +233,14 @@ class ZeroShard:
     """One rank's shard: plan + torch-allocated device buffers + bound context."""
 
     def __init__(self, numel, decay, world_size=1, rank=0, M=1, device=None, bucket_cap=25_000_000,
-                 align=64, chunk_elems=0, flags=0, stream=None):
+                 align=64, flags=0, stream=None):
         import torch
         self.device = torch.device(device if device is not None else "cuda")
         self.M = M
-        self.plan = zs_plan_create(numel, decay, world_size, rank, bucket_cap, align, chunk_elems)
+        self.plan = zs_plan_create(numel, decay, world_size, rank, bucket_cap, align)
         q = zs_plan_query(self.plan)
         self.shard_len = q["shard_len"]
-        self.n_chunks = q["n_chunks"]
+        self.n_runs = q["n_runs"]
         S = max(self.shard_len, 8)
         dev = self.device
         self.master = torch.zeros(S, dtype=torch.float32, device=dev)

@@ -4,8 +4,11 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <stdlib.h>
+
 #include <new>
 #include <string>
+#include <vector>
 
 #include "../../include/zeroshard.h"
 #include "internal.h"
@@ -21,8 +24,9 @@ void set_error(const std::string& msg) { g_last_error = msg; }
 struct zs_ctx {
   int32_t M = 0;
   uint32_t flags = 0;
-  int64_t shard_len = 0, n_chunks = 0;
-  int32_t n_partials = 0;
+  int64_t shard_len = 0;
+  int32_t n_runs = 0, n_partials = 0;
+  int32_t waves_per_cu = 0;
   uint16_t* param = nullptr;
   float* master = nullptr;
   float* m = nullptr;
@@ -36,14 +40,28 @@ namespace {
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-zs::WorkspaceLayout workspace_layout(int64_t n_chunks, int32_t n_partials) {
+zs::WorkspaceLayout workspace_layout(int64_t n_runs, int32_t n_partials) {
   zs::WorkspaceLayout l{};
-  l.chunks_off = 0;
-  l.chunks_bytes = (size_t)n_chunks * sizeof(zs::Chunk);
-  l.partials_off = round256(l.chunks_bytes);
+  l.runs_off = 0;
+  l.runs_bytes = (size_t)(n_runs + 1) * sizeof(zs::Run);
+  l.partials_off = round256(l.runs_bytes);
   l.scalars_off = l.partials_off + round256((size_t)n_partials * sizeof(double));
   l.total = l.scalars_off + round256(sizeof(zs::ClipScalars));
   return l;
+}
+
+// Resident-wave cap of the step kernel per CU, measured on MI355X: fewer
+// contributions leave each wave less in flight, so more waves pay off.
+// ZS_WAVES_PER_CU overrides it (0: no cap).
+int32_t default_waves_per_cu(int32_t M) {
+  const char* env = getenv("ZS_WAVES_PER_CU");
+  if (env && *env) {
+    const long v = strtol(env, nullptr, 10);
+    if (v == 0 || (v >= 3 && v <= 64)) return (int32_t)v;
+  }
+  if (M >= 6) return 7;
+  if (M >= 2) return 8;
+  return 10;
 }
 
 int einval(const char* msg) {
@@ -102,8 +120,8 @@ zs::ClipScalars* scalars(zs_ctx* ctx) {
   return reinterpret_cast<zs::ClipScalars*>(ctx->ws + ctx->lay.scalars_off);
 }
 double* partials(zs_ctx* ctx) { return reinterpret_cast<double*>(ctx->ws + ctx->lay.partials_off); }
-const zs::Chunk* chunk_table(zs_ctx* ctx) {
-  return reinterpret_cast<const zs::Chunk*>(ctx->ws + ctx->lay.chunks_off);
+const zs::Run* run_table(zs_ctx* ctx) {
+  return reinterpret_cast<const zs::Run*>(ctx->ws + ctx->lay.runs_off);
 }
 
 }  // namespace
@@ -111,7 +129,7 @@ const zs::Chunk* chunk_table(zs_ctx* ctx) {
 extern "C" size_t zs_workspace_bytes(const zs_plan* plan, int32_t M) {
   (void)M;
   if (!plan) return 0;
-  return workspace_layout((int64_t)plan->chunks.size(), zs::sumsq_partials(plan->shard_len)).total;
+  return workspace_layout((int64_t)plan->runs.size(), zs::sumsq_partials(plan->shard_len)).total;
 }
 
 extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, void* param_bf16,
@@ -129,9 +147,19 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
     return einval("zero_shard_init: buffers must be 16-byte aligned");
   if (((uintptr_t)workspace & 255u) != 0)
     return einval("zero_shard_init: workspace must be 256-byte aligned");
+  if (plan->runs.size() > 0x3fffffff) return einval("zero_shard_init: too many runs");
   const int32_t n_partials = zs::sumsq_partials(plan->shard_len);
-  const zs::WorkspaceLayout lay = workspace_layout((int64_t)plan->chunks.size(), n_partials);
+  const zs::WorkspaceLayout lay = workspace_layout((int64_t)plan->runs.size(), n_partials);
   if (workspace_bytes < lay.total) return einval("zero_shard_init: workspace too small");
+  std::vector<zs::Run> table;
+  try {
+    table = plan->runs;
+    if (table.empty()) table.push_back({0, 0, 0});
+    table.push_back({plan->shard_len, 0, 0});  // sentinel: starts past every element
+  } catch (const std::bad_alloc&) {
+    zs::set_error("zero_shard_init: out of host memory");
+    return ZS_ENOMEM;
+  }
 
   zs_ctx* c = new (std::nothrow) zs_ctx;
   if (!c) {
@@ -141,8 +169,9 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   c->M = M;
   c->flags = flags;
   c->shard_len = plan->shard_len;
-  c->n_chunks = (int64_t)plan->chunks.size();
+  c->n_runs = (int32_t)(table.size() - 1);
   c->n_partials = n_partials;
+  c->waves_per_cu = default_waves_per_cu(M);
   c->param = static_cast<uint16_t*>(param_bf16);
   c->master = master;
   c->m = exp_avg;
@@ -150,13 +179,14 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   c->ws = static_cast<char*>(workspace);
   c->lay = lay;
   c->stream = static_cast<hipStream_t>(stream);
-  if (lay.chunks_bytes) {
-    hipError_t e = hipMemcpyAsync(c->ws + lay.chunks_off, plan->chunks.data(), lay.chunks_bytes,
-                                  hipMemcpyHostToDevice, c->stream);
+  {
+    hipError_t e = hipMemcpyAsync(c->ws + lay.runs_off, table.data(),
+                                  table.size() * sizeof(zs::Run), hipMemcpyHostToDevice,
+                                  c->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
     if (e != hipSuccess) {
       delete c;
-      return ehip("zero_shard_init: chunk table upload", e);
+      return ehip("zero_shard_init: run table upload", e);
     }
   }
   *out = c;
@@ -181,7 +211,8 @@ int enqueue_step(zs_ctx* ctx, const zs::GradPtrs& g, const zs::StepConsts& k, bo
     if (e != hipSuccess) return ehip("zero_shard_step: norm finalize", e);
   }
   e = zs::launch_step(ctx->M, need_norm, g, ctx->master, ctx->m, ctx->v, ctx->param,
-                      chunk_table(ctx), ctx->n_chunks, sc, k, ctx->stream);
+                      ctx->shard_len, run_table(ctx), ctx->n_runs, sc, k, ctx->waves_per_cu,
+                      ctx->stream);
   if (e != hipSuccess) return ehip("zero_shard_step: step kernel", e);
   return ZS_OK;
 }

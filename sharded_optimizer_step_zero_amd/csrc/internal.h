@@ -9,14 +9,15 @@
 
 namespace zs {
 
-// One entry of the step kernel's chunk table: a piece of the shard with one
-// weight-decay flag, processed by one workgroup.  16 bytes.
-struct Chunk {
-  int64_t off;  // shard offset, a multiple of 8 elements
-  int32_t len;  // elements, a multiple of 8
+// A run of the shard with one weight-decay flag (padding joins a neighbouring
+// run; it is zero in every array and stays zero under either flag).  The step
+// kernel finds the run of each element by binary search over `start`.
+struct Run {
+  int64_t start;  // shard offset, a multiple of 8 elements
   int32_t flags;  // bit 0: weight decay applies
+  int32_t pad;
 };
-static_assert(sizeof(Chunk) == 16, "chunk descriptor is 16 bytes");
+static_assert(sizeof(Run) == 16, "run descriptor is 16 bytes");
 
 struct Segment {
   int64_t shard_off, len, tensor, tensor_off;
@@ -42,9 +43,9 @@ struct GradPtrs {
 
 // Device workspace layout (offsets in bytes from the workspace base).
 struct WorkspaceLayout {
-  size_t chunks_off, chunks_bytes;
-  size_t partials_off;  // n_partials doubles
-  size_t scalars_off;   // ClipScalars
+  size_t runs_off, runs_bytes;  // n_runs + 1 Run entries (the last is a sentinel)
+  size_t partials_off;          // n_partials doubles
+  size_t scalars_off;           // ClipScalars
   size_t total;
 };
 
@@ -69,21 +70,23 @@ hipError_t launch_finalize(const double* partials, int32_t n_partials,
                            int skip_nonfinite, ClipScalars* out, hipStream_t stream);
 hipError_t launch_sumsq_total(const double* partials, int32_t n_partials, double* out,
                               hipStream_t stream);
+// waves_per_cu > 0 caps the resident waves per CU of the step kernel (0: no cap).
 hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, float* m,
-                       float* v, uint16_t* param, const Chunk* chunks, int64_t n_chunks,
-                       const ClipScalars* clip, const StepConsts& k, hipStream_t stream);
+                       float* v, uint16_t* param, int64_t shard_len, const Run* runs,
+                       int32_t n_runs, const ClipScalars* clip, const StepConsts& k,
+                       int32_t waves_per_cu, hipStream_t stream);
 
 }  // namespace zs
 
 struct zs_plan {
   int32_t world_size = 1, rank = 0, align = 64;
-  int64_t bucket_cap = 0, chunk_elems = 0;
+  int64_t bucket_cap = 0;
   std::vector<int64_t> numel;
   std::vector<uint8_t> decay;
   std::vector<int64_t> tensor_flat_off;
   std::vector<int64_t> tensor_segment;  // segment index of the tensor's piece, or -1
   std::vector<int64_t> bucket_off, bucket_len;
   std::vector<zs::Segment> segments;
-  std::vector<zs::Chunk> chunks;
+  std::vector<zs::Run> runs;
   int64_t shard_len = 0, padded_total = 0, total_params = 0;
 };

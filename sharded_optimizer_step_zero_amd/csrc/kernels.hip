@@ -4,9 +4,19 @@
 // gradient contributions and the fp32 master, m, v (2M + 12 bytes) and writes
 // master, m, v and the bf16 param (14 bytes).  At well under one flop per byte
 // it is bound by HBM bandwidth, far from the VALU and MFMA limits, so there is
-// no matrix-core work here: each lane moves 16-byte (dwordx4) words, holds the
-// M-way reduction in registers in a fixed order, and every element is read
-// and written exactly once.
+// no matrix-core work here; every element is read and written exactly once.
+//
+// Launch shape (measured on MI355X): the flat shard is cut into tiles of 256
+// elements, one tile per single-wave workgroup, each lane owning 4 consecutive
+// elements (one 8-byte load per bf16 stream, one 16-byte load per fp32
+// stream).  Small, short-lived workgroups dispatched in order keep the waves
+// in flight on a compact window of every stream, and a cap of a few waves per
+// CU (set through an LDS reservation the kernel never touches) keeps the
+// outstanding requests near what HBM serves best; both beat a persistent
+// grid-stride loop, which spreads concurrent accesses over the whole array.
+// The tile's weight-decay flag comes from the plan's run table by a
+// wave-uniform (scalar-memory) binary search issued after the vector loads,
+// so it overlaps their latency.
 //
 // Arithmetic per element (each operation one fp32 rounding, the build uses
 // -ffp-contract=off and correctly rounded division and square root):
@@ -93,53 +103,81 @@ __device__ __forceinline__ void adamw(float g, float& p, float& m, float& v, con
   v = v1;
 }
 
+// Index of the run containing shard offset e (runs[0].start == 0 <= e).
+__device__ __forceinline__ int32_t find_run(const Run* __restrict__ runs, int32_t n_runs, int64_t e) {
+  int32_t lo = 0, hi = n_runs - 1;  // invariant: runs[lo].start <= e, answer in [lo, hi]
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (runs[mid].start <= e) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+constexpr int kStepLanes = 64;   // one wave64 per workgroup
+constexpr int kStepVec = 4;      // elements per lane
+constexpr int kTile = kStepLanes * kStepVec;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 template <int M, bool CLIP>
-__global__ __launch_bounds__(kThreads) void step_kernel(
+__global__ __launch_bounds__(kStepLanes) void step_kernel(
     GradPtrs g, float* __restrict__ master, float* __restrict__ mom1, float* __restrict__ mom2,
-    uint16_t* __restrict__ param, const Chunk* __restrict__ chunks,
+    uint16_t* __restrict__ param, int64_t n, const Run* __restrict__ runs, int32_t n_runs,
     const ClipScalars* __restrict__ clip, StepConsts k) {
-  const Chunk c = chunks[blockIdx.x];
+  const int64_t tile0 = (int64_t)blockIdx.x * kTile;
+  const int64_t e = tile0 + (int64_t)threadIdx.x * kStepVec;
+  if (e >= n) return;  // n is a multiple of 8: a lane's 4 elements are all in or all out
+
+  // vector loads first: the M contributions, then master, m, v
+  u32x2 w[M];
+#pragma unroll
+  for (int j = 0; j < M; j++) w[j] = *reinterpret_cast<const u32x2*>(g.p[j] + e);
+  f32x4 p4 = *reinterpret_cast<const f32x4*>(master + e);
+  f32x4 m4 = *reinterpret_cast<const f32x4*>(mom1 + e);
+  f32x4 v4 = *reinterpret_cast<const f32x4*>(mom2 + e);
+
+  // the tile's decay flag (uniform search; per lane only where a run starts inside the tile)
+  int32_t r = 0;
+  if (n_runs > 1) {
+    r = find_run(runs, n_runs, tile0);
+    if (runs[r + 1].start < tile0 + kTile) {
+      while (runs[r + 1].start <= e) r++;  // runs[n_runs] is a sentinel past the shard
+    }
+  }
+  const float d = (runs[r].flags & 1) ? k.decay_mul : 1.0f;
   float coef = 1.0f;
   if (CLIP) {
     if (clip->skip) return;  // uniform: the whole grid leaves the state untouched
     coef = clip->coef;
   }
-  const float d = (c.flags & 1) ? k.decay_mul : 1.0f;
-  for (int32_t i = (int32_t)threadIdx.x * kVec; i < c.len; i += kThreads * kVec) {
-    const int64_t e = c.off + i;
-    float s[kVec];
-    reduce8<M>(g, e, s);
-    f32x4* pp = reinterpret_cast<f32x4*>(master + e);
-    f32x4* mp = reinterpret_cast<f32x4*>(mom1 + e);
-    f32x4* vp = reinterpret_cast<f32x4*>(mom2 + e);
-    f32x4 p4[2] = {pp[0], pp[1]};
-    f32x4 m4[2] = {mp[0], mp[1]};
-    f32x4 v4[2] = {vp[0], vp[1]};
-    uint32_t b[kVec];
+
+  float s[kStepVec];
+  s[0] = bf16_lo(w[0].x); s[1] = bf16_hi(w[0].x);
+  s[2] = bf16_lo(w[0].y); s[3] = bf16_hi(w[0].y);
 #pragma unroll
-    for (int h = 0; h < 2; h++) {
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        float gq = s[4 * h + q];
-        if (CLIP) gq = gq * coef;
-        float p = p4[h][q], m = m4[h][q], v = v4[h][q];
-        adamw(gq, p, m, v, k, d);
-        p4[h][q] = p;
-        m4[h][q] = m;
-        v4[h][q] = v;
-        b[4 * h + q] = to_bf16(p);
-      }
-    }
-    pp[0] = p4[0]; pp[1] = p4[1];
-    mp[0] = m4[0]; mp[1] = m4[1];
-    vp[0] = v4[0]; vp[1] = v4[1];
-    u32x4 pb;
-    pb.x = b[0] | (b[1] << 16);
-    pb.y = b[2] | (b[3] << 16);
-    pb.z = b[4] | (b[5] << 16);
-    pb.w = b[6] | (b[7] << 16);
-    *reinterpret_cast<u32x4*>(param + e) = pb;
+  for (int j = 1; j < M; j++) {
+    s[0] = s[0] + bf16_lo(w[j].x); s[1] = s[1] + bf16_hi(w[j].x);
+    s[2] = s[2] + bf16_lo(w[j].y); s[3] = s[3] + bf16_hi(w[j].y);
   }
+  uint32_t b[kStepVec];
+#pragma unroll
+  for (int q = 0; q < kStepVec; q++) {
+    float gq = s[q] / (float)M;
+    if (CLIP) gq = gq * coef;
+    float p = p4[q], m = m4[q], v = v4[q];
+    adamw(gq, p, m, v, k, d);
+    p4[q] = p;
+    m4[q] = m;
+    v4[q] = v;
+    b[q] = to_bf16(p);
+  }
+  __builtin_nontemporal_store(p4, reinterpret_cast<f32x4*>(master + e));
+  __builtin_nontemporal_store(m4, reinterpret_cast<f32x4*>(mom1 + e));
+  __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(mom2 + e));
+  u32x2 pb;
+  pb.x = b[0] | (b[1] << 16);
+  pb.y = b[2] | (b[3] << 16);
+  __builtin_nontemporal_store(pb, reinterpret_cast<u32x2*>(param + e));
 }
 
 // Sum over the workgroup in a fixed order: butterfly inside each wave64, then
@@ -214,15 +252,17 @@ __global__ __launch_bounds__(kThreads) void sumsq_total_kernel(const double* __r
 
 template <int M>
 hipError_t launch_step_m(bool use_clip, const GradPtrs& g, float* master, float* m, float* v,
-                         uint16_t* param, const Chunk* chunks, int64_t n_chunks,
-                         const ClipScalars* clip, const StepConsts& k, hipStream_t stream) {
-  const dim3 grid((unsigned)n_chunks), block(kThreads);
+                         uint16_t* param, int64_t n, const Run* runs, int32_t n_runs,
+                         const ClipScalars* clip, const StepConsts& k, size_t lds,
+                         hipStream_t stream) {
+  const int64_t tiles = (n + kTile - 1) / kTile;
+  const dim3 grid((unsigned)tiles), block(kStepLanes);
   if (use_clip)
-    hipLaunchKernelGGL((step_kernel<M, true>), grid, block, 0, stream, g, master, m, v, param,
-                       chunks, clip, k);
+    hipLaunchKernelGGL((step_kernel<M, true>), grid, block, lds, stream, g, master, m, v, param,
+                       n, runs, n_runs, clip, k);
   else
-    hipLaunchKernelGGL((step_kernel<M, false>), grid, block, 0, stream, g, master, m, v, param,
-                       chunks, clip, k);
+    hipLaunchKernelGGL((step_kernel<M, false>), grid, block, lds, stream, g, master, m, v, param,
+                       n, runs, n_runs, clip, k);
   return hipGetLastError();
 }
 
@@ -265,13 +305,19 @@ int32_t sumsq_partials(int64_t shard_len) {
     default: return hipErrorInvalidValue; \
   }
 
+// LDS per CU on gfx950; reserving lds_cu / waves_per_cu bytes per single-wave
+// workgroup lets at most waves_per_cu of them reside on a CU.
+constexpr size_t kLdsPerCu = 160 * 1024;
+
 hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, float* m,
-                       float* v, uint16_t* param, const Chunk* chunks, int64_t n_chunks,
-                       const ClipScalars* clip, const StepConsts& k, hipStream_t stream) {
-  if (n_chunks <= 0) return hipSuccess;
-  if (n_chunks > 0x7fffffff) return hipErrorInvalidValue;
+                       float* v, uint16_t* param, int64_t shard_len, const Run* runs,
+                       int32_t n_runs, const ClipScalars* clip, const StepConsts& k,
+                       int32_t waves_per_cu, hipStream_t stream) {
+  if (shard_len <= 0) return hipSuccess;
+  if ((shard_len + kTile - 1) / kTile > 0x7fffffff || n_runs < 1) return hipErrorInvalidValue;
+  const size_t lds = waves_per_cu > 0 ? (kLdsPerCu / (size_t)waves_per_cu) & ~(size_t)255 : 0;
 #define ZS_CALL_STEP(X) \
-  launch_step_m<X>(use_clip, g, master, m, v, param, chunks, n_chunks, clip, k, stream)
+  launch_step_m<X>(use_clip, g, master, m, v, param, shard_len, runs, n_runs, clip, k, lds, stream)
   ZS_DISPATCH_M(M, ZS_CALL_STEP)
 #undef ZS_CALL_STEP
 }

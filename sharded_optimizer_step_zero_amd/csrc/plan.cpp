@@ -1,4 +1,4 @@
-// plan.cpp -- the flat bucket / shard layout and the step kernel's chunk table.
+// plan.cpp -- the flat bucket / shard layout and the weight-decay runs of a shard.
 //
 // Layout (integer work, once per model):
 //  1. Tensors are placed in forward order into buckets, each at the next
@@ -15,11 +15,12 @@
 //     slices in bucket order; flat cutting is legal because AdamW is
 //     elementwise (CS324 notes §3.4).
 //  4. Segments are maximal runs of one tensor or of padding in the shard.
-//  5. The chunk table cuts the shard into pieces of at most chunk_elems
-//     elements, each inside one run of equal weight-decay flag (padding joins
-//     the run it follows, or the next one at the shard's start; it is zero
-//     in every array and stays zero under either flag).  Every run boundary
-//     is a tensor start, hence a multiple of `align`.
+//  5. Runs: maximal stretches of the shard with one weight-decay flag; padding
+//     joins the run it follows (or the next one at the shard's start) -- it is
+//     zero in every array and stays zero under either flag.  Every run start
+//     is a tensor start, hence a multiple of `align`.  The step kernel tiles
+//     the flat shard uniformly and looks each tile's flag up in this table,
+//     so thousands of mixed-size tensors cost one launch and a short search.
 #include <string.h>
 
 #include <algorithm>
@@ -34,8 +35,6 @@ void set_error(const std::string& msg);
 
 namespace {
 
-constexpr int64_t kDefaultChunk = 16384;
-constexpr int64_t kMaxChunk = int64_t(1) << 30;
 constexpr int64_t kMaxElems = int64_t(1) << 52;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -45,29 +44,20 @@ int fail(const char* msg) {
   return ZS_EINVAL;
 }
 
-void build_chunks(zs_plan& p) {
-  // runs of equal decay flag over the segments
-  struct Run { int64_t off, len; int flag; };
-  std::vector<Run> runs;
+void build_runs(zs_plan& p) {
+  p.runs.clear();
+  int last_flag = -1;  // flag of the open run; -1 while it holds only padding
   for (const zs::Segment& s : p.segments) {
     if (s.tensor < 0) {  // padding joins the current run
-      if (runs.empty()) runs.push_back({s.shard_off, 0, -1});
-      runs.back().len += s.len;
+      if (p.runs.empty()) p.runs.push_back({s.shard_off, 0, 0});
       continue;
     }
-    if (!runs.empty() && (runs.back().flag == -1 || runs.back().flag == s.decay)) {
-      runs.back().flag = s.decay;
-      runs.back().len += s.len;
+    if (!p.runs.empty() && (last_flag == -1 || last_flag == s.decay)) {
+      p.runs.back().flags = s.decay;
     } else {
-      runs.push_back({s.shard_off, s.len, s.decay});
+      p.runs.push_back({s.shard_off, s.decay, 0});
     }
-  }
-  p.chunks.clear();
-  for (const Run& r : runs) {
-    for (int64_t o = 0; o < r.len; o += p.chunk_elems) {
-      int64_t len = std::min(p.chunk_elems, r.len - o);
-      p.chunks.push_back({r.off + o, (int32_t)len, r.flag > 0 ? 1 : 0});
-    }
+    last_flag = s.decay;
   }
 }
 
@@ -75,7 +65,7 @@ void build_chunks(zs_plan& p) {
 
 extern "C" int zs_plan_create(const int64_t* numel, const uint8_t* decay, int64_t n_tensors,
                               int32_t world_size, int32_t rank, int64_t bucket_cap,
-                              int32_t align, int64_t chunk_elems, zs_plan** out) {
+                              int32_t align, zs_plan** out) {
   if (!out) return fail("zs_plan_create: out is NULL");
   *out = nullptr;
   if (n_tensors < 0 || (n_tensors > 0 && (!numel || !decay)))
@@ -85,9 +75,6 @@ extern "C" int zs_plan_create(const int64_t* numel, const uint8_t* decay, int64_
   if (bucket_cap < 1) return fail("zs_plan_create: bucket_cap must be >= 1");
   if (align < 8 || align % 8 != 0 || align > (1 << 20))
     return fail("zs_plan_create: align must be a multiple of 8 (at most 2^20)");
-  if (chunk_elems == 0) chunk_elems = kDefaultChunk;
-  if (chunk_elems < 8 || chunk_elems % 8 != 0 || chunk_elems > kMaxChunk)
-    return fail("zs_plan_create: chunk_elems must be 0 or a multiple of 8 up to 2^30");
   int64_t total = 0;
   for (int64_t t = 0; t < n_tensors; t++) {
     if (numel[t] < 0 || numel[t] > kMaxElems)
@@ -108,7 +95,6 @@ extern "C" int zs_plan_create(const int64_t* numel, const uint8_t* decay, int64_
     p->rank = rank;
     p->align = align;
     p->bucket_cap = bucket_cap;
-    p->chunk_elems = chunk_elems;
     p->numel.assign(numel, numel + n_tensors);
     p->decay.resize(n_tensors);
     for (int64_t t = 0; t < n_tensors; t++) p->decay[t] = decay[t] ? 1 : 0;
@@ -176,8 +162,8 @@ extern "C" int zs_plan_create(const int64_t* numel, const uint8_t* decay, int64_
     }
     p->shard_len = shard;
 
-    // 5. chunk table
-    build_chunks(*p);
+    // 5. weight-decay runs
+    build_runs(*p);
   } catch (const std::bad_alloc&) {
     delete p;
     zs::set_error("zs_plan_create: out of host memory");
@@ -188,11 +174,11 @@ extern "C" int zs_plan_create(const int64_t* numel, const uint8_t* decay, int64_
 }
 
 extern "C" int zs_plan_query(const zs_plan* p, int64_t* shard_len, int64_t* n_segments,
-                             int64_t* n_chunks, int64_t* padded_total, int64_t* n_buckets) {
+                             int64_t* n_runs, int64_t* padded_total, int64_t* n_buckets) {
   if (!p) return fail("zs_plan_query: plan is NULL");
   if (shard_len) *shard_len = p->shard_len;
   if (n_segments) *n_segments = (int64_t)p->segments.size();
-  if (n_chunks) *n_chunks = (int64_t)p->chunks.size();
+  if (n_runs) *n_runs = (int64_t)p->runs.size();
   if (padded_total) *padded_total = p->padded_total;
   if (n_buckets) *n_buckets = (int64_t)p->bucket_off.size();
   return ZS_OK;
@@ -238,13 +224,14 @@ extern "C" int zs_plan_bucket(const zs_plan* p, int64_t b, int64_t* flat_off, in
   return ZS_OK;
 }
 
-extern "C" int zs_plan_chunk(const zs_plan* p, int64_t i, int64_t* shard_off, int32_t* len,
-                             int32_t* decay) {
-  if (!p || !shard_off || !len || !decay) return fail("zs_plan_chunk: NULL argument");
-  if (i < 0 || i >= (int64_t)p->chunks.size()) return fail("zs_plan_chunk: index out of range");
-  *shard_off = p->chunks[i].off;
-  *len = p->chunks[i].len;
-  *decay = p->chunks[i].flags & 1;
+extern "C" int zs_plan_run(const zs_plan* p, int64_t i, int64_t* shard_off, int64_t* len,
+                           int32_t* decay) {
+  if (!p || !shard_off || !len || !decay) return fail("zs_plan_run: NULL argument");
+  if (i < 0 || i >= (int64_t)p->runs.size()) return fail("zs_plan_run: index out of range");
+  const int64_t end = i + 1 < (int64_t)p->runs.size() ? p->runs[i + 1].start : p->shard_len;
+  *shard_off = p->runs[i].start;
+  *len = end - p->runs[i].start;
+  *decay = p->runs[i].flags & 1;
   return ZS_OK;
 }
 

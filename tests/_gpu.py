@@ -70,12 +70,11 @@ def to_host(t) -> np.ndarray:
 class Shard:
     """A ZeroShard bound to a workload's synthetic inputs (geometry from the oracle layout)."""
 
-    def __init__(self, w: Workload, chunk_elems=0, flags=0, device="cuda"):
+    def __init__(self, w: Workload, flags=0, device="cuda"):
         self.w = w
         self.lay = L.plan(w.numel, w.decay, w.world_size, w.rank, w.bucket_cap, w.align)
         self.zs = ZeroShard(w.numel, w.decay, w.world_size, w.rank, w.M, device=device,
-                            bucket_cap=w.bucket_cap, align=w.align, chunk_elems=chunk_elems,
-                            flags=flags)
+                            bucket_cap=w.bucket_cap, align=w.align, flags=flags)
         assert self.zs.shard_len == self.lay.shard_len
         self.S = self.lay.shard_len
         self.case = DeviceCase(w, self.S, self.lay.padding_ranges(), self.zs.device)
@@ -104,9 +103,9 @@ class Shard:
         torch.cuda.empty_cache()
 
 
-def full_parity(w: Workload, steps: int, chunk_elems=0, flags=0, exact=True):
+def full_parity(w: Workload, steps: int, flags=0, exact=True):
     """Whole-shard parity for `steps` steps.  Returns the per-step stats."""
-    sh = Shard(w, chunk_elems, flags)
+    sh = Shard(w, flags)
     S = sh.S
     hp = sh.hp()
     mask = sh.lay.decay_mask()

@@ -25,8 +25,7 @@ def _libraries_built():
     if not (_built("synth/libsynth_host.so") and _built("synth/libsynth_dev.so")):
         import synth.build
         synth.build.build()
-    if (_built("sharded_optimizer_step_zero_amd/_build.py")
-            and not _built("sharded_optimizer_step_zero_amd/libzeroshard.so")):
-        from sharded_optimizer_step_zero_amd import _build
-        _build.build()
+    if not _built("sharded_optimizer_step_zero_amd/libzeroshard.so"):
+        import __graft_entry__
+        __graft_entry__.build_product()
     yield

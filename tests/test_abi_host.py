@@ -35,8 +35,6 @@ def test_plan_argument_errors():
     with pytest.raises(zs.ZeroShardError):
         zs.zs_plan_create([10], [1], 1, 0, align=12)
     with pytest.raises(zs.ZeroShardError):
-        zs.zs_plan_create([10], [1], 1, 0, chunk_elems=100)
-    with pytest.raises(zs.ZeroShardError):
         zs.zs_plan_create([-1], [1], 1, 0)
     with pytest.raises(zs.ZeroShardError):
         zs.zs_plan_create([10], [1], 1, 0, bucket_cap=0)
@@ -49,7 +47,7 @@ def test_plan_argument_errors():
         with pytest.raises(zs.ZeroShardError):
             zs.zs_plan_state_bytes(p, 4)
         with pytest.raises(zs.ZeroShardError):
-            zs.zs_plan_chunk(p, -1)
+            zs.zs_plan_run(p, -1)
     finally:
         zs.zs_plan_destroy(p)
 
@@ -84,6 +82,6 @@ def test_empty_plan():
     p = zs.zs_plan_create([], [], 4, 3)
     try:
         q = zs.zs_plan_query(p)
-        assert q == dict(shard_len=0, n_segments=0, n_chunks=0, padded_total=0, n_buckets=0)
+        assert q == dict(shard_len=0, n_segments=0, n_runs=0, padded_total=0, n_buckets=0)
     finally:
         zs.zs_plan_destroy(p)

@@ -37,25 +37,28 @@ def test_tiny_flat_full():
 
 
 SMALL = [
-    # (numel, decay, N, rank, M, max_norm, chunk)
-    ([1, 63, 64, 65, 1000, 0, 4097, 12_345, 7, 300_001, 3], None, 3, 1, 3, 0.0, 0),
-    ([5000] * 7 + [1], None, 8, 7, 8, 0.05, 2048),
+    # (numel, decay, N, rank, M, max_norm, align): many decay runs, runs starting
+    # inside 256-element tiles, ragged shard ends, N up to 16, M up to 16
+    ([1, 63, 64, 65, 1000, 0, 4097, 12_345, 7, 300_001, 3], None, 3, 1, 3, 0.0, 64),
+    ([5000] * 7 + [1], None, 8, 7, 8, 0.05, 64),
     ([70_001, 64, 5, 2 ** 17 + 8], [1, 0, 0, 1], 1, 0, 5, 0.0, 8),
-    ([33_333] * 5, [0, 1, 0, 1, 0], 2, 0, 16, 1e-4, 4096),
-    ([1 << 16], [1], 1, 0, 1, 0.0, 0),
-    ([200_000, 17], [1, 1], 16, 5, 7, 10.0, 16384),
+    ([33_333] * 5, [0, 1, 0, 1, 0], 2, 0, 16, 1e-4, 64),
+    ([1 << 16], [1], 1, 0, 1, 0.0, 64),
+    ([200_000, 17], [1, 1], 16, 5, 7, 10.0, 128),
+    ([3, 9, 1, 17, 2, 40, 5, 8] * 40, [1, 0] * 160, 1, 0, 2, 0.0, 8),
 ]
 
 
 @pytest.mark.parametrize("case", range(len(SMALL)))
 def test_small_multi_tensor_full(case):
-    numel, decay, N, rank, M, clip, chunk = SMALL[case]
+    numel, decay, N, rank, M, clip, align = SMALL[case]
     w = scaled(workload(1), numel, decay, world_size=N, rank=rank, M=M,
                name=f"small{case}")
     w.max_grad_norm = clip
+    w.align = align
     log(f"test_small_multi_tensor_full[{case}]: tensors={len(numel)} N={N} r={rank} M={M} "
-        f"clip={clip} chunk={chunk}")
-    _report(w.name, full_parity(w, 4, chunk_elems=chunk))
+        f"clip={clip} align={align}")
+    _report(w.name, full_parity(w, 4))
 
 
 def test_gpt13b_shard_full():

@@ -10,9 +10,9 @@ from oracle import layout as L
 from synth.workloads import workload
 
 
-def _compare(numel, decay, N, r, cap, align, chunk=0):
+def _compare(numel, decay, N, r, cap, align):
     lay = L.plan(numel, decay, N, r, cap, align)
-    p = zs.zs_plan_create(numel, decay, N, r, cap, align, chunk)
+    p = zs.zs_plan_create(numel, decay, N, r, cap, align)
     try:
         q = zs.zs_plan_query(p)
         assert q["shard_len"] == lay.shard_len
@@ -28,25 +28,28 @@ def _compare(numel, decay, N, r, cap, align, chunk=0):
             assert zs.zs_plan_tensor_slice(p, t) == lay.tensor_slice(t), t
         for stage in range(4):
             assert zs.zs_plan_state_bytes(p, stage) == lay.state_bytes(stage)
-        _check_chunks(p, q, lay, chunk or 16384, align)
+        _check_runs(p, q, lay, align)
     finally:
         zs.zs_plan_destroy(p)
 
 
-def _check_chunks(p, q, lay, chunk, align):
-    n = q["n_chunks"]
+def _check_runs(p, q, lay, align):
+    n = q["n_runs"]
     offs = np.empty(n, np.int64)
     lens = np.empty(n, np.int64)
     flags = np.empty(n, np.int64)
     for i in range(n):
-        offs[i], lens[i], flags[i] = zs.zs_plan_chunk(p, i)
-    # an exact partition of [0, shard_len), in order: every element is written by one workgroup
-    assert offs[0] == 0 if n else lay.shard_len == 0
+        offs[i], lens[i], flags[i] = zs.zs_plan_run(p, i)
+    if lay.shard_len == 0:
+        assert n == 0
+        return
+    # an exact partition of [0, shard_len), in order, runs starting on align boundaries
+    assert offs[0] == 0
     assert np.array_equal(offs[1:], offs[:-1] + lens[:-1])
-    assert offs[-1] + lens[-1] == lay.shard_len if n else True
-    assert (lens > 0).all() and (lens <= chunk).all()
-    assert (offs % 8 == 0).all() and (lens % 8 == 0).all()
-    # the chunk's decay flag equals every tensor element's flag inside it
+    assert offs[-1] + lens[-1] == lay.shard_len
+    assert (lens > 0).all() and (offs % align == 0).all()
+    # neighbouring runs differ (maximal), and each run's flag is every tensor element's flag
+    assert (flags[1:] != flags[:-1]).all()
     seg_off = np.array([x.shard_off for x in lay.segments], np.int64)
     seg_end = np.array([x.shard_off + x.length for x in lay.segments], np.int64)
     seg_flag = np.array([x.decay for x in lay.segments], np.int64)
@@ -75,6 +78,5 @@ def test_random_lists(seed):
     N = int(rng.choice([1, 2, 3, 5, 8, 16]))
     align = int(rng.choice([8, 64, 128]))
     cap = int(rng.choice([1000, 8192, 40_000]))
-    chunk = int(rng.choice([0, 8, 2048, 4096]))
     for r in {0, N - 1, int(rng.integers(0, N))}:
-        _compare(numel, decay, N, r, cap, align, chunk)
+        _compare(numel, decay, N, r, cap, align)
