@@ -113,7 +113,7 @@ def main():
     import synth
     from sharded_optimizer_step_zero_amd import ZeroShard
     from synth.device_case import DeviceCase
-    from synth.workloads import workload
+    from synth.workloads import special_ranges, workload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -121,8 +121,10 @@ def main():
     t_setup = time.time()
     zs = ZeroShard(w.numel, w.decay, w.world_size, w.rank, w.M, device=dev,
                    bucket_cap=w.bucket_cap, align=w.align)
-    pad = [(o, n) for o, n, t, _, _ in zs.segments() if t < 0]
-    case = DeviceCase(w, zs.shard_len, pad, dev)
+    segs = zs.segments()
+    pad = [(o, n) for o, n, t, _, _ in segs if t < 0]
+    special = special_ranges(w, [(o, n, t) for o, n, t, _, _ in segs])
+    case = DeviceCase(w, zs.shard_len, pad, dev, special)
     case.fill_master(zs.master)
     grads = case.fill_grads(0)
     stream = torch.cuda.current_stream(dev)

@@ -8,8 +8,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import dev_grad_bf16, dev_normal_f32, dev_zero_ranges, host_grad_bf16, \
-    host_grad_bf16_at, host_normal_f32, host_normal_f32_at
+from . import Kinds, dev_grad_bf16, dev_normal_f32, dev_scatter, dev_zero_ranges, \
+    host_grad_bf16, host_grad_bf16_at, host_normal_f32, host_normal_f32_at, key
 from .workloads import Workload
 
 
@@ -29,14 +29,25 @@ def padding_mask_at(idx: np.ndarray, padding_ranges) -> np.ndarray:
     return out
 
 
-class DeviceCase:
-    """Device inputs of workload `w` for a shard of `shard_len` elements."""
+ALL_SUBNORMAL = Kinds(subnormal_ppm=1_000_000)
 
-    def __init__(self, w: Workload, shard_len: int, padding_ranges, device):
+
+class DeviceCase:
+    """Device inputs of workload `w` for a shard of `shard_len` elements.
+
+    special: (offset, length, kind) ranges whose gradient contributions are
+    overridden in every contribution ("zero": +0.0; "subnormal": bf16
+    subnormals from their own hash stream)."""
+
+    def __init__(self, w: Workload, shard_len: int, padding_ranges, device, special=()):
         import torch
         self.w = w
         self.S = shard_len
         self.pad = [(int(o), int(n)) for o, n in padding_ranges if n > 0]
+        self.zero = [(o, n) for o, n, k in special if k == "zero"]
+        sub = [(o, n) for o, n, k in special if k == "subnormal"]
+        self.sub_idx = (np.concatenate([np.arange(o, o + n) for o, n in sub]).astype(np.int64)
+                        if sub else np.zeros(0, np.int64))
         self.device = device
         n = max(shard_len, 8)
         self.grads = [torch.empty(n, dtype=torch.bfloat16, device=device) for _ in range(w.M)]
@@ -53,11 +64,34 @@ class DeviceCase:
         s = self.w.grad_step_index(step0)
         if self._grads_step == s:
             return self.grads
-        for g, (k, ks) in zip(self.grads, self.w.grad_keys(step0)):
+        for j, (g, (k, ks)) in enumerate(zip(self.grads, self.w.grad_keys(step0))):
             dev_grad_bf16(g[:self.S], k, ks, self.w.sigma_grad, self.w.kinds)
-            dev_zero_ranges(g, self.pad)
+            dev_zero_ranges(g, self.pad + self.zero)
+            if self.sub_idx.size:
+                dev_scatter(g, self.sub_idx, self._subnormals(j, step0, self.sub_idx))
         self._grads_step = s
         return self.grads
+
+    def _subnormals(self, j, step0, idx):
+        st = 0x30000 + j + self.w.M * self.w.grad_step_index(step0)
+        return host_grad_bf16_at(idx, key(self.w.seed, st), key(self.w.seed, st + 0x8000), 1.0,
+                                 ALL_SUBNORMAL)
+
+    def _override(self, g, j, step0, idx=None):
+        """Apply the special ranges to a host array (whole shard, or sampled at idx)."""
+        if idx is None:
+            for o, n in self.zero:
+                g[o:o + n] = 0
+            if self.sub_idx.size:
+                g[self.sub_idx] = self._subnormals(j, step0, self.sub_idx)
+            return g
+        if self.zero:
+            g[padding_mask_at(idx, self.zero)] = 0
+        if self.sub_idx.size:
+            hit = np.isin(idx, self.sub_idx)
+            if hit.any():
+                g[hit] = self._subnormals(j, step0, idx[hit])
+        return g
 
     # ---------------------------------------------------------- host twins
 
@@ -73,7 +107,7 @@ class DeviceCase:
 
     def host_grads(self, step0: int, idx=None):
         out = []
-        for k, ks in self.w.grad_keys(step0):
+        for j, (k, ks) in enumerate(self.w.grad_keys(step0)):
             if idx is None:
                 g = host_grad_bf16(self.S, k, ks, self.w.sigma_grad, self.w.kinds)
                 for o, n in self.pad:
@@ -81,5 +115,5 @@ class DeviceCase:
             else:
                 g = host_grad_bf16_at(idx, k, ks, self.w.sigma_grad, self.w.kinds)
                 g[padding_mask_at(idx, self.pad)] = 0
-            out.append(g)
+            out.append(self._override(g, j, step0, idx))
         return out

@@ -48,6 +48,9 @@ class Workload:
     align: int = ALIGN
     index: int = 0
     description: str = ""
+    # tensors whose gradient contributions are overridden in every step and
+    # every contribution: "zero" -> exact +0.0, "subnormal" -> bf16 subnormals
+    special: dict = field(default_factory=dict)
 
     @property
     def seed(self) -> int:
@@ -136,6 +139,8 @@ def workload(index: int, rank: Optional[int] = None) -> Workload:
                      description="10,000 tensors of 1..4096 + 64 x 4096x4096, shuffled; decay on "
                                  "matrices only; 1% x1e3 outliers, 5% zeros, 0.1% subnormals; "
                                  "fixed grads, global-norm clip 1.0, 1000 steps")
+        small = [t for t, d in enumerate(d) if d == 0]
+        w.special = {"zero": small[:16], "subnormal": small[16:32]}
     else:
         raise ValueError(f"no workload {index}")
     w.index = index
@@ -144,6 +149,21 @@ def workload(index: int, rank: Optional[int] = None) -> Workload:
             raise ValueError("rank out of range")
         w.rank = rank
     return w
+
+
+def special_ranges(w: Workload, segments):
+    """(shard offset, length, kind) of the overridden tensors' pieces in a shard.
+
+    segments: iterable of (shard_off, length, tensor) in shard order."""
+    kind_of = {}
+    for kind, ts in w.special.items():
+        for t in ts:
+            kind_of[t] = kind
+    out = []
+    for off, ln, t in segments:
+        if t in kind_of and ln > 0:
+            out.append((int(off), int(ln), kind_of[t]))
+    return out
 
 
 def scaled(w: Workload, numel: List[int], decay: Optional[List[int]] = None,

@@ -20,7 +20,7 @@ import synth
 from oracle import layout as L
 from sharded_optimizer_step_zero_amd import ZeroShard
 from synth.device_case import DeviceCase, padding_mask_at
-from synth.workloads import Workload
+from synth.workloads import Workload, special_ranges
 
 TOL_REL = 1e-6           # fp32 master, m, v: max relative error per step
 TINY = 2.0 ** -126
@@ -77,7 +77,8 @@ class Shard:
                             bucket_cap=w.bucket_cap, align=w.align, flags=flags)
         assert self.zs.shard_len == self.lay.shard_len
         self.S = self.lay.shard_len
-        self.case = DeviceCase(w, self.S, self.lay.padding_ranges(), self.zs.device)
+        special = special_ranges(w, [(x.shard_off, x.length, x.tensor) for x in self.lay.segments])
+        self.case = DeviceCase(w, self.S, self.lay.padding_ranges(), self.zs.device, special)
         self.case.fill_master(self.zs.master)
         torch.cuda.synchronize()
 

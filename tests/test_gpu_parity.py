@@ -84,8 +84,10 @@ def test_stress_clip_sampled():
     from oracle import layout as L
     w = workload(5)
     log(f"test_stress_clip_sampled: {w.description}")
+    from synth.workloads import special_ranges
     lay = L.plan(w.numel, w.decay, 1, 0, w.bucket_cap, w.align)
-    case = DeviceCase(w, lay.shard_len, lay.padding_ranges(), "cpu")
+    special = special_ranges(w, [(x.shard_off, x.length, x.tensor) for x in lay.segments])
+    case = DeviceCase(w, lay.shard_len, lay.padding_ranges(), "cpu", special)
     norms = {}
 
     def full_norm(step0):
@@ -96,7 +98,8 @@ def test_stress_clip_sampled():
         return norms[gs]
 
     from _gpu import sample_indices
-    idx = sample_indices(lay, n_windows=1024, edge=16)
+    idx = np.union1d(sample_indices(lay, n_windows=1024, edge=16),
+                     np.concatenate([np.arange(o, o + n) for o, n, _ in special]))
     log(f"  {idx.size:,} sampled elements")
     checks = {1, 2, 3, 10, 100, 500, 1000} | set(range(50, 1001, 50))
     _report(w.name, sampled_parity(w, w.steps, idx=idx, check_steps=checks,

@@ -77,3 +77,30 @@ def test_stress_workload_shapes():
     assert min(small) >= 1 and max(small) <= 4096
     assert all((d == 1) == (n == 4096 * 4096) for n, d in zip(w.numel, w.decay))
     assert workload(5).numel == w.numel   # seeded, reproducible
+
+
+def test_special_tensor_overrides_host_sampled_equals_whole():
+    from oracle import layout as L
+    from synth.device_case import DeviceCase
+    from synth.workloads import scaled, special_ranges
+    w = scaled(workload(5), [300, 4000, 70, 1000, 5], [0, 0, 0, 1, 0], M=3)
+    w.special = {"zero": [0, 2], "subnormal": [1]}
+    lay = L.plan(w.numel, w.decay, 1, 0, w.bucket_cap, w.align)
+    sp = special_ranges(w, [(s.shard_off, s.length, s.tensor) for s in lay.segments])
+    case = DeviceCase.__new__(DeviceCase)      # host twins only: no device buffers
+    case.w, case.S, case.pad = w, lay.shard_len, lay.padding_ranges()
+    case.zero = [(o, n) for o, n, k in sp if k == "zero"]
+    sub = [(o, n) for o, n, k in sp if k == "subnormal"]
+    case.sub_idx = np.concatenate([np.arange(o, o + n) for o, n in sub]).astype(np.int64)
+    whole = case.host_grads(0)
+    idx = np.arange(0, lay.shard_len, 7, dtype=np.int64)
+    at = case.host_grads(0, idx)
+    for a, b in zip(whole, at):
+        assert np.array_equal(a[idx], b)
+    for g in whole:
+        for o, n, k in sp:
+            piece = g[o:o + n]
+            if k == "zero":
+                assert not piece.any()
+            else:
+                assert ((piece & 0x7F80) == 0).all() and ((piece & 0x7F) != 0).all()
