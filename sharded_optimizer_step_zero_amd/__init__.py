@@ -187,17 +187,16 @@ def zero_shard_init(plan: int, M: int, param_bf16: int, master: int, exp_avg: in
 
 def zero_shard_step(ctx: int, grads: Sequence[int], lr: float, beta1: float, beta2: float,
                     eps: float, weight_decay: float, step: int, max_grad_norm: float = 0.0,
-                    want_norm: bool = False):
-    """Enqueues one step.  Returns the fp64 grad norm when want_norm (waits), else None."""
+                    want_norm: bool = False, return_code: bool = False):
+    """Enqueues one step.  Returns the fp64 grad norm when want_norm (the call then
+    waits), else None; with return_code, returns (code, norm) -- code is ZS_OK or
+    the warning ZS_NONFINITE.  Negative codes raise ZeroShardError."""
     arr = _ptr_array(grads)
-    if want_norm:
-        nrm = ctypes.c_double()
-        _check(_lib.zero_shard_step(ctx, arr, lr, beta1, beta2, eps, weight_decay, step,
-                                    max_grad_norm, ctypes.byref(nrm)))
-        return nrm.value
-    _check(_lib.zero_shard_step(ctx, arr, lr, beta1, beta2, eps, weight_decay, step,
-                                max_grad_norm, None))
-    return None
+    nrm = ctypes.c_double()
+    rc = _check(_lib.zero_shard_step(ctx, arr, lr, beta1, beta2, eps, weight_decay, step,
+                                     max_grad_norm, ctypes.byref(nrm) if want_norm else None))
+    norm = nrm.value if want_norm else None
+    return (rc, norm) if return_code else norm
 
 
 def zero_shard_grad_sumsq(ctx: int, grads: Sequence[int], sumsq_dev: int) -> None:
@@ -260,12 +259,12 @@ class ZeroShard:
         zero_shard_set_stream(self.ctx, stream)
 
     def step(self, grads, *, lr, beta1, beta2, eps, weight_decay, step, max_grad_norm=0.0,
-             want_norm=False):
+             want_norm=False, return_code=False):
         ptrs = [g if isinstance(g, int) else g.data_ptr() for g in grads]
         if len(ptrs) != self.M:
             raise ValueError(f"expected {self.M} gradient contributions")
         return zero_shard_step(self.ctx, ptrs, lr, beta1, beta2, eps, weight_decay, step,
-                               max_grad_norm, want_norm)
+                               max_grad_norm, want_norm, return_code)
 
     def segments(self):
         n = zs_plan_query(self.plan)["n_segments"]
