@@ -44,37 +44,48 @@ def build(verbose: bool = False) -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
-            raise RuntimeError(f"{LIB} is not built; run __graft_entry__.build()")
-        L = ctypes.CDLL(LIB)
-        vp, i64, i32, f32, f64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
-                                  ctypes.c_float, ctypes.c_double)
-        L.zo_bf16_to_f32_array.argtypes = [i64, vp, vp]
-        L.zo_bf16_to_f32_array.restype = None
-        L.zo_f32_to_bf16_array.argtypes = [i64, vp, vp]
-        L.zo_f32_to_bf16_array.restype = None
-        L.zo_set_threads.argtypes = [i32]
-        L.zo_set_threads.restype = None
-        L.zo_get_threads.argtypes = []
-        L.zo_get_threads.restype = i32
-        L.zo_scalars_f32_get.argtypes = [f32, f32, f32, f32, f32, i64, vp]
-        L.zo_scalars_f32_get.restype = None
-        L.zo_reduce_mean_f32.argtypes = [i64, i32, vp, vp]
-        L.zo_reduce_mean_f32.restype = None
-        L.zo_grad_sumsq.argtypes = [i64, i32, vp]
-        L.zo_grad_sumsq.restype = f64
-        L.zo_clip_coef.argtypes = [f64, f32]
-        L.zo_clip_coef.restype = f32
-        L.zo_coef_from_norm.argtypes = [f64, f32]
-        L.zo_coef_from_norm.restype = f32
-        L.zo_step_f32.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, f32, f32, f32, f32, f32,
-                                  i64, i32, f32]
-        L.zo_step_f32.restype = i32
-        L.zo_step_f64.argtypes = [i64, i32, vp, vp, vp, vp, vp, f64, f64, f64, f64, f64, i64,
-                                  i32, f64]
-        L.zo_step_f64.restype = i32
-        _lib = L
+        _lib = _load(LIB)
     return _lib
+
+
+def use_library(path: str = None) -> None:
+    """Point every function here at another build of zo.c (the mutation tests use
+    deliberately broken builds); None returns to libzo.so."""
+    global _lib
+    _lib = _load(path) if path else None
+
+
+def _load(path: str):
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    vp, i64, i32, f32, f64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                              ctypes.c_float, ctypes.c_double)
+    L.zo_bf16_to_f32_array.argtypes = [i64, vp, vp]
+    L.zo_bf16_to_f32_array.restype = None
+    L.zo_f32_to_bf16_array.argtypes = [i64, vp, vp]
+    L.zo_f32_to_bf16_array.restype = None
+    L.zo_set_threads.argtypes = [i32]
+    L.zo_set_threads.restype = None
+    L.zo_get_threads.argtypes = []
+    L.zo_get_threads.restype = i32
+    L.zo_scalars_f32_get.argtypes = [f32, f32, f32, f32, f32, i64, vp]
+    L.zo_scalars_f32_get.restype = None
+    L.zo_reduce_mean_f32.argtypes = [i64, i32, vp, vp]
+    L.zo_reduce_mean_f32.restype = None
+    L.zo_grad_sumsq.argtypes = [i64, i32, vp]
+    L.zo_grad_sumsq.restype = f64
+    L.zo_clip_coef.argtypes = [f64, f32]
+    L.zo_clip_coef.restype = f32
+    L.zo_coef_from_norm.argtypes = [f64, f32]
+    L.zo_coef_from_norm.restype = f32
+    L.zo_step_f32.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, f32, f32, f32, f32, f32,
+                              i64, i32, f32]
+    L.zo_step_f32.restype = i32
+    L.zo_step_f64.argtypes = [i64, i32, vp, vp, vp, vp, vp, f64, f64, f64, f64, f64, i64,
+                              i32, f64]
+    L.zo_step_f64.restype = i32
+    return L
 
 
 def set_threads(n: int) -> None:
