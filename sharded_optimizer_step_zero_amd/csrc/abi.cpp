@@ -25,7 +25,7 @@ struct zs_ctx {
   int32_t M = 0;
   uint32_t flags = 0;
   int64_t shard_len = 0;
-  int32_t n_runs = 0, n_partials = 0;
+  int32_t n_runs = 0;
   int32_t waves_per_cu = 0;
   uint16_t* param = nullptr;
   float* master = nullptr;
@@ -40,7 +40,7 @@ namespace {
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-zs::WorkspaceLayout workspace_layout(int64_t n_runs, int32_t n_partials) {
+zs::WorkspaceLayout workspace_layout(int64_t n_runs, int64_t n_partials) {
   zs::WorkspaceLayout l{};
   l.runs_off = 0;
   l.runs_bytes = (size_t)(n_runs + 1) * sizeof(zs::Run);
@@ -120,6 +120,10 @@ zs::ClipScalars* scalars(zs_ctx* ctx) {
   return reinterpret_cast<zs::ClipScalars*>(ctx->ws + ctx->lay.scalars_off);
 }
 double* partials(zs_ctx* ctx) { return reinterpret_cast<double*>(ctx->ws + ctx->lay.partials_off); }
+// the level-2 partials the finalize step sums
+const double* final_partials(zs_ctx* ctx) {
+  return partials(ctx) + zs::level1_partials(ctx->shard_len);
+}
 const zs::Run* run_table(zs_ctx* ctx) {
   return reinterpret_cast<const zs::Run*>(ctx->ws + ctx->lay.runs_off);
 }
@@ -148,7 +152,7 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   if (((uintptr_t)workspace & 255u) != 0)
     return einval("zero_shard_init: workspace must be 256-byte aligned");
   if (plan->runs.size() > 0x3fffffff) return einval("zero_shard_init: too many runs");
-  const int32_t n_partials = zs::sumsq_partials(plan->shard_len);
+  const int64_t n_partials = zs::sumsq_partials(plan->shard_len);
   const zs::WorkspaceLayout lay = workspace_layout((int64_t)plan->runs.size(), n_partials);
   if (workspace_bytes < lay.total) return einval("zero_shard_init: workspace too small");
   std::vector<zs::Run> table;
@@ -170,7 +174,6 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   c->flags = flags;
   c->shard_len = plan->shard_len;
   c->n_runs = (int32_t)(table.size() - 1);
-  c->n_partials = n_partials;
   c->waves_per_cu = default_waves_per_cu(M);
   c->param = static_cast<uint16_t*>(param_bf16);
   c->master = master;
@@ -202,11 +205,11 @@ int enqueue_step(zs_ctx* ctx, const zs::GradPtrs& g, const zs::StepConsts& k, bo
   zs::ClipScalars* sc = scalars(ctx);
   if (need_norm) {
     if (!external_sumsq) {
-      e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), ctx->n_partials,
-                           ctx->stream);
+      e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), ctx->stream);
       if (e != hipSuccess) return ehip("zero_shard_step: norm pass", e);
     }
-    e = zs::launch_finalize(partials(ctx), ctx->n_partials, external_sumsq, max_norm, clip ? 1 : 0,
+    e = zs::launch_finalize(final_partials(ctx), zs::final_partials(ctx->shard_len),
+                            external_sumsq, max_norm, clip ? 1 : 0,
                             (ctx->flags & ZS_SKIP_NONFINITE) ? 1 : 0, sc, ctx->stream);
     if (e != hipSuccess) return ehip("zero_shard_step: norm finalize", e);
   }
@@ -257,11 +260,10 @@ extern "C" int zero_shard_grad_sumsq(zs_ctx* ctx, const void* const* grads, doub
   int rc = gather_grads(ctx, grads, &g);
   if (rc) return rc;
   // an empty shard sums zero partials, which writes 0 (no memset: capture-safe)
-  const int32_t n_partials = ctx->shard_len ? ctx->n_partials : 0;
+  const int32_t n_final = ctx->shard_len ? zs::final_partials(ctx->shard_len) : 0;
   hipError_t e = hipSuccess;
-  if (n_partials)
-    e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), n_partials, ctx->stream);
-  if (e == hipSuccess) e = zs::launch_sumsq_total(partials(ctx), n_partials, sumsq_dev,
+  if (n_final) e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), ctx->stream);
+  if (e == hipSuccess) e = zs::launch_sumsq_total(final_partials(ctx), n_final, sumsq_dev,
                                                   ctx->stream);
   return e == hipSuccess ? ZS_OK : ehip("zero_shard_grad_sumsq", e);
 }

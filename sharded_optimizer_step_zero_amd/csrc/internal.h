@@ -44,7 +44,7 @@ struct GradPtrs {
 // Device workspace layout (offsets in bytes from the workspace base).
 struct WorkspaceLayout {
   size_t runs_off, runs_bytes;  // n_runs + 1 Run entries (the last is a sentinel)
-  size_t partials_off;          // n_partials doubles
+  size_t partials_off;          // sumsq_partials(shard_len) doubles
   size_t scalars_off;           // ClipScalars
   size_t total;
 };
@@ -58,12 +58,17 @@ struct ClipScalars {
   uint32_t pad[2];
 };
 
-// Number of fp64 partial sums (= workgroups) of the norm pass for a shard.
-int32_t sumsq_partials(int64_t shard_len);
+// fp64 partial sums of the norm pass: level-1 (one per 2048-element tile) followed
+// by level-2 (one per 8192 level-1 partials); the finalize step sums the level-2
+// ones, final_partials of them starting at level1_partials.
+int64_t level1_partials(int64_t shard_len);
+int64_t sumsq_partials(int64_t shard_len);
+int32_t final_partials(int64_t shard_len);
 
 // Kernel launchers (kernels.hip).  All enqueue on `stream`.
+// The norm pass over a non-empty shard: both partial levels into `partials`.
 hipError_t launch_sumsq(int M, const GradPtrs& g, int64_t shard_len, double* partials,
-                        int32_t n_partials, hipStream_t stream);
+                        hipStream_t stream);
 // Reduces the partials (or takes *external_sumsq when non-null) into *out.
 hipError_t launch_finalize(const double* partials, int32_t n_partials,
                            const double* external_sumsq, float max_norm, int clip,

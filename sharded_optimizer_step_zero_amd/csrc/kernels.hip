@@ -32,9 +32,10 @@
 // prescribes.
 //
 // The optional clip needs the global norm before any update, so it is a
-// separate read pass: sumsq_kernel recomputes g and accumulates g^2 in fp64
-// per lane, reduces each workgroup in a fixed order, and finalize_kernel adds
-// the per-workgroup partials in index order -- run-to-run deterministic.
+// separate read pass: sumsq_kernel recomputes g over 2048-element tiles and
+// accumulates g^2 in fp64 per lane, each workgroup sums in a fixed order,
+// sum_blocks_kernel adds fixed blocks of those partials, and finalize_kernel
+// adds the remaining few thousand in index order -- run-to-run deterministic.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -45,8 +46,10 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;  // 4 wave64s per workgroup
-constexpr int kVec = 8;        // elements per lane per iteration (one dwordx4 of bf16)
+constexpr int kThreads = 256;  // 4 wave64s per workgroup (norm pass)
+constexpr int kVec = 8;        // elements per lane in the norm pass (one dwordx4 of bf16)
+constexpr int64_t kNormTile = (int64_t)kThreads * kVec;
+constexpr int64_t kLevel2 = 8192;  // level-1 partials summed by one level-2 workgroup
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -197,23 +200,37 @@ __device__ __forceinline__ double block_sum(double x) {
   return t;
 }
 
+// Norm pass, level 1: one 2048-element tile per workgroup (in-order, short-lived
+// workgroups stream best); each lane squares its 8 averaged values in fp64 (the
+// square of an fp32 value is exact in fp64), the workgroup sums in a fixed order.
 template <int M>
-__global__ __launch_bounds__(kThreads) void sumsq_kernel(GradPtrs g, int64_t n_groups,
+__global__ __launch_bounds__(kThreads) void sumsq_kernel(GradPtrs g, int64_t n,
                                                          double* __restrict__ partials) {
+  const int64_t e = (int64_t)blockIdx.x * kNormTile + (int64_t)threadIdx.x * kVec;
   double acc = 0.0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t grp = (int64_t)blockIdx.x * kThreads + threadIdx.x; grp < n_groups;
-       grp += stride) {
+  if (e < n) {  // n is a multiple of 8
     float s[kVec];
-    reduce8<M>(g, grp * kVec, s);
+    reduce8<M>(g, e, s);
 #pragma unroll
     for (int q = 0; q < kVec; q++) {
       const double x = (double)s[q];
-      acc = acc + x * x;  // the square of an fp32 value is exact in fp64
+      acc = acc + x * x;
     }
   }
   const double t = block_sum(acc);
   if (threadIdx.x == 0) partials[blockIdx.x] = t;
+}
+
+// Norm pass, level 2: workgroup b sums partials [b*kLevel2, (b+1)*kLevel2) in a
+// fixed order (lane t takes t, t+256, ...; then the fixed workgroup sum).
+__global__ __launch_bounds__(kThreads) void sum_blocks_kernel(const double* __restrict__ in,
+                                                              int64_t n, double* __restrict__ out) {
+  const int64_t base = (int64_t)blockIdx.x * kLevel2;
+  const int64_t end = base + kLevel2 < n ? base + kLevel2 : n;
+  double acc = 0.0;
+  for (int64_t i = base + threadIdx.x; i < end; i += kThreads) acc = acc + in[i];
+  const double t = block_sum(acc);
+  if (threadIdx.x == 0) out[blockIdx.x] = t;
 }
 
 __device__ __forceinline__ double sum_partials(const double* __restrict__ partials, int32_t n) {
@@ -268,20 +285,34 @@ hipError_t launch_step_m(bool use_clip, const GradPtrs& g, float* master, float*
 
 template <int M>
 hipError_t launch_sumsq_m(const GradPtrs& g, int64_t shard_len, double* partials,
-                          int32_t n_partials, hipStream_t stream) {
-  hipLaunchKernelGGL((sumsq_kernel<M>), dim3((unsigned)n_partials), dim3(kThreads), 0, stream,
-                     g, shard_len / kVec, partials);
+                          hipStream_t stream) {
+  const int64_t p1 = (shard_len + kNormTile - 1) / kNormTile;
+  hipLaunchKernelGGL((sumsq_kernel<M>), dim3((unsigned)p1), dim3(kThreads), 0, stream, g,
+                     shard_len, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t p2 = (p1 + kLevel2 - 1) / kLevel2;
+  hipLaunchKernelGGL(sum_blocks_kernel, dim3((unsigned)p2), dim3(kThreads), 0, stream,
+                     partials, p1, partials + p1);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int32_t sumsq_partials(int64_t shard_len) {
-  int64_t groups = shard_len / kVec;
-  int64_t wg = (groups + kThreads - 1) / kThreads;
-  if (wg > 2048) wg = 2048;
-  if (wg < 1) wg = 1;
-  return (int32_t)wg;
+// Level-1 plus level-2 partials of the norm pass; the level-2 ones (at most a few
+// thousand) start at offset level1_partials(shard_len) and feed the finalize step.
+int64_t level1_partials(int64_t shard_len) {
+  const int64_t p1 = (shard_len + kNormTile - 1) / kNormTile;
+  return p1 > 0 ? p1 : 1;
+}
+
+int64_t sumsq_partials(int64_t shard_len) {
+  const int64_t p1 = level1_partials(shard_len);
+  return p1 + (p1 + kLevel2 - 1) / kLevel2;
+}
+
+int32_t final_partials(int64_t shard_len) {
+  return (int32_t)((level1_partials(shard_len) + kLevel2 - 1) / kLevel2);
 }
 
 #define ZS_DISPATCH_M(M_, CALL) \
@@ -323,8 +354,9 @@ hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, f
 }
 
 hipError_t launch_sumsq(int M, const GradPtrs& g, int64_t shard_len, double* partials,
-                        int32_t n_partials, hipStream_t stream) {
-#define ZS_CALL_SUMSQ(X) launch_sumsq_m<X>(g, shard_len, partials, n_partials, stream)
+                        hipStream_t stream) {
+  if (shard_len <= 0 || level1_partials(shard_len) > 0x7fffffff) return hipErrorInvalidValue;
+#define ZS_CALL_SUMSQ(X) launch_sumsq_m<X>(g, shard_len, partials, stream)
   ZS_DISPATCH_M(M, ZS_CALL_SUMSQ)
 #undef ZS_CALL_SUMSQ
 }
