@@ -59,9 +59,8 @@ int32_t default_waves_per_cu(int32_t M) {
     const long v = strtol(env, nullptr, 10);
     if (v == 0 || (v >= 3 && v <= 64)) return (int32_t)v;
   }
-  if (M >= 6) return 7;
-  if (M >= 2) return 8;
-  return 10;
+  if (M >= 6) return 9;
+  return 12;
 }
 
 int einval(const char* msg) {
