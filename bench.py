@@ -88,6 +88,31 @@ def cpu_baseline(w, slab: int, min_seconds: float = 10.0) -> dict:
                       f"(M={w.M}{', with the norm pass' if clip else ''}), {el:.1f} s"}
 
 
+def time_checkpoint(zs, w, stream, reps: int = 10) -> dict:
+    """Export and import of this rank's fp32 state to/from the canonical order:
+    12 B read + 12 B written per shard parameter (import also writes the 2-byte
+    bf16 param)."""
+    import torch
+    total = w.total_params
+    canon = [torch.zeros(total, dtype=torch.float32, device=zs.device) for _ in range(3)]
+    out = {}
+    for name, fn, nbytes in (("export", zs.export_state, 24), ("import", zs.import_state, 26)):
+        fn(*canon)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn(*canon)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": ms, "bytes_per_param": nbytes,
+                     "gbs": zs.shard_len * nbytes / (ms * 1e-3) / 1e9}
+    del canon
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +122,8 @@ def main():
                     help="1 tiny, 2 GPT-1.3B 1/8 shard (default), 3 Llama-6.7B, "
                          "4 Llama-70B 1/16 shard, 5 stress with clip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--checkpoint", action="store_true",
+                    help="also time the state export/import used for checkpoints and resharding")
     ap.add_argument("--cpu-slab", type=int, default=1 << 25)
     ap.add_argument("--calibrate-copy-gib", type=float, default=1.0,
                     help="size of the plain copy run once before timing (counter calibration)")
@@ -217,6 +244,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.checkpoint:
+        out["checkpoint"] = time_checkpoint(zs, w, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_slab, S))
     print(json.dumps(out), flush=True)

@@ -131,8 +131,8 @@ int zs_plan_state_bytes(const zs_plan *plan, int32_t stage, int64_t *bytes);
 
 void zs_plan_destroy(zs_plan *plan);
 
-/* Device workspace a context of this plan needs (run table, norm partials,
- * clip coefficient), in bytes; 0 if plan is NULL.  M is accepted for forward
+/* Device workspace a context of this plan needs (run table, piece table, norm
+ * partials, clip coefficient), in bytes; 0 if plan is NULL.  M is accepted for forward
  * compatibility and does not change the size. */
 size_t zs_workspace_bytes(const zs_plan *plan, int32_t M);
 
@@ -186,6 +186,28 @@ int zero_shard_grad_sumsq(zs_ctx *ctx, const void *const *grads, double *sumsq_d
 int zero_shard_step_global_norm(zs_ctx *ctx, const void *const *grads, float lr, float beta1,
                                 float beta2, float eps, float weight_decay, int64_t step,
                                 float max_grad_norm, const double *global_sumsq_dev);
+
+/*
+ * Checkpoint / resharding.  The canonical state is every tensor's fp32 values
+ * contiguous and unpadded, tensors in forward order (sum of numel elements per
+ * array) -- independent of world_size, rank and bucket layout.  Saving it and
+ * the step count is a checkpoint; exporting from N contexts and importing into
+ * N' contexts of another plan over the same tensor list reshards (ZeRO shards
+ * must be merged to resume on another card count: CS324 notes, exercise 11).
+ * Each rank touches only the elements it owns; over all ranks of a plan the
+ * pieces cover the canonical arrays exactly once.
+ *
+ * export: copies this rank's master, exp_avg, exp_avg_sq into the canonical
+ *   device arrays.  import: the reverse, and also writes param_bf16 =
+ *   bf16_rne(master) for the imported elements; padding is not touched.
+ * Canonical pointers are device pointers to sum(numel) floats each (may be
+ * NULL only when the model is empty).  Enqueued on the context's stream.
+ * Errors: ZS_EINVAL, ZS_EHIP.
+ */
+int zero_shard_export_state(zs_ctx *ctx, float *canon_master, float *canon_exp_avg,
+                            float *canon_exp_avg_sq);
+int zero_shard_import_state(zs_ctx *ctx, const float *canon_master, const float *canon_exp_avg,
+                            const float *canon_exp_avg_sq);
 
 /* The bf16 parameter shard (the all-gather send buffer) and its length. */
 int zero_shard_params(zs_ctx *ctx, const void **param_bf16, int64_t *shard_len);

@@ -65,6 +65,7 @@ class Layout:
     padded_total: int
     segments: List[Segment]
     total_params: int
+    numel: List[int] = None
 
     def decay_mask(self) -> np.ndarray:
         mask = np.zeros(self.shard_len, dtype=np.uint8)
@@ -75,6 +76,31 @@ class Layout:
 
     def padding_ranges(self) -> List[Tuple[int, int]]:
         return [(s.shard_off, s.length) for s in self.segments if s.tensor < 0]
+
+    def canonical_offsets(self) -> List[int]:
+        """Offset of each tensor in the canonical order: tensors concatenated in
+        forward order without padding (the layout-independent checkpoint format)."""
+        out, acc = [], 0
+        for n in self.numel:
+            out.append(acc)
+            acc += n
+        return out
+
+    def to_canonical(self, shard: np.ndarray, canon: np.ndarray) -> None:
+        """Write this rank's tensor elements of a shard array into a canonical array."""
+        co = self.canonical_offsets()
+        for s in self.segments:
+            if s.tensor >= 0:
+                c = co[s.tensor] + s.tensor_off
+                canon[c:c + s.length] = shard[s.shard_off:s.shard_off + s.length]
+
+    def from_canonical(self, canon: np.ndarray, shard: np.ndarray) -> None:
+        """The reverse of to_canonical; padding is left as it is."""
+        co = self.canonical_offsets()
+        for s in self.segments:
+            if s.tensor >= 0:
+                c = co[s.tensor] + s.tensor_off
+                shard[s.shard_off:s.shard_off + s.length] = canon[c:c + s.length]
 
     def tensor_slice(self, t: int) -> Tuple[int, int, int]:
         """(shard offset, offset inside tensor, length) of tensor t on this rank."""
@@ -161,4 +187,4 @@ def plan(numel, decay, world_size: int, rank: int, bucket_cap: int = 25_000_000,
 
     padded_total = buckets[-1][0] + buckets[-1][1] if buckets else 0
     return Layout(world_size, rank, align, bucket_cap, flat_off, which, buckets, shard_off,
-                  padded_total, merged, sum(numel))
+                  padded_total, merged, sum(numel), list(numel))

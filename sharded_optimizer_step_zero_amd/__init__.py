@@ -71,6 +71,8 @@ _sig("zero_shard_step", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _i
 _sig("zero_shard_grad_sumsq", ctypes.c_int, _vp, _vp, _vp)
 _sig("zero_shard_step_global_norm", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _i64,
      _f32, _vp)
+_sig("zero_shard_export_state", ctypes.c_int, _vp, _vp, _vp, _vp)
+_sig("zero_shard_import_state", ctypes.c_int, _vp, _vp, _vp, _vp)
 _sig("zero_shard_params", ctypes.c_int, _vp, _P(_vp), _P(_i64))
 _sig("zero_shard_set_stream", ctypes.c_int, _vp, _vp)
 _sig("zero_shard_destroy", None, _vp)
@@ -79,7 +81,8 @@ _sig("zero_shard_last_error", ctypes.c_char_p)
 EXPORTED = ["zs_plan_create", "zs_plan_query", "zs_plan_tensor_slice", "zs_plan_segment",
             "zs_plan_bucket", "zs_plan_run", "zs_plan_state_bytes", "zs_plan_destroy",
             "zs_workspace_bytes", "zero_shard_init", "zero_shard_step", "zero_shard_grad_sumsq",
-            "zero_shard_step_global_norm", "zero_shard_params", "zero_shard_set_stream",
+            "zero_shard_step_global_norm", "zero_shard_export_state", "zero_shard_import_state",
+            "zero_shard_params", "zero_shard_set_stream",
             "zero_shard_destroy", "zero_shard_last_error"]
 
 
@@ -211,6 +214,18 @@ def zero_shard_step_global_norm(ctx: int, grads: Sequence[int], lr: float, beta1
                                             global_sumsq_dev))
 
 
+def zero_shard_export_state(ctx: int, canon_master: int, canon_exp_avg: int,
+                            canon_exp_avg_sq: int) -> None:
+    _check(_lib.zero_shard_export_state(ctx, canon_master or None, canon_exp_avg or None,
+                                        canon_exp_avg_sq or None))
+
+
+def zero_shard_import_state(ctx: int, canon_master: int, canon_exp_avg: int,
+                            canon_exp_avg_sq: int) -> None:
+    _check(_lib.zero_shard_import_state(ctx, canon_master or None, canon_exp_avg or None,
+                                        canon_exp_avg_sq or None))
+
+
 def zero_shard_params(ctx: int):
     p, n = ctypes.c_void_p(), ctypes.c_int64()
     _check(_lib.zero_shard_params(ctx, ctypes.byref(p), ctypes.byref(n)))
@@ -265,6 +280,15 @@ class ZeroShard:
             raise ValueError(f"expected {self.M} gradient contributions")
         return zero_shard_step(self.ctx, ptrs, lr, beta1, beta2, eps, weight_decay, step,
                                max_grad_norm, want_norm, return_code)
+
+    def export_state(self, canon_master, canon_exp_avg, canon_exp_avg_sq):
+        """Copy this rank's state into canonical device tensors (sum(numel) floats each)."""
+        zero_shard_export_state(self.ctx, canon_master.data_ptr(), canon_exp_avg.data_ptr(),
+                                canon_exp_avg_sq.data_ptr())
+
+    def import_state(self, canon_master, canon_exp_avg, canon_exp_avg_sq):
+        zero_shard_import_state(self.ctx, canon_master.data_ptr(), canon_exp_avg.data_ptr(),
+                                canon_exp_avg_sq.data_ptr())
 
     def segments(self):
         n = zs_plan_query(self.plan)["n_segments"]

@@ -24,7 +24,7 @@ void set_error(const std::string& msg) { g_last_error = msg; }
 struct zs_ctx {
   int32_t M = 0;
   uint32_t flags = 0;
-  int64_t shard_len = 0;
+  int64_t shard_len = 0, n_pieces = 0, canon_len = 0;
   int32_t n_runs = 0;
   int32_t waves_per_cu = 0;
   uint16_t* param = nullptr;
@@ -40,11 +40,13 @@ namespace {
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-zs::WorkspaceLayout workspace_layout(int64_t n_runs, int64_t n_partials) {
+zs::WorkspaceLayout workspace_layout(int64_t n_runs, int64_t n_pieces, int64_t n_partials) {
   zs::WorkspaceLayout l{};
   l.runs_off = 0;
   l.runs_bytes = (size_t)(n_runs + 1) * sizeof(zs::Run);
-  l.partials_off = round256(l.runs_bytes);
+  l.pieces_off = round256(l.runs_bytes);
+  l.pieces_bytes = (size_t)n_pieces * sizeof(zs::Piece);
+  l.partials_off = l.pieces_off + round256(l.pieces_bytes);
   l.scalars_off = l.partials_off + round256((size_t)n_partials * sizeof(double));
   l.total = l.scalars_off + round256(sizeof(zs::ClipScalars));
   return l;
@@ -132,7 +134,9 @@ const zs::Run* run_table(zs_ctx* ctx) {
 extern "C" size_t zs_workspace_bytes(const zs_plan* plan, int32_t M) {
   (void)M;
   if (!plan) return 0;
-  return workspace_layout((int64_t)plan->runs.size(), zs::sumsq_partials(plan->shard_len)).total;
+  return workspace_layout((int64_t)plan->runs.size(), (int64_t)plan->pieces.size(),
+                          zs::sumsq_partials(plan->shard_len))
+      .total;
 }
 
 extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, void* param_bf16,
@@ -152,7 +156,8 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
     return einval("zero_shard_init: workspace must be 256-byte aligned");
   if (plan->runs.size() > 0x3fffffff) return einval("zero_shard_init: too many runs");
   const int64_t n_partials = zs::sumsq_partials(plan->shard_len);
-  const zs::WorkspaceLayout lay = workspace_layout((int64_t)plan->runs.size(), n_partials);
+  const zs::WorkspaceLayout lay =
+      workspace_layout((int64_t)plan->runs.size(), (int64_t)plan->pieces.size(), n_partials);
   if (workspace_bytes < lay.total) return einval("zero_shard_init: workspace too small");
   std::vector<zs::Run> table;
   try {
@@ -173,6 +178,8 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   c->flags = flags;
   c->shard_len = plan->shard_len;
   c->n_runs = (int32_t)(table.size() - 1);
+  c->n_pieces = (int64_t)plan->pieces.size();
+  c->canon_len = plan->total_params;
   c->waves_per_cu = default_waves_per_cu(M);
   c->param = static_cast<uint16_t*>(param_bf16);
   c->master = master;
@@ -185,10 +192,13 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
     hipError_t e = hipMemcpyAsync(c->ws + lay.runs_off, table.data(),
                                   table.size() * sizeof(zs::Run), hipMemcpyHostToDevice,
                                   c->stream);
+    if (e == hipSuccess && lay.pieces_bytes)
+      e = hipMemcpyAsync(c->ws + lay.pieces_off, plan->pieces.data(), lay.pieces_bytes,
+                         hipMemcpyHostToDevice, c->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
     if (e != hipSuccess) {
       delete c;
-      return ehip("zero_shard_init: run table upload", e);
+      return ehip("zero_shard_init: table upload", e);
     }
   }
   *out = c;
@@ -283,6 +293,33 @@ extern "C" int zero_shard_step_global_norm(zs_ctx* ctx, const void* const* grads
   if (ctx->shard_len == 0) return ZS_OK;
   const zs::StepConsts k = step_consts(lr, beta1, beta2, eps, weight_decay, step);
   return enqueue_step(ctx, g, k, true, true, max_grad_norm, global_sumsq_dev);
+}
+
+namespace {
+
+int state_copy(zs_ctx* ctx, bool do_export, float* cm, float* cmm, float* cv, const char* who) {
+  if (!ctx) return einval((std::string(who) + ": ctx is NULL").c_str());
+  if (ctx->canon_len > 0 && (!cm || !cmm || !cv))
+    return einval((std::string(who) + ": canonical buffers must be non-NULL").c_str());
+  const hipError_t e = zs::launch_state_copy(
+      do_export, reinterpret_cast<const zs::Piece*>(ctx->ws + ctx->lay.pieces_off),
+      ctx->n_pieces, ctx->master, ctx->m, ctx->v, ctx->param, cm, cmm, cv, ctx->stream);
+  return e == hipSuccess ? ZS_OK : ehip(who, e);
+}
+
+}  // namespace
+
+extern "C" int zero_shard_export_state(zs_ctx* ctx, float* canon_master, float* canon_exp_avg,
+                                       float* canon_exp_avg_sq) {
+  return state_copy(ctx, true, canon_master, canon_exp_avg, canon_exp_avg_sq,
+                    "zero_shard_export_state");
+}
+
+extern "C" int zero_shard_import_state(zs_ctx* ctx, const float* canon_master,
+                                       const float* canon_exp_avg,
+                                       const float* canon_exp_avg_sq) {
+  return state_copy(ctx, false, const_cast<float*>(canon_master), const_cast<float*>(canon_exp_avg),
+                    const_cast<float*>(canon_exp_avg_sq), "zero_shard_import_state");
 }
 
 extern "C" int zero_shard_params(zs_ctx* ctx, const void** param_bf16, int64_t* shard_len) {

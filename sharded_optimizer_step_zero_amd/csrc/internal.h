@@ -24,6 +24,16 @@ struct Segment {
   int32_t decay;
 };
 
+// A piece of a tensor segment (at most kPieceElems elements) for the state
+// export/import kernel: shard offset, offset in the canonical order (tensors
+// concatenated without padding), length.
+struct Piece {
+  int64_t shard_off, canon_off;
+  int32_t len, pad;
+};
+static_assert(sizeof(Piece) == 24, "piece descriptor is 24 bytes");
+constexpr int64_t kPieceElems = 65536;
+
 // Per-step constants, each computed in fp64 from the fp32 hyper-parameters
 // and rounded once to fp32.
 struct StepConsts {
@@ -44,6 +54,7 @@ struct GradPtrs {
 // Device workspace layout (offsets in bytes from the workspace base).
 struct WorkspaceLayout {
   size_t runs_off, runs_bytes;  // n_runs + 1 Run entries (the last is a sentinel)
+  size_t pieces_off, pieces_bytes;  // n_pieces Piece entries
   size_t partials_off;          // sumsq_partials(shard_len) doubles
   size_t scalars_off;           // ClipScalars
   size_t total;
@@ -76,6 +87,12 @@ hipError_t launch_finalize(const double* partials, int32_t n_partials,
 hipError_t launch_sumsq_total(const double* partials, int32_t n_partials, double* out,
                               hipStream_t stream);
 // waves_per_cu > 0 caps the resident waves per CU of the step kernel (0: no cap).
+// Copies fp32 master/m/v between the shard and the canonical order over the
+// piece table (export: shard -> canonical; import: canonical -> shard, which
+// also writes param = bf16_rne(master) for the imported elements).
+hipError_t launch_state_copy(bool do_export, const Piece* pieces, int64_t n_pieces,
+                             float* master, float* m, float* v, uint16_t* param, float* c_master,
+                             float* c_m, float* c_v, hipStream_t stream);
 hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, float* m,
                        float* v, uint16_t* param, int64_t shard_len, const Run* runs,
                        int32_t n_runs, const ClipScalars* clip, const StepConsts& k,
@@ -93,5 +110,6 @@ struct zs_plan {
   std::vector<int64_t> bucket_off, bucket_len;
   std::vector<zs::Segment> segments;
   std::vector<zs::Run> runs;
+  std::vector<zs::Piece> pieces;
   int64_t shard_len = 0, padded_total = 0, total_params = 0;
 };

@@ -275,6 +275,31 @@ __global__ __launch_bounds__(kThreads) void sumsq_total_kernel(const double* __r
   if (threadIdx.x == 0) *out = t;
 }
 
+// State export/import: one workgroup per piece (at most 65536 elements), the
+// lanes striding over it; the canonical side has no alignment guarantee, so
+// accesses are 4 bytes wide (still coalesced 256 B per wave).
+template <bool EXPORT>
+__global__ __launch_bounds__(kThreads) void state_copy_kernel(
+    const Piece* __restrict__ pieces, float* __restrict__ master, float* __restrict__ mom1,
+    float* __restrict__ mom2, uint16_t* __restrict__ param, float* __restrict__ c_master,
+    float* __restrict__ c_m, float* __restrict__ c_v) {
+  const Piece pc = pieces[blockIdx.x];
+  for (int32_t i = threadIdx.x; i < pc.len; i += kThreads) {
+    const int64_t s = pc.shard_off + i, c = pc.canon_off + i;
+    if (EXPORT) {
+      c_master[c] = master[s];
+      c_m[c] = mom1[s];
+      c_v[c] = mom2[s];
+    } else {
+      const float p = c_master[c];
+      master[s] = p;
+      mom1[s] = c_m[c];
+      mom2[s] = c_v[c];
+      param[s] = (uint16_t)to_bf16(p);
+    }
+  }
+}
+
 template <int M>
 hipError_t launch_step_m(bool use_clip, const GradPtrs& g, float* master, float* m, float* v,
                          uint16_t* param, int64_t n, const Run* runs, int32_t n_runs,
@@ -367,6 +392,20 @@ hipError_t launch_sumsq(int M, const GradPtrs& g, int64_t shard_len, double* par
 #define ZS_CALL_SUMSQ(X) launch_sumsq_m<X>(g, shard_len, partials, stream)
   ZS_DISPATCH_M(M, ZS_CALL_SUMSQ)
 #undef ZS_CALL_SUMSQ
+}
+
+hipError_t launch_state_copy(bool do_export, const Piece* pieces, int64_t n_pieces,
+                             float* master, float* m, float* v, uint16_t* param, float* c_master,
+                             float* c_m, float* c_v, hipStream_t stream) {
+  if (n_pieces <= 0) return hipSuccess;
+  if (n_pieces > 0x7fffffff) return hipErrorInvalidValue;
+  if (do_export)
+    hipLaunchKernelGGL(state_copy_kernel<true>, dim3((unsigned)n_pieces), dim3(kThreads), 0,
+                       stream, pieces, master, m, v, param, c_master, c_m, c_v);
+  else
+    hipLaunchKernelGGL(state_copy_kernel<false>, dim3((unsigned)n_pieces), dim3(kThreads), 0,
+                       stream, pieces, master, m, v, param, c_master, c_m, c_v);
+  return hipGetLastError();
 }
 
 hipError_t launch_finalize(const double* partials, int32_t n_partials,

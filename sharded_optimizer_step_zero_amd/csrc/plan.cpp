@@ -21,6 +21,9 @@
 //     is a tensor start, hence a multiple of `align`.  The step kernel tiles
 //     the flat shard uniformly and looks each tile's flag up in this table,
 //     so thousands of mixed-size tensors cost one launch and a short search.
+//  6. Pieces: the tensor segments again, with their offsets in the canonical
+//     order (every tensor contiguous and unpadded, in forward order) -- the
+//     format a checkpoint stores, independent of N and of the bucket layout.
 #include <string.h>
 
 #include <algorithm>
@@ -164,6 +167,18 @@ extern "C" int zs_plan_create(const int64_t* numel, const uint8_t* decay, int64_
 
     // 5. weight-decay runs
     build_runs(*p);
+
+    // 6. pieces for state export/import: each tensor segment, cut into at most
+    //    kPieceElems elements, with its offset in the canonical order
+    std::vector<int64_t> canon(n_tensors, 0);
+    for (int64_t t = 1; t < n_tensors; t++) canon[t] = canon[t - 1] + numel[t - 1];
+    for (const zs::Segment& s : p->segments) {
+      if (s.tensor < 0) continue;
+      for (int64_t o = 0; o < s.len; o += zs::kPieceElems) {
+        const int64_t len = std::min(zs::kPieceElems, s.len - o);
+        p->pieces.push_back({s.shard_off + o, canon[s.tensor] + s.tensor_off + o, (int32_t)len, 0});
+      }
+    }
   } catch (const std::bad_alloc&) {
     delete p;
     zs::set_error("zs_plan_create: out of host memory");

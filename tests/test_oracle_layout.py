@@ -135,3 +135,31 @@ def test_gpt_buckets():
     lay = L.plan(w.numel, w.decay, 8, 0, w.bucket_cap, w.align)
     assert len(lay.buckets) == 73
     assert all(bl <= w.bucket_cap or bl == 50304 * 2048 for _, bl in lay.buckets)
+
+
+@pytest.mark.parametrize("N", [1, 3, 8])
+def test_canonical_mapping_partitions_the_model(N):
+    """Over all ranks, the shards' tensor elements map onto the canonical order
+    (tensors concatenated, unpadded) exactly once, and back."""
+    numel = [1, 63, 64, 65, 1000, 0, 4097, 12_345, 7, 30_001, 3]
+    decay = [i % 2 for i in range(len(numel))]
+    canon_want = np.concatenate([np.full(n, t, np.int64) * 100_000 + np.arange(n)
+                                 for t, n in enumerate(numel)])
+    got = np.full(canon_want.size, -1, np.int64)
+    seen = np.zeros(canon_want.size, np.int64)
+    for r in range(N):
+        lay = L.plan(numel, decay, N, r, 20_000, 64)
+        shard = np.full(lay.shard_len, -7, np.int64)
+        for s in lay.segments:
+            if s.tensor >= 0:
+                shard[s.shard_off:s.shard_off + s.length] = \
+                    s.tensor * 100_000 + np.arange(s.tensor_off, s.tensor_off + s.length)
+        part = np.full(canon_want.size, -1, np.int64)
+        lay.to_canonical(shard, part)
+        seen += part >= 0
+        got[part >= 0] = part[part >= 0]
+        back = np.full(lay.shard_len, -7, np.int64)
+        lay.from_canonical(canon_want, back)
+        assert np.array_equal(back, shard)
+    assert (seen == 1).all()
+    assert np.array_equal(got, canon_want)
