@@ -85,6 +85,23 @@ def _load(path: str):
     L.zo_step_f64.argtypes = [i64, i32, vp, vp, vp, vp, vp, f64, f64, f64, f64, f64, i64,
                               i32, f64]
     L.zo_step_f64.restype = i32
+    L.zo_f16_to_f32_array.argtypes = [i64, vp, vp]
+    L.zo_f16_to_f32_array.restype = None
+    L.zo_f32_to_f16_array.argtypes = [i64, vp, vp]
+    L.zo_f32_to_f16_array.restype = None
+    L.zo_pow_int.argtypes = [f64, i64]
+    L.zo_pow_int.restype = f64
+    L.zo_inv_scale.argtypes = [f32]
+    L.zo_inv_scale.restype = f32
+    L.zo_reduce_mean_f16.argtypes = [i64, i32, vp, f32, vp]
+    L.zo_reduce_mean_f16.restype = None
+    L.zo_grad_sumsq_f16.argtypes = [i64, i32, vp, f32]
+    L.zo_grad_sumsq_f16.restype = f64
+    L.zo_step_f16.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, f32, f32, f32, f32, f32, i64,
+                              f32, i32, f32]
+    L.zo_step_f16.restype = i32
+    L.zo_scaler_update.argtypes = [vp, vp, i32, f32, f32, i32]
+    L.zo_scaler_update.restype = None
     return L
 
 
@@ -128,6 +145,10 @@ def step_scalars_f32(lr, beta1, beta2, eps, wd, t) -> dict:
     lib().zo_scalars_f32_get(lr, beta1, beta2, eps, wd, int(t), out.ctypes.data)
     names = ["beta1", "beta2", "c1", "c2", "alpha", "bhat", "eps", "decay_mul"]
     return dict(zip(names, out.tolist()))
+
+
+def pow_int(b: float, t: int) -> float:
+    return float(lib().zo_pow_int(float(b), int(t)))
 
 
 def reduce_mean_f32(grads) -> np.ndarray:
@@ -190,3 +211,93 @@ def step_f64(grads, master, m, v, decay=None, *, lr, beta1, beta2, eps, weight_d
                            0 if coef is None else 1, 0.0 if coef is None else float(coef))
     if rc != 0:
         raise ValueError("zo_step_f64 rejected its arguments")
+
+
+# ------------------------------------------- fp16 with dynamic loss scaling
+
+
+def f16_to_f32(h: np.ndarray) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.size, dtype=np.float32)
+    lib().zo_f16_to_f32_array(h.size, h.ctypes.data, out.ctypes.data)
+    return out.reshape(h.shape)
+
+
+def f32_to_f16(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.size, dtype=np.uint16)
+    lib().zo_f32_to_f16_array(x.size, x.ctypes.data, out.ctypes.data)
+    return out.reshape(x.shape)
+
+
+def inv_scale(scale: float) -> np.float32:
+    return np.float32(lib().zo_inv_scale(float(scale)))
+
+
+def reduce_mean_f16(grads, inv: float) -> np.ndarray:
+    gs, n = _grads_u16(grads)
+    out = np.empty(n, dtype=np.float32)
+    lib().zo_reduce_mean_f16(n, len(gs), _ptr_array(gs), float(inv), out.ctypes.data)
+    return out
+
+
+def grad_sumsq_f16(grads, inv: float) -> float:
+    gs, n = _grads_u16(grads)
+    return float(lib().zo_grad_sumsq_f16(n, len(gs), _ptr_array(gs), float(inv)))
+
+
+def step_f16(grads, master, m, v, param=None, decay=None, *, lr, beta1, beta2, eps,
+             weight_decay, step, inv_scale, coef=None):
+    """One fp32 step on fp16 contributions (uint16 fp16 patterns), unscaled by
+    inv_scale; writes the fp16 param copy when given."""
+    gs, n = _grads_u16(grads)
+    for a in (master, m, v):
+        if a.dtype != np.float32 or not a.flags.c_contiguous or a.size != n:
+            raise ValueError("master/m/v must be contiguous float32 of the shard length")
+    if decay is not None:
+        decay = np.ascontiguousarray(decay, dtype=np.uint8)
+    rc = lib().zo_step_f16(n, len(gs), _ptr_array(gs), master.ctypes.data, m.ctypes.data,
+                           v.ctypes.data, None if param is None else param.ctypes.data,
+                           None if decay is None else decay.ctypes.data, lr, beta1, beta2, eps,
+                           weight_decay, int(step), float(inv_scale), 0 if coef is None else 1,
+                           0.0 if coef is None else float(coef))
+    if rc != 0:
+        raise ValueError("zo_step_f16 rejected its arguments")
+
+
+class Scaler:
+    """Dynamic loss-scale state: fp32 scale, int32 growth count, and the number of
+    optimizer steps actually applied (skipped steps do not count, so the bias
+    correction of the next applied step uses t = applied + 1)."""
+
+    def __init__(self, scale=65536.0, growth_factor=2.0, backoff_factor=0.5, growth_interval=2000):
+        self.scale = np.array([scale], np.float32)
+        self.tracker = np.array([0], np.int32)
+        self.applied = 0
+        self.growth_factor = growth_factor
+        self.backoff_factor = backoff_factor
+        self.growth_interval = growth_interval
+
+    def update(self, found_inf: bool) -> None:
+        lib().zo_scaler_update(self.scale.ctypes.data, self.tracker.ctypes.data,
+                               1 if found_inf else 0, self.growth_factor, self.backoff_factor,
+                               self.growth_interval)
+
+
+def amp_step(grads, master, m, v, param, decay, scaler: Scaler, *, lr, beta1, beta2, eps,
+             weight_decay, max_grad_norm=0.0):
+    """The whole fp16 step: unscale, found-inf (a non-finite sum of squares of the
+    unscaled average), optional clip on the unscaled norm, the update (at
+    t = applied + 1) unless found-inf, then the scale update.
+    Returns (found_inf, norm)."""
+    inv = inv_scale(float(scaler.scale[0]))
+    sumsq = grad_sumsq_f16(grads, inv)
+    found_inf = not np.isfinite(sumsq)
+    norm = float(np.sqrt(sumsq)) if np.isfinite(sumsq) else float("nan")
+    if not found_inf:
+        coef = coef_from_norm(norm, max_grad_norm) if max_grad_norm > 0 else None
+        step_f16(grads, master, m, v, param, decay, lr=lr, beta1=beta1, beta2=beta2, eps=eps,
+                 weight_decay=weight_decay, step=scaler.applied + 1, inv_scale=inv, coef=coef)
+        scaler.applied += 1
+    scaler.update(found_inf)
+    return found_inf, norm

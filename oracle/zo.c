@@ -34,12 +34,21 @@
  * fast-math, on SSE (no x87 excess precision), and subnormals are kept.
  * The host scalars (1-beta, bias corrections, lr/bc1, sqrt(bc2), 1-lr*wd)
  * are computed in fp64 from the fp32 hyper-parameters and rounded once to
- * fp32.  zo_step_f64 runs the same formula entirely in fp64; it exists only
+ * fp32; beta^t is taken by fp64 binary powering (zo_pow_int).  zo_step_f64 runs the same formula entirely in fp64; it exists only
  * so the formula itself can be pinned against fp64 references.
  *
  * Thread count never changes a result: the update is elementwise, and the
  * fp64 norm is summed over fixed blocks of 65536 elements whose partial
  * sums are then added in block order.
+ *
+ * fp16 variant with dynamic loss scaling (the end of this file).  The pages
+ * name fp16 overflow and the loss scaler that must keep up with it as the
+ * hazard of 16-bit training (CS324 notes §13; 大模型基础设施工程 06, §12
+ * pitfall 7) without spelling the scaler out; the reading taken is torch's
+ * GradScaler: contributions of the loss scaled by `scale` are averaged in
+ * fp32, multiplied by inv_scale = fp32(1/scale), and if any result is not
+ * finite the step is skipped and scale *= backoff; otherwise the step runs
+ * and, after growth_interval consecutive good steps, scale *= growth.
  */
 #include <math.h>
 #include <stdint.h>
@@ -115,13 +124,28 @@ typedef struct {
     double beta1, beta2, c1, c2, alpha, bhat, eps, decay_mul;
 } zo_scalars_f64;
 
+/* b^t in fp64 by binary powering: square-and-multiply over the bits of t from
+ * the lowest, each product rounded once.  A fixed sequence of IEEE multiplies,
+ * so any conforming implementation gives the same bits. */
+double zo_pow_int(double b, int64_t t)
+{
+    double r = 1.0, x = b;
+    while (t > 0) {
+        if (t & 1)
+            r = r * x;
+        x = x * x;
+        t >>= 1;
+    }
+    return r;
+}
+
 /* fp64 evaluation of the per-step constants; t is 1-based. */
 static zo_scalars_f64 scalars_f64(double lr, double beta1, double beta2,
                                   double eps, double wd, int64_t t)
 {
     zo_scalars_f64 k;
-    double bc1 = 1.0 - pow(beta1, (double)t);
-    double bc2 = 1.0 - pow(beta2, (double)t);
+    double bc1 = 1.0 - zo_pow_int(beta1, t);
+    double bc2 = 1.0 - zo_pow_int(beta2, t);
     k.beta1 = beta1;
     k.beta2 = beta2;
     k.c1 = 1.0 - beta1;
@@ -304,4 +328,167 @@ int32_t zo_step_f64(int64_t n, int32_t M, const double *const *grads,
         update_f64(g, &master[i], &m[i], &v[i], &k, d);
     }
     return 0;
+}
+
+/* --------------------------------- fp16 variant with dynamic loss scaling */
+
+/* fp16 -> fp32 (exact). */
+static float f16_to_f32(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    uint32_t e = (h >> 10) & 0x1fu, mant = h & 0x3ffu;
+    uint32_t u;
+    if (e == 0x1f) {
+        u = sign | 0x7f800000u | (mant << 13);             /* Inf / NaN */
+    } else if (e != 0) {
+        u = sign | ((e + 112u) << 23) | (mant << 13);      /* normal: rebias 15 -> 127 */
+    } else if (mant == 0) {
+        u = sign;                                         /* +-0 */
+    } else {                                              /* subnormal: mant * 2^-24 */
+        float f = (float)mant * 5.9604644775390625e-8f;    /* exact: mant < 2^10 */
+        memcpy(&u, &f, sizeof u);
+        u |= sign;
+    }
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* fp32 -> fp16, round to nearest, ties to even; overflow to Inf; NaN stays
+ * a quiet NaN with the top payload bits. */
+static uint16_t f32_to_f16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u)                                  /* NaN */
+        return (uint16_t)(sign | 0x7e00u | ((a >> 13) & 0x1ffu));
+    if (a >= 0x477ff000u)                                 /* >= 65520: rounds to Inf */
+        return (uint16_t)(sign | 0x7c00u);
+    if (a >= 0x38800000u) {                               /* fp16 normal range */
+        uint32_t m = a - 0x38000000u;                     /* rebias 127 -> 15 */
+        uint32_t r = (m + 0xfffu + ((m >> 13) & 1u)) >> 13;
+        return (uint16_t)(sign | r);
+    }
+    if (a <= 0x33000000u)                                 /* <= 2^-25: rounds to 0 */
+        return sign;
+    {                                                     /* fp16 subnormal */
+        uint32_t e = a >> 23, mant = (a & 0x7fffffu) | 0x800000u;
+        uint32_t sh = 126u - e;                           /* value / 2^-24 = mant >> sh */
+        uint32_t q = mant >> sh, rem = mant & ((1u << sh) - 1u), half = 1u << (sh - 1u);
+        if (rem > half || (rem == half && (q & 1u)))
+            q++;
+        return (uint16_t)(sign | q);
+    }
+}
+
+void zo_f16_to_f32_array(int64_t n, const uint16_t *in, float *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = f16_to_f32(in[i]);
+}
+
+void zo_f32_to_f16_array(int64_t n, const float *in, uint16_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        out[i] = f32_to_f16(in[i]);
+}
+
+/* inv_scale = fp32(1 / scale), the reciprocal taken in fp64. */
+float zo_inv_scale(float scale)
+{
+    return (float)(1.0 / (double)scale);
+}
+
+/* The unscaled fp32 average of M fp16 contributions: ((sum_j g_j) / M) * inv_scale. */
+static float mean_f16_unscaled(const uint16_t *const *grads, int32_t M, int64_t i,
+                               float inv_scale)
+{
+    float s = f16_to_f32(grads[0][i]);
+    for (int32_t j = 1; j < M; j++)
+        s = s + f16_to_f32(grads[j][i]);
+    float g = s / (float)M;
+    return g * inv_scale;
+}
+
+void zo_reduce_mean_f16(int64_t n, int32_t M, const uint16_t *const *grads, float inv_scale,
+                        float *g_out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        g_out[i] = mean_f16_unscaled(grads, M, i, inv_scale);
+}
+
+/* Sum of squares of the unscaled average (fp64, fixed blocks as above); it is
+ * not finite exactly when some unscaled element is not finite (the found-inf
+ * test). */
+double zo_grad_sumsq_f16(int64_t n, int32_t M, const uint16_t *const *grads, float inv_scale)
+{
+    if (n <= 0 || M < 1)
+        return 0.0;
+    int64_t nb = (n + ZO_NORM_BLOCK - 1) / ZO_NORM_BLOCK;
+    double *part = (double *)malloc((size_t)nb * sizeof(double));
+    if (!part)
+        return NAN;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nb; b++) {
+        int64_t lo = b * ZO_NORM_BLOCK;
+        int64_t hi = lo + ZO_NORM_BLOCK < n ? lo + ZO_NORM_BLOCK : n;
+        double acc = 0.0;
+        for (int64_t i = lo; i < hi; i++) {
+            double g = (double)mean_f16_unscaled(grads, M, i, inv_scale);
+            acc += g * g;
+        }
+        part[b] = acc;
+    }
+    double total = 0.0;
+    for (int64_t b = 0; b < nb; b++)
+        total += part[b];
+    free(part);
+    return total;
+}
+
+/* One fp32 step on fp16 contributions of a loss scaled by 1/inv_scale; the
+ * param copy is fp16.  The caller skips the call when found-inf holds. */
+int32_t zo_step_f16(int64_t n, int32_t M, const uint16_t *const *grads, float *master, float *m,
+                    float *v, uint16_t *param_f16, const uint8_t *decay, float lr, float beta1,
+                    float beta2, float eps, float wd, int64_t t, float inv_scale,
+                    int32_t use_coef, float coef)
+{
+    if (n < 0 || M < 1 || t < 1 || !grads || !master || !m || !v)
+        return -1;
+    zo_scalars_f32 k = scalars_f32(lr, beta1, beta2, eps, wd, t);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        float g = mean_f16_unscaled(grads, M, i, inv_scale);
+        if (use_coef)
+            g = g * coef;
+        float d = (decay == NULL || decay[i]) ? k.decay_mul : 1.0f;
+        update_f32(g, &master[i], &m[i], &v[i], &k, d);
+        if (param_f16)
+            param_f16[i] = f32_to_f16(master[i]);
+    }
+    return 0;
+}
+
+/* The loss-scale update after a step: found_inf -> scale *= backoff and the
+ * growth count restarts; otherwise the count grows and, on reaching
+ * growth_interval, scale *= growth and the count restarts. */
+void zo_scaler_update(float *scale, int32_t *growth_tracker, int32_t found_inf,
+                      float growth_factor, float backoff_factor, int32_t growth_interval)
+{
+    if (found_inf) {
+        *scale = *scale * backoff_factor;
+        *growth_tracker = 0;
+    } else {
+        int32_t good = *growth_tracker + 1;
+        if (good == growth_interval) {
+            *scale = *scale * growth_factor;
+            *growth_tracker = 0;
+        } else {
+            *growth_tracker = good;
+        }
+    }
 }

@@ -77,11 +77,12 @@ int ehip(const char* where, hipError_t e) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Per-step constants: fp64 from the fp32 hyper-parameters, rounded once to fp32.
+// Per-step constants: fp64 from the fp32 hyper-parameters, rounded once to fp32;
+// beta^t by binary powering (zs::pow_int), the same sequence the device uses.
 zs::StepConsts step_consts(float lr, float beta1, float beta2, float eps, float wd, int64_t t) {
   const double b1 = beta1, b2 = beta2, l = lr;
-  const double bc1 = 1.0 - pow(b1, (double)t);
-  const double bc2 = 1.0 - pow(b2, (double)t);
+  const double bc1 = 1.0 - zs::pow_int(b1, t);
+  const double bc2 = 1.0 - zs::pow_int(b2, t);
   zs::StepConsts k;
   k.beta1 = beta1;
   k.beta2 = beta2;

@@ -47,6 +47,19 @@ struct StepConsts {
 
 constexpr int kMaxM = 16;
 
+// b^t in fp64 by binary powering: square-and-multiply over the bits of t from
+// the lowest, each product rounded once -- a fixed sequence of IEEE multiplies,
+// so host and device compute the same bits (used for the bias corrections).
+__host__ __device__ inline double pow_int(double b, int64_t t) {
+  double r = 1.0, x = b;
+  while (t > 0) {
+    if (t & 1) r = r * x;
+    x = x * x;
+    t >>= 1;
+  }
+  return r;
+}
+
 struct GradPtrs {
   const uint16_t* p[kMaxM];
 };

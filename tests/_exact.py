@@ -57,9 +57,9 @@ def sqrt_rne_f32(x: Fraction) -> np.float32:
         raise ValueError
     if x == 0:
         return np.float32(0.0)
-    s = 200                                             # extra bits: far beyond fp32's 24
-    num, den = x.numerator, x.denominator               # den = 2^k (x is an fp32 value)
+    num, den = x.numerator, x.denominator               # den = 2^k (x is dyadic)
     k = den.bit_length() - 1
+    s = max(200, (k + 400) // 2)                        # extra bits: far beyond fp32's 24
     shift = 2 * s - k                                   # sqrt(x) * 2^s = sqrt(num << shift)
     assert shift >= 0 and den == 1 << k
     big = num << shift

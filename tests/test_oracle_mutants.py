@@ -15,6 +15,7 @@ import pytest
 
 import oracle
 import test_oracle_adamw as A
+import test_oracle_amp as P
 import test_oracle_bf16 as B
 import test_oracle_clip as K
 import test_oracle_reduce as R
@@ -45,6 +46,13 @@ PINS = [
     lambda: Z.test_sharded_equals_unsharded(3, 0, 0.05),
     lambda: K.test_norm_of_constant_gradient_closed_form(),
     lambda: K.test_norm_and_coef_match_torch_clip_grad_norm(),
+    lambda: X.test_pow_int_against_exact_rationals(),
+    lambda: X.test_step_constants_exactly_rounded(1000),
+    lambda: P.test_f32_to_f16_special_cases(),
+    lambda: P.test_f16_to_f32_exhaustive(),
+    lambda: P.test_scale_update_matches_torch(),
+    lambda: P.test_unscale_and_found_inf_match_torch(),
+    lambda: P.test_amp_sequence_matches_torch_adamw_and_gradscaler(),
 ]
 
 U, C = "zo_update.inc", "zo.c"
@@ -69,11 +77,22 @@ MUTANTS = [
     ("bf16-truncates", C, "return (uint16_t)((u + 0x7fffu + lsb) >> 16);",
      "return (uint16_t)(u >> 16);"),
     ("bf16-ties-away", C, "uint32_t lsb = (u >> 16) & 1u;", "uint32_t lsb = 1u;"),
-    ("norm-not-squared", C, "acc += g * g;", "acc += g < 0 ? -g : g;"),
+    ("norm-not-squared", C, "double g = (double)mean_f32(grads, M, i);\n            acc += g * g;",
+     "double g = (double)mean_f32(grads, M, i);\n            acc += g < 0 ? -g : g;"),
     ("clip-no-guard", C, "double c = (double)max_norm / (norm + 1e-6);",
      "double c = (double)max_norm / norm;"),
     ("clip-not-clamped", C, "    if (c > 1.0)\n        c = 1.0;\n    return (float)c;",
      "    return (float)c;"),
+    ("pow-int-wrong-square", C, "        x = x * x;", "        x = x * b;"),
+    ("f16-no-unscale", C, "    return g * inv_scale;", "    return g;"),
+    ("f16-truncates", C, "uint32_t r = (m + 0xfffu + ((m >> 13) & 1u)) >> 13;",
+     "uint32_t r = m >> 13;"),
+    ("f16-subnormal-ties-up", C, "if (rem > half || (rem == half && (q & 1u)))",
+     "if (rem >= half)"),
+    ("f16-widen-subnormal-scale", C, "float f = (float)mant * 5.9604644775390625e-8f;",
+     "float f = (float)mant * 1.1920928955078125e-7f;"),
+    ("scaler-no-backoff", C, "*scale = *scale * backoff_factor;", "*scale = *scale;"),
+    ("scaler-growth-late", C, "if (good == growth_interval) {", "if (good > growth_interval) {"),
     ("fma-contraction", None, None, None),
 ]
 

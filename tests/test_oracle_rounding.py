@@ -111,3 +111,29 @@ def test_exact_helpers_against_known_values():
     assert E.sqrt(np.float32(2.0)).view(np.uint32) == np.uint32(0x3FB504F3)
     assert E.rne_f32(Fraction(1, 2 ** 150)) == np.float32(0.0)      # tie to even (zero)
     assert E.rne_f32(Fraction(3, 2 ** 150)).view(np.uint32) == np.uint32(2)  # 1.5 ulp -> 2
+
+
+def test_pow_int_against_exact_rationals():
+    """beta^t by fp64 binary powering stays within 1e-13 of the exact power, so the
+    fp32 step constants equal the exactly rounded constants of the exact values."""
+    for beta in (0.9, 0.95, 0.99, 0.999):
+        b32 = float(np.float32(beta))
+        exact = Fraction(1)
+        for t in range(1, 1201):
+            exact *= Fraction(b32)
+            if t % 7 and t > 40:
+                continue
+            p = oracle.pow_int(b32, t)
+            assert abs(Fraction(p) - exact) <= Fraction(1, 10 ** 13) * exact, (beta, t)
+
+
+@pytest.mark.parametrize("t", [1, 2, 3, 10, 100, 1000])
+def test_step_constants_exactly_rounded(t):
+    lr, b1, b2 = np.float32(3e-4), np.float32(0.9), np.float32(0.95)
+    k = oracle.step_scalars_f32(float(lr), float(b1), float(b2), 1e-8, 0.1, t)
+    bc1 = 1 - Fraction(float(b1)) ** t
+    bc2 = 1 - Fraction(float(b2)) ** t
+    assert np.float32(k["alpha"]) == E.rne_f32(Fraction(float(lr)) / bc1)
+    assert np.float32(k["bhat"]) == E.sqrt_rne_f32(bc2)
+    assert np.float32(k["c1"]) == E.rne_f32(1 - Fraction(float(b1)))
+    assert np.float32(k["decay_mul"]) == E.rne_f32(1 - Fraction(float(lr)) * Fraction(float(np.float32(0.1))))
