@@ -79,6 +79,15 @@ enum {
 
 /* zero_shard_init flags */
 #define ZS_SKIP_NONFINITE 1u /* non-finite norm: the step leaves every array untouched */
+#define ZS_FP16 2u           /* gradients and the param copy are fp16 (zero_shard_step_amp) */
+
+/* Device state of the dynamic loss scaler (16 bytes of caller-owned device
+ * memory, 16-byte aligned), read and updated by zero_shard_step_amp. */
+typedef struct zs_amp_state {
+    float scale;            /* the loss scale the next gradients carry */
+    int32_t growth_tracker; /* consecutive steps without Inf/NaN */
+    int64_t applied_steps;  /* optimizer steps applied (skipped ones do not count) */
+} zs_amp_state;
 
 #define ZS_MAX_M 16
 
@@ -198,8 +207,9 @@ int zero_shard_step_global_norm(zs_ctx *ctx, const void *const *grads, float lr,
  * pieces cover the canonical arrays exactly once.
  *
  * export: copies this rank's master, exp_avg, exp_avg_sq into the canonical
- *   device arrays.  import: the reverse, and also writes param_bf16 =
- *   bf16_rne(master) for the imported elements; padding is not touched.
+ *   device arrays.  import: the reverse, and also writes the param copy
+ *   (bf16_rne(master), or fp16 for a ZS_FP16 context) for the imported
+ *   elements; padding is not touched.
  * Canonical pointers are device pointers to sum(numel) floats each (may be
  * NULL only when the model is empty).  Enqueued on the context's stream.
  * Errors: ZS_EINVAL, ZS_EHIP.
@@ -208,6 +218,31 @@ int zero_shard_export_state(zs_ctx *ctx, float *canon_master, float *canon_exp_a
                             float *canon_exp_avg_sq);
 int zero_shard_import_state(zs_ctx *ctx, const float *canon_master, const float *canon_exp_avg,
                             const float *canon_exp_avg_sq);
+
+/*
+ * fp16 training with dynamic loss scaling (a context created with ZS_FP16:
+ * grads[j] and the param buffer hold fp16).  The pages name fp16 overflow and
+ * a loss scaler that must keep up as the hazard of 16-bit training (CS324
+ * notes §13; 大模型基础设施工程 06, §12 pitfall 7); the scaler here is the usual
+ * one (torch's GradScaler):
+ *   g = ((sum_j grad_j) / M) * inv_scale,  inv_scale = fp32(1/scale)
+ *   found_inf = the fp64 sum of g^2 is not finite (some g is NaN or Inf)
+ *   found_inf:  nothing is updated; scale *= backoff_factor; tracker = 0
+ *   otherwise:  [clip on the unscaled norm] the AdamW step at
+ *               t = applied_steps + 1, param = fp16_rne(master);
+ *               applied_steps += 1; after growth_interval such steps in a row
+ *               scale *= growth_factor.
+ * Everything, including the bias-correction constants for t, is decided on
+ * the device: no host round trip per step.  zero_shard_amp_state_init enqueues
+ * the initial state {init_scale, 0, 0}.  grad_norm_out (optional, waits)
+ * receives the unscaled norm; ZS_NONFINITE then reports found_inf.
+ * Errors: ZS_EINVAL, ZS_ESTATE (context without ZS_FP16), ZS_EHIP.
+ */
+int zero_shard_amp_state_init(zs_ctx *ctx, zs_amp_state *state_dev, float init_scale);
+int zero_shard_step_amp(zs_ctx *ctx, const void *const *grads, float lr, float beta1, float beta2,
+                        float eps, float weight_decay, float max_grad_norm,
+                        zs_amp_state *state_dev, float growth_factor, float backoff_factor,
+                        int32_t growth_interval, double *grad_norm_out);
 
 /* The bf16 parameter shard (the all-gather send buffer) and its length. */
 int zero_shard_params(zs_ctx *ctx, const void **param_bf16, int64_t *shard_len);

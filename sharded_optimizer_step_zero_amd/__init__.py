@@ -26,6 +26,7 @@ ZS_ENOMEM = -2
 ZS_EHIP = -3
 ZS_ESTATE = -4
 ZS_SKIP_NONFINITE = 1
+ZS_FP16 = 2
 ZS_MAX_M = 16
 
 if not os.path.exists(LIB_PATH):
@@ -71,6 +72,9 @@ _sig("zero_shard_step", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _i
 _sig("zero_shard_grad_sumsq", ctypes.c_int, _vp, _vp, _vp)
 _sig("zero_shard_step_global_norm", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _i64,
      _f32, _vp)
+_sig("zero_shard_amp_state_init", ctypes.c_int, _vp, _vp, _f32)
+_sig("zero_shard_step_amp", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _f32, _vp, _f32,
+     _f32, _i32, _P(_f64))
 _sig("zero_shard_export_state", ctypes.c_int, _vp, _vp, _vp, _vp)
 _sig("zero_shard_import_state", ctypes.c_int, _vp, _vp, _vp, _vp)
 _sig("zero_shard_params", ctypes.c_int, _vp, _P(_vp), _P(_i64))
@@ -81,7 +85,8 @@ _sig("zero_shard_last_error", ctypes.c_char_p)
 EXPORTED = ["zs_plan_create", "zs_plan_query", "zs_plan_tensor_slice", "zs_plan_segment",
             "zs_plan_bucket", "zs_plan_run", "zs_plan_state_bytes", "zs_plan_destroy",
             "zs_workspace_bytes", "zero_shard_init", "zero_shard_step", "zero_shard_grad_sumsq",
-            "zero_shard_step_global_norm", "zero_shard_export_state", "zero_shard_import_state",
+            "zero_shard_step_global_norm", "zero_shard_amp_state_init", "zero_shard_step_amp",
+            "zero_shard_export_state", "zero_shard_import_state",
             "zero_shard_params", "zero_shard_set_stream",
             "zero_shard_destroy", "zero_shard_last_error"]
 
@@ -214,6 +219,26 @@ def zero_shard_step_global_norm(ctx: int, grads: Sequence[int], lr: float, beta1
                                             global_sumsq_dev))
 
 
+def zero_shard_amp_state_init(ctx: int, state_dev: int, init_scale: float) -> None:
+    _check(_lib.zero_shard_amp_state_init(ctx, state_dev, init_scale))
+
+
+def zero_shard_step_amp(ctx: int, grads: Sequence[int], lr: float, beta1: float, beta2: float,
+                        eps: float, weight_decay: float, max_grad_norm: float, state_dev: int,
+                        growth_factor: float = 2.0, backoff_factor: float = 0.5,
+                        growth_interval: int = 2000, want_norm: bool = False,
+                        return_code: bool = False):
+    """Enqueues one loss-scaled fp16 step (see zeroshard.h).  Returns the unscaled
+    norm when want_norm (waits), else None; with return_code, (code, norm)."""
+    nrm = ctypes.c_double()
+    rc = _check(_lib.zero_shard_step_amp(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
+                                         weight_decay, max_grad_norm, state_dev, growth_factor,
+                                         backoff_factor, growth_interval,
+                                         ctypes.byref(nrm) if want_norm else None))
+    norm = nrm.value if want_norm else None
+    return (rc, norm) if return_code else norm
+
+
 def zero_shard_export_state(ctx: int, canon_master: int, canon_exp_avg: int,
                             canon_exp_avg_sq: int) -> None:
     _check(_lib.zero_shard_export_state(ctx, canon_master or None, canon_exp_avg or None,
@@ -247,7 +272,7 @@ class ZeroShard:
     """One rank's shard: plan + torch-allocated device buffers + bound context."""
 
     def __init__(self, numel, decay, world_size=1, rank=0, M=1, device=None, bucket_cap=25_000_000,
-                 align=64, flags=0, stream=None):
+                 align=64, flags=0, stream=None, fp16=False):
         import torch
         self.device = torch.device(device if device is not None else "cuda")
         self.M = M
@@ -260,7 +285,11 @@ class ZeroShard:
         self.master = torch.zeros(S, dtype=torch.float32, device=dev)
         self.exp_avg = torch.zeros(S, dtype=torch.float32, device=dev)
         self.exp_avg_sq = torch.zeros(S, dtype=torch.float32, device=dev)
-        self.param = torch.zeros(S, dtype=torch.bfloat16, device=dev)
+        self.fp16 = fp16
+        if fp16:
+            flags |= ZS_FP16
+        self.param = torch.zeros(S, dtype=torch.float16 if fp16 else torch.bfloat16, device=dev)
+        self.amp_state = None
         self.ws_bytes = zs_workspace_bytes(self.plan, M)
         # torch's caching allocator returns 512-byte aligned blocks
         self.workspace = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -280,6 +309,29 @@ class ZeroShard:
             raise ValueError(f"expected {self.M} gradient contributions")
         return zero_shard_step(self.ctx, ptrs, lr, beta1, beta2, eps, weight_decay, step,
                                max_grad_norm, want_norm, return_code)
+
+    def amp_init(self, init_scale=65536.0):
+        """Allocate and initialise the device loss-scaler state {scale, 0, 0}."""
+        import torch
+        self.amp_state = torch.zeros(2, dtype=torch.int64, device=self.device)
+        zero_shard_amp_state_init(self.ctx, self.amp_state.data_ptr(), init_scale)
+
+    def amp_read(self):
+        """(scale, growth_tracker, applied_steps) from the device state (waits)."""
+        import numpy as np
+        raw = self.amp_state.cpu().numpy()
+        head = raw[:1].view(np.float32)
+        return float(head[0]), int(raw[:1].view(np.int32)[1]), int(raw[1])
+
+    def step_amp(self, grads, *, lr, beta1, beta2, eps, weight_decay, max_grad_norm=0.0,
+                 growth_factor=2.0, backoff_factor=0.5, growth_interval=2000, want_norm=False,
+                 return_code=False):
+        ptrs = [g if isinstance(g, int) else g.data_ptr() for g in grads]
+        if len(ptrs) != self.M:
+            raise ValueError(f"expected {self.M} gradient contributions")
+        return zero_shard_step_amp(self.ctx, ptrs, lr, beta1, beta2, eps, weight_decay,
+                                   max_grad_norm, self.amp_state.data_ptr(), growth_factor,
+                                   backoff_factor, growth_interval, want_norm, return_code)
 
     def export_state(self, canon_master, canon_exp_avg, canon_exp_avg_sq):
         """Copy this rank's state into canonical device tensors (sum(numel) floats each)."""

@@ -24,6 +24,7 @@ void set_error(const std::string& msg) { g_last_error = msg; }
 struct zs_ctx {
   int32_t M = 0;
   uint32_t flags = 0;
+  bool fp16 = false;
   int64_t shard_len = 0, n_pieces = 0, canon_len = 0;
   int32_t n_runs = 0;
   int32_t waves_per_cu = 0;
@@ -77,22 +78,8 @@ int ehip(const char* where, hipError_t e) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Per-step constants: fp64 from the fp32 hyper-parameters, rounded once to fp32;
-// beta^t by binary powering (zs::pow_int), the same sequence the device uses.
 zs::StepConsts step_consts(float lr, float beta1, float beta2, float eps, float wd, int64_t t) {
-  const double b1 = beta1, b2 = beta2, l = lr;
-  const double bc1 = 1.0 - zs::pow_int(b1, t);
-  const double bc2 = 1.0 - zs::pow_int(b2, t);
-  zs::StepConsts k;
-  k.beta1 = beta1;
-  k.beta2 = beta2;
-  k.c1 = (float)(1.0 - b1);
-  k.c2 = (float)(1.0 - b2);
-  k.alpha = (float)(l / bc1);
-  k.bhat = (float)sqrt(bc2);
-  k.eps = eps;
-  k.decay_mul = (float)(1.0 - l * (double)wd);
-  return k;
+  return zs::step_consts(lr, beta1, beta2, eps, wd, t);
 }
 
 int check_hparams(float lr, float beta1, float beta2, float eps, float wd, int64_t step) {
@@ -121,6 +108,10 @@ int gather_grads(const zs_ctx* ctx, const void* const* grads, zs::GradPtrs* out)
 zs::ClipScalars* scalars(zs_ctx* ctx) {
   return reinterpret_cast<zs::ClipScalars*>(ctx->ws + ctx->lay.scalars_off);
 }
+// device-computed step constants of the loss-scaled path (same 256-byte block)
+zs::StepConsts* device_consts(zs_ctx* ctx) {
+  return reinterpret_cast<zs::StepConsts*>(ctx->ws + ctx->lay.scalars_off + 64);
+}
 double* partials(zs_ctx* ctx) { return reinterpret_cast<double*>(ctx->ws + ctx->lay.partials_off); }
 // the level-2 partials the finalize step sums
 const double* final_partials(zs_ctx* ctx) {
@@ -147,7 +138,7 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   *out = nullptr;
   if (!plan) return einval("zero_shard_init: plan is NULL");
   if (M < 1 || M > ZS_MAX_M) return einval("zero_shard_init: M must lie in [1, 16]");
-  if (flags & ~ZS_SKIP_NONFINITE) return einval("zero_shard_init: unknown flag");
+  if (flags & ~(ZS_SKIP_NONFINITE | ZS_FP16)) return einval("zero_shard_init: unknown flag");
   if (!param_bf16 || !master || !exp_avg || !exp_avg_sq || !workspace)
     return einval("zero_shard_init: NULL buffer");
   if (!aligned16(param_bf16) || !aligned16(master) || !aligned16(exp_avg) ||
@@ -177,6 +168,7 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   }
   c->M = M;
   c->flags = flags;
+  c->fp16 = (flags & ZS_FP16) != 0;
   c->shard_len = plan->shard_len;
   c->n_runs = (int32_t)(table.size() - 1);
   c->n_pieces = (int64_t)plan->pieces.size();
@@ -232,10 +224,16 @@ int enqueue_step(zs_ctx* ctx, const zs::GradPtrs& g, const zs::StepConsts& k, bo
 
 }  // namespace
 
+int estate(const char* msg) {
+  zs::set_error(msg);
+  return ZS_ESTATE;
+}
+
 extern "C" int zero_shard_step(zs_ctx* ctx, const void* const* grads, float lr, float beta1,
                                float beta2, float eps, float weight_decay, int64_t step,
                                float max_grad_norm, double* grad_norm_out) {
   if (!ctx) return einval("zero_shard_step: ctx is NULL");
+  if (ctx->fp16) return estate("zero_shard_step: fp16 context: use zero_shard_step_amp");
   int rc = check_hparams(lr, beta1, beta2, eps, weight_decay, step);
   if (rc) return rc;
   if (isnan(max_grad_norm) || isinf(max_grad_norm))
@@ -264,6 +262,7 @@ extern "C" int zero_shard_step(zs_ctx* ctx, const void* const* grads, float lr, 
 
 extern "C" int zero_shard_grad_sumsq(zs_ctx* ctx, const void* const* grads, double* sumsq_dev) {
   if (!ctx) return einval("zero_shard_grad_sumsq: ctx is NULL");
+  if (ctx->fp16) return estate("zero_shard_grad_sumsq: not available on an fp16 context");
   if (!sumsq_dev || ((uintptr_t)sumsq_dev & 7u))
     return einval("zero_shard_grad_sumsq: sumsq_dev must be an 8-byte-aligned device pointer");
   zs::GradPtrs g;
@@ -283,6 +282,7 @@ extern "C" int zero_shard_step_global_norm(zs_ctx* ctx, const void* const* grads
                                            float weight_decay, int64_t step, float max_grad_norm,
                                            const double* global_sumsq_dev) {
   if (!ctx) return einval("zero_shard_step_global_norm: ctx is NULL");
+  if (ctx->fp16) return estate("zero_shard_step_global_norm: not available on an fp16 context");
   int rc = check_hparams(lr, beta1, beta2, eps, weight_decay, step);
   if (rc) return rc;
   if (!(max_grad_norm > 0.0f) || isinf(max_grad_norm))
@@ -303,7 +303,7 @@ int state_copy(zs_ctx* ctx, bool do_export, float* cm, float* cmm, float* cv, co
   if (ctx->canon_len > 0 && (!cm || !cmm || !cv))
     return einval((std::string(who) + ": canonical buffers must be non-NULL").c_str());
   const hipError_t e = zs::launch_state_copy(
-      do_export, reinterpret_cast<const zs::Piece*>(ctx->ws + ctx->lay.pieces_off),
+      do_export, ctx->fp16, reinterpret_cast<const zs::Piece*>(ctx->ws + ctx->lay.pieces_off),
       ctx->n_pieces, ctx->master, ctx->m, ctx->v, ctx->param, cm, cmm, cv, ctx->stream);
   return e == hipSuccess ? ZS_OK : ehip(who, e);
 }
@@ -321,6 +321,72 @@ extern "C" int zero_shard_import_state(zs_ctx* ctx, const float* canon_master,
                                        const float* canon_exp_avg_sq) {
   return state_copy(ctx, false, const_cast<float*>(canon_master), const_cast<float*>(canon_exp_avg),
                     const_cast<float*>(canon_exp_avg_sq), "zero_shard_import_state");
+}
+
+extern "C" int zero_shard_amp_state_init(zs_ctx* ctx, zs_amp_state* state_dev, float init_scale) {
+  if (!ctx) return einval("zero_shard_amp_state_init: ctx is NULL");
+  if (!state_dev || ((uintptr_t)state_dev & 15u))
+    return einval("zero_shard_amp_state_init: state_dev must be a 16-byte-aligned device pointer");
+  if (!(init_scale > 0.0f) || isinf(init_scale))
+    return einval("zero_shard_amp_state_init: init_scale must be finite and > 0");
+  const hipError_t e = zs::launch_amp_state_init(reinterpret_cast<zs::AmpState*>(state_dev),
+                                                 init_scale, ctx->stream);
+  return e == hipSuccess ? ZS_OK : ehip("zero_shard_amp_state_init", e);
+}
+
+extern "C" int zero_shard_step_amp(zs_ctx* ctx, const void* const* grads, float lr, float beta1,
+                                   float beta2, float eps, float weight_decay,
+                                   float max_grad_norm, zs_amp_state* state_dev,
+                                   float growth_factor, float backoff_factor,
+                                   int32_t growth_interval, double* grad_norm_out) {
+  if (!ctx) return einval("zero_shard_step_amp: ctx is NULL");
+  if (!ctx->fp16) return estate("zero_shard_step_amp: needs a context created with ZS_FP16");
+  int rc = check_hparams(lr, beta1, beta2, eps, weight_decay, 1);
+  if (rc) return rc;
+  if (isnan(max_grad_norm) || isinf(max_grad_norm))
+    return einval("zero_shard_step_amp: max_grad_norm must be finite");
+  if (!state_dev || ((uintptr_t)state_dev & 15u))
+    return einval("zero_shard_step_amp: state_dev must be a 16-byte-aligned device pointer");
+  if (!(growth_factor >= 1.0f) || isinf(growth_factor) || !(backoff_factor > 0.0f) ||
+      !(backoff_factor <= 1.0f) || growth_interval < 1)
+    return einval("zero_shard_step_amp: need growth >= 1, 0 < backoff <= 1, interval >= 1");
+  zs::GradPtrs g;
+  if ((rc = gather_grads(ctx, grads, &g))) return rc;
+  if (ctx->shard_len == 0) {
+    if (grad_norm_out) *grad_norm_out = 0.0;
+    return ZS_OK;
+  }
+  zs::AmpState* st = reinterpret_cast<zs::AmpState*>(state_dev);
+  zs::AmpParams p;
+  p.lr = lr;
+  p.beta1 = beta1;
+  p.beta2 = beta2;
+  p.eps = eps;
+  p.weight_decay = weight_decay;
+  p.max_norm = max_grad_norm;
+  p.growth = growth_factor;
+  p.backoff = backoff_factor;
+  p.interval = growth_interval;
+  p.clip = max_grad_norm > 0.0f ? 1 : 0;
+  hipError_t e = zs::launch_sumsq_f16(ctx->M, g, ctx->shard_len, partials(ctx), st, ctx->stream);
+  if (e != hipSuccess) return ehip("zero_shard_step_amp: norm pass", e);
+  e = zs::launch_amp_finalize(final_partials(ctx), zs::final_partials(ctx->shard_len), st, p,
+                              scalars(ctx), device_consts(ctx), ctx->stream);
+  if (e != hipSuccess) return ehip("zero_shard_step_amp: finalize", e);
+  e = zs::launch_step_f16(ctx->M, g, ctx->master, ctx->m, ctx->v, ctx->param, ctx->shard_len,
+                          run_table(ctx), ctx->n_runs, scalars(ctx), device_consts(ctx),
+                          ctx->waves_per_cu, ctx->stream);
+  if (e != hipSuccess) return ehip("zero_shard_step_amp: step kernel", e);
+  if (grad_norm_out) {
+    double norm = 0.0;
+    e = hipMemcpyAsync(&norm, &scalars(ctx)->norm, sizeof(double), hipMemcpyDeviceToHost,
+                       ctx->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+    if (e != hipSuccess) return ehip("zero_shard_step_amp: reading the norm", e);
+    *grad_norm_out = norm;
+    if (!isfinite(norm)) return ZS_NONFINITE;
+  }
+  return ZS_OK;
 }
 
 extern "C" int zero_shard_params(zs_ctx* ctx, const void** param_bf16, int64_t* shard_len) {

@@ -75,12 +75,46 @@ struct WorkspaceLayout {
 
 // Written by the finalize kernel, read by the step kernel.
 struct ClipScalars {
-  double sumsq;    // sum of g^2 of the reduced gradient
-  double norm;     // sqrt(sumsq)
-  float coef;      // clip coefficient applied to g (1 when not clipping)
-  uint32_t skip;   // nonzero: leave the state untouched this step
-  uint32_t pad[2];
+  double sumsq;     // sum of g^2 of the reduced (and unscaled) gradient
+  double norm;      // sqrt(sumsq)
+  float coef;       // clip coefficient applied to g (1 when not clipping)
+  uint32_t skip;    // nonzero: leave the state untouched this step
+  float inv_scale;  // loss-scaled path: fp32(1/scale) of the scale the grads carry
+  uint32_t pad;
 };
+
+// Device state of the dynamic loss scaler (layout of zs_amp_state).
+struct AmpState {
+  float scale;
+  int32_t growth_tracker;
+  int64_t applied_steps;
+};
+static_assert(sizeof(AmpState) == 16, "loss-scaler state is 16 bytes");
+
+struct AmpParams {
+  float lr, beta1, beta2, eps, weight_decay, max_norm, growth, backoff;
+  int32_t interval, clip;
+};
+
+// Per-step constants, each computed in fp64 from the fp32 hyper-parameters and
+// rounded once to fp32 (host for the plain step, device for the loss-scaled
+// step, whose step count lives on the device).
+__host__ __device__ inline StepConsts step_consts(float lr, float beta1, float beta2, float eps,
+                                                  float wd, int64_t t) {
+  const double b1 = beta1, b2 = beta2, l = lr;
+  const double bc1 = 1.0 - pow_int(b1, t);
+  const double bc2 = 1.0 - pow_int(b2, t);
+  StepConsts k;
+  k.beta1 = beta1;
+  k.beta2 = beta2;
+  k.c1 = (float)(1.0 - b1);
+  k.c2 = (float)(1.0 - b2);
+  k.alpha = (float)(l / bc1);
+  k.bhat = (float)__builtin_sqrt(bc2);
+  k.eps = eps;
+  k.decay_mul = (float)(1.0 - l * (double)wd);
+  return k;
+}
 
 // fp64 partial sums of the norm pass: level-1 (one per 2048-element tile) followed
 // by level-2 (one per 8192 level-1 partials); the finalize step sums the level-2
@@ -99,13 +133,28 @@ hipError_t launch_finalize(const double* partials, int32_t n_partials,
                            int skip_nonfinite, ClipScalars* out, hipStream_t stream);
 hipError_t launch_sumsq_total(const double* partials, int32_t n_partials, double* out,
                               hipStream_t stream);
+// Loss-scaled (fp16) path: the norm pass on the unscaled average, the finalize
+// step that also computes the step constants on the device and updates the
+// scaler, the step kernel, and the scaler initialisation.
+hipError_t launch_sumsq_f16(int M, const GradPtrs& g, int64_t shard_len, double* partials,
+                            const AmpState* st, hipStream_t stream);
+hipError_t launch_amp_finalize(const double* partials, int32_t n_partials, AmpState* st,
+                               const AmpParams& p, ClipScalars* out, StepConsts* kout,
+                               hipStream_t stream);
+hipError_t launch_step_f16(int M, const GradPtrs& g, float* master, float* m, float* v,
+                           uint16_t* param, int64_t shard_len, const Run* runs, int32_t n_runs,
+                           const ClipScalars* clip, const StepConsts* k, int32_t waves_per_cu,
+                           hipStream_t stream);
+hipError_t launch_amp_state_init(AmpState* st, float scale, hipStream_t stream);
+
 // waves_per_cu > 0 caps the resident waves per CU of the step kernel (0: no cap).
 // Copies fp32 master/m/v between the shard and the canonical order over the
 // piece table (export: shard -> canonical; import: canonical -> shard, which
-// also writes param = bf16_rne(master) for the imported elements).
-hipError_t launch_state_copy(bool do_export, const Piece* pieces, int64_t n_pieces,
-                             float* master, float* m, float* v, uint16_t* param, float* c_master,
-                             float* c_m, float* c_v, hipStream_t stream);
+// also writes param = bf16_rne(master), or fp16 when param_f16, for the
+// imported elements).
+hipError_t launch_state_copy(bool do_export, bool param_f16, const Piece* pieces,
+                             int64_t n_pieces, float* master, float* m, float* v, uint16_t* param,
+                             float* c_master, float* c_m, float* c_v, hipStream_t stream);
 hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, float* m,
                        float* v, uint16_t* param, int64_t shard_len, const Run* runs,
                        int32_t n_runs, const ClipScalars* clip, const StepConsts& k,

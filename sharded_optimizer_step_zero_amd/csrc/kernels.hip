@@ -68,6 +68,15 @@ __device__ __forceinline__ uint32_t to_bf16(float x) {
   return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : r;
 }
 
+// fp16 <-> fp32 with the hardware's IEEE conversions: exact widening; narrowing
+// rounds to nearest even with overflow to Inf.
+__device__ __forceinline__ float h2f(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xffffu));
+}
+__device__ __forceinline__ uint32_t f2h(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
 __device__ __forceinline__ void unpack(const u32x4 w, float s[kVec]) {
   s[0] = bf16_lo(w.x); s[1] = bf16_hi(w.x);
   s[2] = bf16_lo(w.y); s[3] = bf16_hi(w.y);
@@ -122,6 +131,10 @@ __device__ __forceinline__ int32_t find_run(const Run* __restrict__ runs, int32_
   }
   return lo;
 }
+
+// LDS per CU on gfx950; reserving lds_cu / waves_per_cu bytes per single-wave
+// workgroup lets at most waves_per_cu of them reside on a CU.
+constexpr size_t kLdsPerCu = 160 * 1024;
 
 constexpr int kStepLanes = 64;   // one wave64 per workgroup
 constexpr int kStepVec = 4;      // elements per lane
@@ -265,7 +278,8 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
   r.norm = norm;
   r.coef = coef;
   r.skip = (skip_nonfinite && !__builtin_isfinite(total)) ? 1u : 0u;
-  r.pad[0] = r.pad[1] = 0;
+  r.inv_scale = 1.0f;
+  r.pad = 0;
   *out = r;
 }
 
@@ -278,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void sumsq_total_kernel(const double* __r
 // State export/import: one workgroup per piece (at most 65536 elements), the
 // lanes striding over it; the canonical side has no alignment guarantee, so
 // accesses are 4 bytes wide (still coalesced 256 B per wave).
-template <bool EXPORT>
+template <bool EXPORT, bool F16>
 __global__ __launch_bounds__(kThreads) void state_copy_kernel(
     const Piece* __restrict__ pieces, float* __restrict__ master, float* __restrict__ mom1,
     float* __restrict__ mom2, uint16_t* __restrict__ param, float* __restrict__ c_master,
@@ -295,9 +309,184 @@ __global__ __launch_bounds__(kThreads) void state_copy_kernel(
       master[s] = p;
       mom1[s] = c_m[c];
       mom2[s] = c_v[c];
-      param[s] = (uint16_t)to_bf16(p);
+      param[s] = (uint16_t)(F16 ? f2h(p) : to_bf16(p));
     }
   }
+}
+
+// ------------------------------------------------- loss-scaled fp16 path
+//
+// fp16 contributions carry the loss scale; each element's average is unscaled
+// by inv_scale = fp32(1/scale) right after the M-way divide.  Found-inf is a
+// non-finite sum of squares of the unscaled average (any NaN/Inf element makes
+// it so), decided by the finalize step together with the clip coefficient, the
+// step constants at t = applied + 1, and the scaler update -- all on the
+// device, so a skipped step costs no host round trip.  Conversions use the
+// hardware's IEEE fp16 <-> fp32 instructions (exact widening; round to nearest
+// even narrowing with overflow to Inf).
+
+template <int M>
+__global__ __launch_bounds__(kThreads) void sumsq_f16_kernel(GradPtrs g, int64_t n,
+                                                             double* __restrict__ partials,
+                                                             const AmpState* __restrict__ st) {
+  const float inv = (float)(1.0 / (double)st->scale);
+  const int64_t e = (int64_t)blockIdx.x * kNormTile + (int64_t)threadIdx.x * kVec;
+  double acc = 0.0;
+  if (e < n) {
+    u32x4 w[M];
+#pragma unroll
+    for (int j = 0; j < M; j++) w[j] = ld_stream(reinterpret_cast<const u32x4*>(g.p[j] + e));
+    float s[kVec];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      s[2 * q] = h2f(w[0][q]);
+      s[2 * q + 1] = h2f(w[0][q] >> 16);
+    }
+#pragma unroll
+    for (int j = 1; j < M; j++) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        s[2 * q] = s[2 * q] + h2f(w[j][q]);
+        s[2 * q + 1] = s[2 * q + 1] + h2f(w[j][q] >> 16);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kVec; q++) {
+      const float gq = (s[q] / (float)M) * inv;
+      const double x = (double)gq;
+      acc = acc + x * x;
+    }
+  }
+  const double t = block_sum(acc);
+  if (threadIdx.x == 0) partials[blockIdx.x] = t;
+}
+
+__global__ __launch_bounds__(kThreads) void amp_finalize_kernel(
+    const double* __restrict__ partials, int32_t n, AmpState* __restrict__ st, AmpParams p,
+    ClipScalars* __restrict__ out, StepConsts* __restrict__ kout) {
+  const double total = sum_partials(partials, n);
+  if (threadIdx.x != 0) return;
+  AmpState s = *st;
+  const bool found_inf = !__builtin_isfinite(total);
+  const double norm = __builtin_sqrt(total);
+  float coef = 1.0f;
+  if (p.clip) {
+    double c = (double)p.max_norm / (norm + 1e-6);
+    if (c > 1.0) c = 1.0;
+    coef = (float)c;
+  }
+  ClipScalars r;
+  r.sumsq = total;
+  r.norm = norm;
+  r.coef = coef;
+  r.skip = found_inf ? 1u : 0u;
+  r.inv_scale = (float)(1.0 / (double)s.scale);
+  r.pad = 0;
+  *kout = step_consts(p.lr, p.beta1, p.beta2, p.eps, p.weight_decay, s.applied_steps + 1);
+  if (found_inf) {
+    s.scale = s.scale * p.backoff;
+    s.growth_tracker = 0;
+  } else {
+    s.applied_steps += 1;
+    const int32_t good = s.growth_tracker + 1;
+    if (good == p.interval) {
+      s.scale = s.scale * p.growth;
+      s.growth_tracker = 0;
+    } else {
+      s.growth_tracker = good;
+    }
+  }
+  *out = r;
+  *st = s;
+}
+
+template <int M>
+__global__ __launch_bounds__(kStepLanes) void step_f16_kernel(
+    GradPtrs g, float* __restrict__ master, float* __restrict__ mom1, float* __restrict__ mom2,
+    uint16_t* __restrict__ param, int64_t n, const Run* __restrict__ runs, int32_t n_runs,
+    const ClipScalars* __restrict__ clip, const StepConsts* __restrict__ kp) {
+  const int64_t tile0 = (int64_t)blockIdx.x * kTile;
+  const int64_t e = tile0 + (int64_t)threadIdx.x * kStepVec;
+  if (e >= n) return;
+  u32x2 w[M];
+#pragma unroll
+  for (int j = 0; j < M; j++) w[j] = ld_stream(reinterpret_cast<const u32x2*>(g.p[j] + e));
+  f32x4 p4 = ld_stream(reinterpret_cast<const f32x4*>(master + e));
+  f32x4 m4 = ld_stream(reinterpret_cast<const f32x4*>(mom1 + e));
+  f32x4 v4 = ld_stream(reinterpret_cast<const f32x4*>(mom2 + e));
+  int32_t r = 0;
+  if (n_runs > 1) {
+    r = find_run(runs, n_runs, tile0);
+    if (runs[r + 1].start < tile0 + kTile) {
+      while (runs[r + 1].start <= e) r++;
+    }
+  }
+  if (clip->skip) return;  // found-inf: uniform over the grid
+  const StepConsts k = *kp;
+  const float inv = clip->inv_scale, coef = clip->coef;
+  const float d = (runs[r].flags & 1) ? k.decay_mul : 1.0f;
+  float s[kStepVec];
+  s[0] = h2f(w[0].x); s[1] = h2f(w[0].x >> 16);
+  s[2] = h2f(w[0].y); s[3] = h2f(w[0].y >> 16);
+#pragma unroll
+  for (int j = 1; j < M; j++) {
+    s[0] = s[0] + h2f(w[j].x); s[1] = s[1] + h2f(w[j].x >> 16);
+    s[2] = s[2] + h2f(w[j].y); s[3] = s[3] + h2f(w[j].y >> 16);
+  }
+  uint32_t b[kStepVec];
+#pragma unroll
+  for (int q = 0; q < kStepVec; q++) {
+    float gq = (s[q] / (float)M) * inv;
+    gq = gq * coef;
+    float p = p4[q], m = m4[q], v = v4[q];
+    adamw(gq, p, m, v, k, d);
+    p4[q] = p;
+    m4[q] = m;
+    v4[q] = v;
+    b[q] = f2h(p);
+  }
+  __builtin_nontemporal_store(p4, reinterpret_cast<f32x4*>(master + e));
+  __builtin_nontemporal_store(m4, reinterpret_cast<f32x4*>(mom1 + e));
+  __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(mom2 + e));
+  u32x2 ph;
+  ph.x = b[0] | (b[1] << 16);
+  ph.y = b[2] | (b[3] << 16);
+  __builtin_nontemporal_store(ph, reinterpret_cast<u32x2*>(param + e));
+}
+
+__global__ void amp_state_init_kernel(AmpState* st, float scale) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    AmpState s;
+    s.scale = scale;
+    s.growth_tracker = 0;
+    s.applied_steps = 0;
+    *st = s;
+  }
+}
+
+template <int M>
+hipError_t launch_sumsq_f16_m(const GradPtrs& g, int64_t shard_len, double* partials,
+                              const AmpState* st, hipStream_t stream) {
+  const int64_t p1 = (shard_len + kNormTile - 1) / kNormTile;
+  hipLaunchKernelGGL((sumsq_f16_kernel<M>), dim3((unsigned)p1), dim3(kThreads), 0, stream, g,
+                     shard_len, partials, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t p2 = (p1 + kLevel2 - 1) / kLevel2;
+  hipLaunchKernelGGL(sum_blocks_kernel, dim3((unsigned)p2), dim3(kThreads), 0, stream,
+                     partials, p1, partials + p1);
+  return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_step_f16_m(const GradPtrs& g, float* master, float* m, float* v,
+                             uint16_t* param, int64_t n, const Run* runs, int32_t n_runs,
+                             const ClipScalars* clip, const StepConsts* k, size_t lds,
+                             hipStream_t stream) {
+  const int64_t tiles = (n + kTile - 1) / kTile;
+  hipLaunchKernelGGL((step_f16_kernel<M>), dim3((unsigned)tiles), dim3(kStepLanes), lds, stream,
+                     g, master, m, v, param, n, runs, n_runs, clip, k);
+  return hipGetLastError();
 }
 
 template <int M>
@@ -369,10 +558,6 @@ int32_t final_partials(int64_t shard_len) {
     default: return hipErrorInvalidValue; \
   }
 
-// LDS per CU on gfx950; reserving lds_cu / waves_per_cu bytes per single-wave
-// workgroup lets at most waves_per_cu of them reside on a CU.
-constexpr size_t kLdsPerCu = 160 * 1024;
-
 hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, float* m,
                        float* v, uint16_t* param, int64_t shard_len, const Run* runs,
                        int32_t n_runs, const ClipScalars* clip, const StepConsts& k,
@@ -394,17 +579,55 @@ hipError_t launch_sumsq(int M, const GradPtrs& g, int64_t shard_len, double* par
 #undef ZS_CALL_SUMSQ
 }
 
-hipError_t launch_state_copy(bool do_export, const Piece* pieces, int64_t n_pieces,
-                             float* master, float* m, float* v, uint16_t* param, float* c_master,
-                             float* c_m, float* c_v, hipStream_t stream) {
+hipError_t launch_state_copy(bool do_export, bool param_f16, const Piece* pieces,
+                             int64_t n_pieces, float* master, float* m, float* v, uint16_t* param,
+                             float* c_master, float* c_m, float* c_v, hipStream_t stream) {
   if (n_pieces <= 0) return hipSuccess;
   if (n_pieces > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)n_pieces), block(kThreads);
   if (do_export)
-    hipLaunchKernelGGL(state_copy_kernel<true>, dim3((unsigned)n_pieces), dim3(kThreads), 0,
-                       stream, pieces, master, m, v, param, c_master, c_m, c_v);
+    hipLaunchKernelGGL((state_copy_kernel<true, false>), grid, block, 0, stream, pieces, master, m,
+                       v, param, c_master, c_m, c_v);
+  else if (param_f16)
+    hipLaunchKernelGGL((state_copy_kernel<false, true>), grid, block, 0, stream, pieces, master,
+                       m, v, param, c_master, c_m, c_v);
   else
-    hipLaunchKernelGGL(state_copy_kernel<false>, dim3((unsigned)n_pieces), dim3(kThreads), 0,
-                       stream, pieces, master, m, v, param, c_master, c_m, c_v);
+    hipLaunchKernelGGL((state_copy_kernel<false, false>), grid, block, 0, stream, pieces, master,
+                       m, v, param, c_master, c_m, c_v);
+  return hipGetLastError();
+}
+
+hipError_t launch_sumsq_f16(int M, const GradPtrs& g, int64_t shard_len, double* partials,
+                            const AmpState* st, hipStream_t stream) {
+  if (shard_len <= 0 || level1_partials(shard_len) > 0x7fffffff) return hipErrorInvalidValue;
+#define ZS_CALL_SUMSQ16(X) launch_sumsq_f16_m<X>(g, shard_len, partials, st, stream)
+  ZS_DISPATCH_M(M, ZS_CALL_SUMSQ16)
+#undef ZS_CALL_SUMSQ16
+}
+
+hipError_t launch_amp_finalize(const double* partials, int32_t n_partials, AmpState* st,
+                               const AmpParams& p, ClipScalars* out, StepConsts* kout,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(amp_finalize_kernel, dim3(1), dim3(kThreads), 0, stream, partials,
+                     n_partials, st, p, out, kout);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_f16(int M, const GradPtrs& g, float* master, float* m, float* v,
+                           uint16_t* param, int64_t shard_len, const Run* runs, int32_t n_runs,
+                           const ClipScalars* clip, const StepConsts* k, int32_t waves_per_cu,
+                           hipStream_t stream) {
+  if (shard_len <= 0) return hipSuccess;
+  if ((shard_len + kTile - 1) / kTile > 0x7fffffff || n_runs < 1) return hipErrorInvalidValue;
+  const size_t lds = waves_per_cu > 0 ? (kLdsPerCu / (size_t)waves_per_cu) & ~(size_t)255 : 0;
+#define ZS_CALL_STEP16(X) \
+  launch_step_f16_m<X>(g, master, m, v, param, shard_len, runs, n_runs, clip, k, lds, stream)
+  ZS_DISPATCH_M(M, ZS_CALL_STEP16)
+#undef ZS_CALL_STEP16
+}
+
+hipError_t launch_amp_state_init(AmpState* st, float scale, hipStream_t stream) {
+  hipLaunchKernelGGL(amp_state_init_kernel, dim3(1), dim3(64), 0, stream, st, scale);
   return hipGetLastError();
 }
 

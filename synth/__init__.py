@@ -70,6 +70,12 @@ def host_lib():
                                            ctypes.c_uint64, ctypes.c_uint64, ctypes.c_float,
                                            ctypes.c_float, ctypes.c_uint32, ctypes.c_uint32,
                                            ctypes.c_uint32]
+        lib.synth_grad_f16.restype = None
+        lib.synth_grad_f16.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
+                                       ctypes.c_int64, ctypes.c_float, ctypes.c_float]
+        lib.synth_grad_f16_at.restype = None
+        lib.synth_grad_f16_at.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_uint64, ctypes.c_float, ctypes.c_float]
         _host = lib
     return _host
 
@@ -89,8 +95,10 @@ def dev_lib():
         lib.synth_dev_gather.argtypes = [vp, vp, i32, vp, i64, vp]
         lib.synth_dev_scatter.argtypes = [vp, vp, i32, vp, i64, vp]
         lib.synth_dev_copy16.argtypes = [vp, vp, i64, vp]
+        lib.synth_dev_grad_f16.argtypes = [vp, i64, u64, i64, f32, f32, vp]
         for f in (lib.synth_dev_normal_f32, lib.synth_dev_grad_bf16, lib.synth_dev_zero_ranges,
-                  lib.synth_dev_gather, lib.synth_dev_scatter, lib.synth_dev_copy16):
+                  lib.synth_dev_gather, lib.synth_dev_scatter, lib.synth_dev_copy16,
+                  lib.synth_dev_grad_f16):
             f.restype = ctypes.c_int
         _dev = lib
     return _dev
@@ -166,6 +174,22 @@ def host_grad_bf16_at(idx: np.ndarray, k: int, ksel: int, sigma: float,
     return out
 
 
+def host_grad_f16(n: int, k: int, sigma: float, loss_scale: float, base: int = 0) -> np.ndarray:
+    """fp16 bit patterns (uint16) of ~N(0, sigma) * loss_scale, narrowed by truncation."""
+    out = np.empty(n, dtype=np.uint16)
+    host_lib().synth_grad_f16(out.ctypes.data, n, _u64(k), base, scale_for(sigma),
+                              np.float32(loss_scale))
+    return out
+
+
+def host_grad_f16_at(idx: np.ndarray, k: int, sigma: float, loss_scale: float) -> np.ndarray:
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    out = np.empty(idx.size, dtype=np.uint16)
+    host_lib().synth_grad_f16_at(out.ctypes.data, idx.ctypes.data, idx.size, _u64(k),
+                                 scale_for(sigma), np.float32(loss_scale))
+    return out
+
+
 # ---------------------------------------------------------- device side
 
 
@@ -193,6 +217,15 @@ def dev_grad_bf16(t, k: int, ksel: int, sigma: float, kinds: Kinds = NO_KINDS, b
     _check(dev_lib().synth_dev_grad_bf16(t.data_ptr(), t.numel(), _u64(k), _u64(ksel), base,
                                          scale_for(sigma), osc, z, sb, o, s),
            "synth_dev_grad_bf16")
+
+
+def dev_grad_f16(t, k: int, sigma: float, loss_scale: float, base: int = 0, stream=None):
+    """Fill a 2-byte device tensor with fp16 patterns of ~N(0, sigma) * loss_scale."""
+    import torch
+    assert t.element_size() == 2 and t.is_contiguous() and t.is_cuda
+    s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    _check(dev_lib().synth_dev_grad_f16(t.data_ptr(), t.numel(), _u64(k), base, scale_for(sigma),
+                                        np.float32(loss_scale), s), "synth_dev_grad_f16")
 
 
 def dev_zero_ranges(t, ranges, stream=None):

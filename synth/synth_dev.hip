@@ -52,6 +52,23 @@ __device__ __forceinline__ uint16_t grad_bf16(uint64_t key, uint64_t ksel,
   return upper16(normal_f32(hash_at(key, i), scale));
 }
 
+// fp32 -> fp16 by truncation (generator only; see synth_host.c).
+__device__ __forceinline__ uint16_t trunc_f16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  const uint32_t a = u & 0x7fffffffu;
+  if (a >= 0x47800000u) return (uint16_t)(sign | 0x7c00u);
+  if (a < 0x38800000u) return sign;
+  return (uint16_t)(sign | ((a - 0x38000000u) >> 13));
+}
+
+__global__ void k_grad_f16(uint16_t* out, int64_t n, uint64_t key, int64_t base, float scale,
+                           float loss_scale) {
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    out[i] = trunc_f16(normal_f32(hash_at(key, (uint64_t)(base + i)), scale) * loss_scale);
+}
+
 __global__ void k_normal_f32(float* out, int64_t n, uint64_t key, int64_t base,
                              float scale) {
   int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -134,6 +151,14 @@ int synth_dev_grad_bf16(uint16_t* out, int64_t n, uint64_t key, uint64_t ksel,
   hipLaunchKernelGGL(k_grad_bf16, dim3(grid_for(n)), dim3(kThreads), 0,
                      (hipStream_t)stream, out, n, key, ksel, base, scale,
                      out_scale, k);
+  return (int)hipGetLastError();
+}
+
+int synth_dev_grad_f16(uint16_t* out, int64_t n, uint64_t key, int64_t base, float scale,
+                       float loss_scale, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_grad_f16, dim3(grid_for(n)), dim3(kThreads), 0, (hipStream_t)stream, out,
+                     n, key, base, scale, loss_scale);
   return (int)hipGetLastError();
 }
 

@@ -16,6 +16,11 @@
  * (sigma / 37837.2275..., the sum's standard deviation).  That single
  * multiply is the only floating-point operation.
  * bf16 values are the upper 16 bits of that fp32 value (truncation).
+ * fp16 values (loss-scaled gradients): the normal value times an fp32 loss
+ * scale (a second single multiply), narrowed to fp16 by truncating the
+ * mantissa toward zero; magnitudes past the fp16 range become Inf and those
+ * below 2^-14 are flushed to zero -- the generator's own narrowing, not the
+ * round-to-nearest conversion of the method.
  * Gradient "kinds" (for the stress workload) come from a second hash stream:
  * r = (h_sel >> 32) mod 10^6 selects exact zero, a bf16 subnormal or an
  * outlier (the normal value with a larger scale) with given counts per million.
@@ -117,4 +122,34 @@ void synth_grad_bf16_at(uint16_t *out, const int64_t *idx, int64_t n,
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; i++)
         out[i] = grad_bf16(key, ksel, (uint64_t)idx[i], scale, out_scale, k);
+}
+
+/* fp32 -> fp16 by truncation (generator only): |x| >= 65536 -> Inf, |x| < 2^-14 -> 0. */
+static inline uint16_t trunc_f16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t a = u & 0x7fffffffu;
+    if (a >= 0x47800000u)
+        return (uint16_t)(sign | 0x7c00u);
+    if (a < 0x38800000u)
+        return sign;
+    return (uint16_t)(sign | ((a - 0x38000000u) >> 13));
+}
+
+void synth_grad_f16(uint16_t *out, int64_t n, uint64_t key, int64_t base, float scale,
+                    float loss_scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        out[i] = trunc_f16(normal_f32(synth_hash(key, (uint64_t)(base + i)), scale) * loss_scale);
+}
+
+void synth_grad_f16_at(uint16_t *out, const int64_t *idx, int64_t n, uint64_t key, float scale,
+                       float loss_scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        out[i] = trunc_f16(normal_f32(synth_hash(key, (uint64_t)idx[i]), scale) * loss_scale);
 }
