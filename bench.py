@@ -12,6 +12,7 @@ using the algorithmic bytes 2M+12 read + 14 written per parameter;
 `cpu_baseline` times the CPU oracle on a bounded slab of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload 1..5] [--no-cpu-baseline]
+                    [--checkpoint] [--amp]
 """
 from __future__ import annotations
 
@@ -73,19 +74,30 @@ def cpu_baseline(w, slab: int, min_seconds: float = 10.0) -> dict:
     b = np.zeros(slab, np.uint16)
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
     clip = w.max_grad_norm > 0
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        coef = oracle.clip_coef(oracle.grad_sumsq(grads), w.max_grad_norm) if clip else None
-        oracle.step_f32(grads, p, m, v, b, None, step=steps + 1, coef=coef, **hp)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
+
+    def run(n: int, seconds: float):
+        oracle.set_threads(n)
+        steps = 0
+        t0 = time.perf_counter()
+        while True:
+            coef = oracle.clip_coef(oracle.grad_sumsq(grads), w.max_grad_norm) if clip else None
+            oracle.step_f32(grads, p, m, v, b, None, step=steps + 1, coef=coef, **hp)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return steps, el
+
+    try:
+        steps, el = run(threads, min_seconds)
+        steps1, el1 = run(1, min_seconds / 4)
+    finally:
+        oracle.set_threads(threads)
     return {"value": slab * steps / el, "unit": "params/s", "cores": int(threads),
             "kind": "oracle",
+            "one_thread_value": slab * steps1 / el1,
             "sample": f"{steps} oracle steps over a {slab:,}-element slab of the shard "
-                      f"(M={w.M}{', with the norm pass' if clip else ''}), {el:.1f} s"}
+                      f"(M={w.M}{', with the norm pass' if clip else ''}), {el:.1f} s on "
+                      f"{threads} threads; then {steps1} steps on one thread, {el1:.1f} s"}
 
 
 def time_checkpoint(zs, w, stream, reps: int = 10) -> dict:
@@ -113,6 +125,86 @@ def time_checkpoint(zs, w, stream, reps: int = 10) -> dict:
     return out
 
 
+def percentiles(xs) -> dict:
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90))}
+
+
+def time_cold(zs, grads, w, hp, stream, step0: int, reps: int) -> dict:
+    """Per-step time with the 256 MB Infinity Cache evicted before each step (a
+    1 GiB buffer is overwritten between steps, outside the timed events)."""
+    import torch
+    junk = torch.empty(1 << 28, dtype=torch.float32, device=zs.device)
+    out = []
+    for r in range(reps):
+        junk.fill_(float(r))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        zs.step(grads, step=step0 + r, max_grad_norm=w.max_grad_norm, **hp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    del junk
+    return percentiles(out)
+
+
+def time_amp(w, pad, dev, stream, steps: int, warmup: int, stage: bool = False,
+             init_scale: float = 2.0 ** 14) -> dict:
+    """The fp16 loss-scaled variant on the same shard: fp16 contributions
+    (generated at the initial loss scale), unscale fused into the reduce, the
+    norm pass that detects overflow on every step, the device-side skip and
+    scaler update, and the fp16 re-cast.  Bytes per parameter: 2M (norm pass)
+    + 2M + 12 read + 14 written (step kernel); staged (ZS_STAGE_AVERAGE): the
+    norm pass reads 2M and writes 4, the step reads 4 + 12 and writes 14."""
+    import torch
+
+    import synth
+    from sharded_optimizer_step_zero_amd import ZS_STAGE_AVERAGE, ZeroShard
+
+    za = ZeroShard(w.numel, w.decay, w.world_size, w.rank, w.M, device=dev,
+                   bucket_cap=w.bucket_cap, align=w.align, fp16=True,
+                   flags=ZS_STAGE_AVERAGE if stage else 0)
+    za.set_stream(stream.cuda_stream)
+    S = za.shard_len
+    synth.dev_normal_f32(za.master[:S], w.master_key(), w.sigma_master)
+    synth.dev_zero_ranges(za.master, pad)
+    grads = []
+    for k, _ in w.grad_keys(0):
+        g = torch.empty(max(S, 8), dtype=torch.float16, device=dev)
+        synth.dev_grad_f16(g[:S], k, w.sigma_grad, init_scale)
+        synth.dev_zero_ranges(g, pad)
+        grads.append(g)
+    za.amp_init(init_scale)
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+              max_grad_norm=w.max_grad_norm)
+    for _ in range(warmup):
+        za.step_amp(grads, **hp)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        za.step_amp(grads, **hp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    scale, tracker, applied = za.amp_read()
+    bpp = 2 * w.M + 34 if stage else 4 * w.M + 26
+    by = S * bpp
+    za.close()
+    del grads
+    return {"ms_per_step": ms, "params_per_s": S / (ms * 1e-3), "staged": stage,
+            "bytes_per_param": bpp,
+            "hbm_gbs_whole_step": by / (ms * 1e-3) / 1e9,
+            "frac_of_peak_whole_step": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "applied_steps": applied, "final_scale": scale,
+            "kernels": "zs::sumsq_f16_kernel, sum_blocks, amp_finalize, "
+                       + ("zs::step_staged_kernel<true>" if stage else "zs::step_f16_kernel")}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +216,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--checkpoint", action="store_true",
                     help="also time the state export/import used for checkpoints and resharding")
+    ap.add_argument("--amp", action="store_true",
+                    help="also time the fp16 loss-scaled variant on the same shard")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps with the Infinity Cache evicted (default for the tiny "
+                         "workload)")
     ap.add_argument("--cpu-slab", type=int, default=1 << 25)
     ap.add_argument("--calibrate-copy-gib", type=float, default=1.0,
                     help="size of the plain copy run once before timing (counter calibration)")
@@ -172,17 +269,23 @@ def main():
         zs.step(grads, step=s + 1, max_grad_norm=w.max_grad_norm, **hp)
     torch.cuda.synchronize()
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: the total and the per-step spread
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    ev0.record(stream)
+    evs[0].record(stream)
     for s in range(args.steps):
         zs.step(grads, step=args.warmup + s + 1, max_grad_norm=w.max_grad_norm, **hp)
-    ev1.record(stream)
+        evs[s + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
+    gpu_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = gpu_ms / args.steps
+    per_step = percentiles([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+
+    cold = None
+    if args.cold or w.name.startswith("tiny"):
+        cold = time_cold(zs, grads, w, hp, stream, args.warmup + args.steps + 1,
+                         max(args.steps // 4, 5))
 
     # the step kernel alone (per-launch average): when clipping, the norm pass is
     # timed separately and removed
@@ -228,6 +331,8 @@ def main():
             "hbm_gbs_whole_step": by["total"] / (ms_per_step * 1e-3) / 1e9,
             "pct_of_peak_whole_step": 100.0 * by["total"] / (ms_per_step * 1e-3) / 1e9
                                       / PEAK_HBM_GBS,
+            "per_step_ms": per_step,
+            "cold_per_step_ms": cold,
             "wall_s_timed": wall,
             "setup_s": setup_s,
         },
@@ -246,6 +351,9 @@ def main():
     }
     if args.checkpoint:
         out["checkpoint"] = time_checkpoint(zs, w, stream)
+    if args.amp:
+        out["amp_fp16"] = time_amp(w, pad, dev, stream, args.steps, args.warmup)
+        out["amp_fp16_staged"] = time_amp(w, pad, dev, stream, args.steps, args.warmup, True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_slab, S))
     print(json.dumps(out), flush=True)

@@ -80,6 +80,13 @@ enum {
 /* zero_shard_init flags */
 #define ZS_SKIP_NONFINITE 1u /* non-finite norm: the step leaves every array untouched */
 #define ZS_FP16 2u           /* gradients and the param copy are fp16 (zero_shard_step_amp) */
+/* When a call runs the norm pass (clip, grad_norm_out or ZS_SKIP_NONFINITE in
+ * zero_shard_step; always in zero_shard_step_amp), that pass also stores each
+ * element's averaged gradient (fp32, unscaled) in the workspace, and the step
+ * reads those 4 bytes instead of the M contributions again.  Gradient bytes per
+ * element go from 2M + 2M to 2M + 4 + 4: fewer for M > 4.  The workspace grows
+ * by 4 * shard_len bytes.  Results are bit-identical either way. */
+#define ZS_STAGE_AVERAGE 4u
 
 /* Device state of the dynamic loss scaler (16 bytes of caller-owned device
  * memory, 16-byte aligned), read and updated by zero_shard_step_amp. */
@@ -140,20 +147,23 @@ int zs_plan_state_bytes(const zs_plan *plan, int32_t stage, int64_t *bytes);
 
 void zs_plan_destroy(zs_plan *plan);
 
-/* Device workspace a context of this plan needs (run table, piece table, norm
- * partials, clip coefficient), in bytes; 0 if plan is NULL.  M is accepted for forward
- * compatibility and does not change the size. */
-size_t zs_workspace_bytes(const zs_plan *plan, int32_t M);
+/* Device workspace a context of this plan needs with these init flags (run
+ * table, piece table, norm partials, clip scalars and, with ZS_STAGE_AVERAGE,
+ * 4 * shard_len bytes of staged averages), in bytes; 0 if plan is NULL.  M is
+ * accepted for forward compatibility and does not change the size. */
+size_t zs_workspace_bytes(const zs_plan *plan, int32_t M, uint32_t flags);
 
 /* ------------------------------------------------------------ the step */
 
 /*
  * Binds a context to one rank's device buffers (each shard_len elements):
  * param_bf16 (bf16, written by every step), master, exp_avg, exp_avg_sq
- * (fp32, read and written), and a workspace of zs_workspace_bytes(plan, M).
+ * (fp32, read and written), and a workspace of zs_workspace_bytes(plan, M, flags)
+ * bytes, 256-byte aligned.
  * The caller initialises master, sets exp_avg = exp_avg_sq = 0 and zeroes
  * the padding; param_bf16 is output only.  M in [1, ZS_MAX_M] is the number of
- * gradient contributions each step reduces.  flags: ZS_SKIP_NONFINITE or 0.
+ * gradient contributions each step reduces.  flags: any of ZS_SKIP_NONFINITE,
+ * ZS_FP16, ZS_STAGE_AVERAGE (0 for none).
  * Uploads the run table on `stream` and waits for that copy.  The plan may
  * be destroyed afterwards.  Errors: ZS_EINVAL, ZS_ENOMEM, ZS_EHIP.
  */

@@ -27,6 +27,7 @@ ZS_EHIP = -3
 ZS_ESTATE = -4
 ZS_SKIP_NONFINITE = 1
 ZS_FP16 = 2
+ZS_STAGE_AVERAGE = 4
 ZS_MAX_M = 16
 
 if not os.path.exists(LIB_PATH):
@@ -64,7 +65,7 @@ _sig("zs_plan_bucket", ctypes.c_int, _vp, _i64, _P(_i64), _P(_i64))
 _sig("zs_plan_run", ctypes.c_int, _vp, _i64, _P(_i64), _P(_i64), _P(_i32))
 _sig("zs_plan_state_bytes", ctypes.c_int, _vp, _i32, _P(_i64))
 _sig("zs_plan_destroy", None, _vp)
-_sig("zs_workspace_bytes", _sz, _vp, _i32)
+_sig("zs_workspace_bytes", _sz, _vp, _i32, _u32)
 _sig("zero_shard_init", ctypes.c_int, _P(_vp), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
      _u32)
 _sig("zero_shard_step", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _i64, _f32,
@@ -176,8 +177,8 @@ def zs_plan_destroy(plan: int) -> None:
     _lib.zs_plan_destroy(plan)
 
 
-def zs_workspace_bytes(plan: int, M: int) -> int:
-    return int(_lib.zs_workspace_bytes(plan, M))
+def zs_workspace_bytes(plan: int, M: int, flags: int = 0) -> int:
+    return int(_lib.zs_workspace_bytes(plan, M, flags))
 
 
 # ------------------------------------------------------------------ step
@@ -290,7 +291,7 @@ class ZeroShard:
             flags |= ZS_FP16
         self.param = torch.zeros(S, dtype=torch.float16 if fp16 else torch.bfloat16, device=dev)
         self.amp_state = None
-        self.ws_bytes = zs_workspace_bytes(self.plan, M)
+        self.ws_bytes = zs_workspace_bytes(self.plan, M, flags)
         # torch's caching allocator returns 512-byte aligned blocks
         self.workspace = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
         self._stream = stream

@@ -25,9 +25,10 @@ struct zs_ctx {
   int32_t M = 0;
   uint32_t flags = 0;
   bool fp16 = false;
+  bool stage = false;  // ZS_STAGE_AVERAGE
   int64_t shard_len = 0, n_pieces = 0, canon_len = 0;
   int32_t n_runs = 0;
-  int32_t waves_per_cu = 0;
+  int32_t waves_per_cu = 0, waves_per_cu_staged = 0;
   uint16_t* param = nullptr;
   float* master = nullptr;
   float* m = nullptr;
@@ -41,7 +42,12 @@ namespace {
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-zs::WorkspaceLayout workspace_layout(int64_t n_runs, int64_t n_pieces, int64_t n_partials) {
+// The scalars block is 256 bytes: ClipScalars at 0, the device-computed
+// StepConsts at 64.  The staging area (ZS_STAGE_AVERAGE) comes last.
+zs::WorkspaceLayout workspace_layout(int64_t n_runs, int64_t n_pieces, int64_t n_partials,
+                                     int64_t stage_elems) {
+  static_assert(sizeof(zs::ClipScalars) <= 64 && sizeof(zs::StepConsts) <= 192,
+                "scalars block overflow");
   zs::WorkspaceLayout l{};
   l.runs_off = 0;
   l.runs_bytes = (size_t)(n_runs + 1) * sizeof(zs::Run);
@@ -49,8 +55,16 @@ zs::WorkspaceLayout workspace_layout(int64_t n_runs, int64_t n_pieces, int64_t n
   l.pieces_bytes = (size_t)n_pieces * sizeof(zs::Piece);
   l.partials_off = l.pieces_off + round256(l.pieces_bytes);
   l.scalars_off = l.partials_off + round256((size_t)n_partials * sizeof(double));
-  l.total = l.scalars_off + round256(sizeof(zs::ClipScalars));
+  l.stage_off = l.scalars_off + 256;
+  l.stage_bytes = round256((size_t)stage_elems * sizeof(float));
+  l.total = l.stage_off + l.stage_bytes;
   return l;
+}
+
+zs::WorkspaceLayout plan_workspace(const zs_plan* plan, uint32_t flags) {
+  return workspace_layout((int64_t)plan->runs.size(), (int64_t)plan->pieces.size(),
+                          zs::sumsq_partials(plan->shard_len),
+                          (flags & ZS_STAGE_AVERAGE) ? plan->shard_len : 0);
 }
 
 // Resident-wave cap of the step kernel per CU, measured on MI355X: fewer
@@ -112,6 +126,9 @@ zs::ClipScalars* scalars(zs_ctx* ctx) {
 zs::StepConsts* device_consts(zs_ctx* ctx) {
   return reinterpret_cast<zs::StepConsts*>(ctx->ws + ctx->lay.scalars_off + 64);
 }
+float* stage_area(zs_ctx* ctx) {
+  return ctx->stage ? reinterpret_cast<float*>(ctx->ws + ctx->lay.stage_off) : nullptr;
+}
 double* partials(zs_ctx* ctx) { return reinterpret_cast<double*>(ctx->ws + ctx->lay.partials_off); }
 // the level-2 partials the finalize step sums
 const double* final_partials(zs_ctx* ctx) {
@@ -123,12 +140,10 @@ const zs::Run* run_table(zs_ctx* ctx) {
 
 }  // namespace
 
-extern "C" size_t zs_workspace_bytes(const zs_plan* plan, int32_t M) {
+extern "C" size_t zs_workspace_bytes(const zs_plan* plan, int32_t M, uint32_t flags) {
   (void)M;
   if (!plan) return 0;
-  return workspace_layout((int64_t)plan->runs.size(), (int64_t)plan->pieces.size(),
-                          zs::sumsq_partials(plan->shard_len))
-      .total;
+  return plan_workspace(plan, flags).total;
 }
 
 extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, void* param_bf16,
@@ -138,7 +153,8 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   *out = nullptr;
   if (!plan) return einval("zero_shard_init: plan is NULL");
   if (M < 1 || M > ZS_MAX_M) return einval("zero_shard_init: M must lie in [1, 16]");
-  if (flags & ~(ZS_SKIP_NONFINITE | ZS_FP16)) return einval("zero_shard_init: unknown flag");
+  if (flags & ~(ZS_SKIP_NONFINITE | ZS_FP16 | ZS_STAGE_AVERAGE))
+    return einval("zero_shard_init: unknown flag");
   if (!param_bf16 || !master || !exp_avg || !exp_avg_sq || !workspace)
     return einval("zero_shard_init: NULL buffer");
   if (!aligned16(param_bf16) || !aligned16(master) || !aligned16(exp_avg) ||
@@ -147,10 +163,9 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   if (((uintptr_t)workspace & 255u) != 0)
     return einval("zero_shard_init: workspace must be 256-byte aligned");
   if (plan->runs.size() > 0x3fffffff) return einval("zero_shard_init: too many runs");
-  const int64_t n_partials = zs::sumsq_partials(plan->shard_len);
-  const zs::WorkspaceLayout lay =
-      workspace_layout((int64_t)plan->runs.size(), (int64_t)plan->pieces.size(), n_partials);
-  if (workspace_bytes < lay.total) return einval("zero_shard_init: workspace too small");
+  const zs::WorkspaceLayout lay = plan_workspace(plan, flags);
+  if (workspace_bytes < lay.total)
+    return einval("zero_shard_init: workspace smaller than zs_workspace_bytes(plan, M, flags)");
   std::vector<zs::Run> table;
   try {
     table = plan->runs;
@@ -169,11 +184,13 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   c->M = M;
   c->flags = flags;
   c->fp16 = (flags & ZS_FP16) != 0;
+  c->stage = (flags & ZS_STAGE_AVERAGE) != 0;
   c->shard_len = plan->shard_len;
   c->n_runs = (int32_t)(table.size() - 1);
   c->n_pieces = (int64_t)plan->pieces.size();
   c->canon_len = plan->total_params;
   c->waves_per_cu = default_waves_per_cu(M);
+  c->waves_per_cu_staged = default_waves_per_cu(2);  // 16 B of gradient per lane, like M = 2
   c->param = static_cast<uint16_t*>(param_bf16);
   c->master = master;
   c->m = exp_avg;
@@ -205,9 +222,11 @@ int enqueue_step(zs_ctx* ctx, const zs::GradPtrs& g, const zs::StepConsts& k, bo
                  bool clip, float max_norm, const double* external_sumsq) {
   hipError_t e;
   zs::ClipScalars* sc = scalars(ctx);
+  // staging pays only where this call runs the norm pass itself
+  float* stage = (need_norm && !external_sumsq) ? stage_area(ctx) : nullptr;
   if (need_norm) {
     if (!external_sumsq) {
-      e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), ctx->stream);
+      e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), stage, ctx->stream);
       if (e != hipSuccess) return ehip("zero_shard_step: norm pass", e);
     }
     e = zs::launch_finalize(final_partials(ctx), zs::final_partials(ctx->shard_len),
@@ -215,9 +234,14 @@ int enqueue_step(zs_ctx* ctx, const zs::GradPtrs& g, const zs::StepConsts& k, bo
                             (ctx->flags & ZS_SKIP_NONFINITE) ? 1 : 0, sc, ctx->stream);
     if (e != hipSuccess) return ehip("zero_shard_step: norm finalize", e);
   }
-  e = zs::launch_step(ctx->M, need_norm, g, ctx->master, ctx->m, ctx->v, ctx->param,
-                      ctx->shard_len, run_table(ctx), ctx->n_runs, sc, k, ctx->waves_per_cu,
-                      ctx->stream);
+  if (stage)
+    e = zs::launch_step_staged(false, stage, ctx->master, ctx->m, ctx->v, ctx->param,
+                               ctx->shard_len, run_table(ctx), ctx->n_runs, sc, k, nullptr,
+                               ctx->waves_per_cu_staged, ctx->stream);
+  else
+    e = zs::launch_step(ctx->M, need_norm, g, ctx->master, ctx->m, ctx->v, ctx->param,
+                        ctx->shard_len, run_table(ctx), ctx->n_runs, sc, k, ctx->waves_per_cu,
+                        ctx->stream);
   if (e != hipSuccess) return ehip("zero_shard_step: step kernel", e);
   return ZS_OK;
 }
@@ -271,7 +295,8 @@ extern "C" int zero_shard_grad_sumsq(zs_ctx* ctx, const void* const* grads, doub
   // an empty shard sums zero partials, which writes 0 (no memset: capture-safe)
   const int32_t n_final = ctx->shard_len ? zs::final_partials(ctx->shard_len) : 0;
   hipError_t e = hipSuccess;
-  if (n_final) e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), ctx->stream);
+  if (n_final)
+    e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), nullptr, ctx->stream);
   if (e == hipSuccess) e = zs::launch_sumsq_total(final_partials(ctx), n_final, sumsq_dev,
                                                   ctx->stream);
   return e == hipSuccess ? ZS_OK : ehip("zero_shard_grad_sumsq", e);
@@ -368,14 +393,22 @@ extern "C" int zero_shard_step_amp(zs_ctx* ctx, const void* const* grads, float 
   p.backoff = backoff_factor;
   p.interval = growth_interval;
   p.clip = max_grad_norm > 0.0f ? 1 : 0;
-  hipError_t e = zs::launch_sumsq_f16(ctx->M, g, ctx->shard_len, partials(ctx), st, ctx->stream);
+  float* stage = stage_area(ctx);
+  hipError_t e =
+      zs::launch_sumsq_f16(ctx->M, g, ctx->shard_len, partials(ctx), st, stage, ctx->stream);
   if (e != hipSuccess) return ehip("zero_shard_step_amp: norm pass", e);
   e = zs::launch_amp_finalize(final_partials(ctx), zs::final_partials(ctx->shard_len), st, p,
                               scalars(ctx), device_consts(ctx), ctx->stream);
   if (e != hipSuccess) return ehip("zero_shard_step_amp: finalize", e);
-  e = zs::launch_step_f16(ctx->M, g, ctx->master, ctx->m, ctx->v, ctx->param, ctx->shard_len,
-                          run_table(ctx), ctx->n_runs, scalars(ctx), device_consts(ctx),
-                          ctx->waves_per_cu, ctx->stream);
+  if (stage)
+    e = zs::launch_step_staged(true, stage, ctx->master, ctx->m, ctx->v, ctx->param,
+                               ctx->shard_len, run_table(ctx), ctx->n_runs, scalars(ctx),
+                               zs::StepConsts{}, device_consts(ctx), ctx->waves_per_cu_staged,
+                               ctx->stream);
+  else
+    e = zs::launch_step_f16(ctx->M, g, ctx->master, ctx->m, ctx->v, ctx->param, ctx->shard_len,
+                            run_table(ctx), ctx->n_runs, scalars(ctx), device_consts(ctx),
+                            ctx->waves_per_cu, ctx->stream);
   if (e != hipSuccess) return ehip("zero_shard_step_amp: step kernel", e);
   if (grad_norm_out) {
     double norm = 0.0;

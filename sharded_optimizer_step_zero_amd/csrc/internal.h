@@ -69,7 +69,8 @@ struct WorkspaceLayout {
   size_t runs_off, runs_bytes;  // n_runs + 1 Run entries (the last is a sentinel)
   size_t pieces_off, pieces_bytes;  // n_pieces Piece entries
   size_t partials_off;          // sumsq_partials(shard_len) doubles
-  size_t scalars_off;           // ClipScalars
+  size_t scalars_off;           // 256-byte block: ClipScalars, then StepConsts at +64
+  size_t stage_off, stage_bytes;  // shard_len floats with ZS_STAGE_AVERAGE, else empty
   size_t total;
 };
 
@@ -125,8 +126,10 @@ int32_t final_partials(int64_t shard_len);
 
 // Kernel launchers (kernels.hip).  All enqueue on `stream`.
 // The norm pass over a non-empty shard: both partial levels into `partials`.
+// stage (nullable): also store the fp32 averages, shard_len floats, for
+// launch_step_staged.
 hipError_t launch_sumsq(int M, const GradPtrs& g, int64_t shard_len, double* partials,
-                        hipStream_t stream);
+                        float* stage, hipStream_t stream);
 // Reduces the partials (or takes *external_sumsq when non-null) into *out.
 hipError_t launch_finalize(const double* partials, int32_t n_partials,
                            const double* external_sumsq, float max_norm, int clip,
@@ -137,7 +140,7 @@ hipError_t launch_sumsq_total(const double* partials, int32_t n_partials, double
 // step that also computes the step constants on the device and updates the
 // scaler, the step kernel, and the scaler initialisation.
 hipError_t launch_sumsq_f16(int M, const GradPtrs& g, int64_t shard_len, double* partials,
-                            const AmpState* st, hipStream_t stream);
+                            const AmpState* st, float* stage, hipStream_t stream);
 hipError_t launch_amp_finalize(const double* partials, int32_t n_partials, AmpState* st,
                                const AmpParams& p, ClipScalars* out, StepConsts* kout,
                                hipStream_t stream);
@@ -146,6 +149,12 @@ hipError_t launch_step_f16(int M, const GradPtrs& g, float* master, float* m, fl
                            const ClipScalars* clip, const StepConsts* k, int32_t waves_per_cu,
                            hipStream_t stream);
 hipError_t launch_amp_state_init(AmpState* st, float scale, hipStream_t stream);
+// The step on the averages a norm pass staged (amp: constants *kd and an fp16
+// param; otherwise kh and a bf16 param).
+hipError_t launch_step_staged(bool amp, const float* stage, float* master, float* m, float* v,
+                              uint16_t* param, int64_t shard_len, const Run* runs, int32_t n_runs,
+                              const ClipScalars* clip, const StepConsts& kh, const StepConsts* kd,
+                              int32_t waves_per_cu, hipStream_t stream);
 
 // waves_per_cu > 0 caps the resident waves per CU of the step kernel (0: no cap).
 // Copies fp32 master/m/v between the shard and the canonical order over the

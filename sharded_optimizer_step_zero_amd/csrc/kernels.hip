@@ -132,6 +132,16 @@ __device__ __forceinline__ int32_t find_run(const Run* __restrict__ runs, int32_
   return lo;
 }
 
+// Eight consecutive fp32 values as two 16-byte non-temporal stores (p is
+// 32-byte aligned: a multiple-of-8 element offset into a 256-byte-aligned array).
+__device__ __forceinline__ void store8(float* p, const float (&s)[8]) {
+  f32x4 a, b;
+  a[0] = s[0]; a[1] = s[1]; a[2] = s[2]; a[3] = s[3];
+  b[0] = s[4]; b[1] = s[5]; b[2] = s[6]; b[3] = s[7];
+  __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p));
+  __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p + 4));
+}
+
 // LDS per CU on gfx950; reserving lds_cu / waves_per_cu bytes per single-wave
 // workgroup lets at most waves_per_cu of them reside on a CU.
 constexpr size_t kLdsPerCu = 160 * 1024;
@@ -224,9 +234,11 @@ __device__ __forceinline__ double block_sum(double x) {
 // Norm pass, level 1: one 2048-element tile per workgroup (in-order, short-lived
 // workgroups stream best); each lane squares its 8 averaged values in fp64 (the
 // square of an fp32 value is exact in fp64), the workgroup sums in a fixed order.
-template <int M>
+// With STAGE it also stores the 8 averages to stage[e..e+8) for the staged step.
+template <int M, bool STAGE>
 __global__ __launch_bounds__(kThreads) void sumsq_kernel(GradPtrs g, int64_t n,
-                                                         double* __restrict__ partials) {
+                                                         double* __restrict__ partials,
+                                                         float* __restrict__ stage) {
   const int64_t e = (int64_t)blockIdx.x * kNormTile + (int64_t)threadIdx.x * kVec;
   double acc = 0.0;
   if (e < n) {  // n is a multiple of 8
@@ -237,6 +249,7 @@ __global__ __launch_bounds__(kThreads) void sumsq_kernel(GradPtrs g, int64_t n,
       const double x = (double)s[q];
       acc = acc + x * x;
     }
+    if (STAGE) store8(stage + e, s);
   }
   const double t = block_sum(acc);
   if (threadIdx.x == 0) partials[blockIdx.x] = t;
@@ -325,10 +338,11 @@ __global__ __launch_bounds__(kThreads) void state_copy_kernel(
 // hardware's IEEE fp16 <-> fp32 instructions (exact widening; round to nearest
 // even narrowing with overflow to Inf).
 
-template <int M>
+template <int M, bool STAGE>
 __global__ __launch_bounds__(kThreads) void sumsq_f16_kernel(GradPtrs g, int64_t n,
                                                              double* __restrict__ partials,
-                                                             const AmpState* __restrict__ st) {
+                                                             const AmpState* __restrict__ st,
+                                                             float* __restrict__ stage) {
   const float inv = (float)(1.0 / (double)st->scale);
   const int64_t e = (int64_t)blockIdx.x * kNormTile + (int64_t)threadIdx.x * kVec;
   double acc = 0.0;
@@ -352,10 +366,11 @@ __global__ __launch_bounds__(kThreads) void sumsq_f16_kernel(GradPtrs g, int64_t
     }
 #pragma unroll
     for (int q = 0; q < kVec; q++) {
-      const float gq = (s[q] / (float)M) * inv;
-      const double x = (double)gq;
+      s[q] = (s[q] / (float)M) * inv;
+      const double x = (double)s[q];
       acc = acc + x * x;
     }
+    if (STAGE) store8(stage + e, s);
   }
   const double t = block_sum(acc);
   if (threadIdx.x == 0) partials[blockIdx.x] = t;
@@ -464,12 +479,66 @@ __global__ void amp_state_init_kernel(AmpState* st, float scale) {
   }
 }
 
+// The step on a staged average: the norm pass of the same call stored each
+// element's averaged (and, for fp16, unscaled) gradient, so this pass reads 4
+// bytes of gradient per element instead of the M contributions.  The values
+// are the very bits the fused kernels recompute, so results are identical.
+// AMP: constants from the device (loss-scaled path), fp16 param; otherwise the
+// host's constants and a bf16 param.
+template <bool AMP>
+__global__ __launch_bounds__(kStepLanes) void step_staged_kernel(
+    const float* __restrict__ stage, float* __restrict__ master, float* __restrict__ mom1,
+    float* __restrict__ mom2, uint16_t* __restrict__ param, int64_t n,
+    const Run* __restrict__ runs, int32_t n_runs, const ClipScalars* __restrict__ clip,
+    StepConsts kh, const StepConsts* __restrict__ kd) {
+  const int64_t tile0 = (int64_t)blockIdx.x * kTile;
+  const int64_t e = tile0 + (int64_t)threadIdx.x * kStepVec;
+  if (e >= n) return;
+  f32x4 g4 = ld_stream(reinterpret_cast<const f32x4*>(stage + e));
+  f32x4 p4 = ld_stream(reinterpret_cast<const f32x4*>(master + e));
+  f32x4 m4 = ld_stream(reinterpret_cast<const f32x4*>(mom1 + e));
+  f32x4 v4 = ld_stream(reinterpret_cast<const f32x4*>(mom2 + e));
+  int32_t r = 0;
+  if (n_runs > 1) {
+    r = find_run(runs, n_runs, tile0);
+    if (runs[r + 1].start < tile0 + kTile) {
+      while (runs[r + 1].start <= e) r++;
+    }
+  }
+  if (clip->skip) return;  // uniform over the grid
+  const StepConsts k = AMP ? *kd : kh;
+  const float coef = clip->coef;  // 1 when the call does not clip
+  const float d = (runs[r].flags & 1) ? k.decay_mul : 1.0f;
+  uint32_t b[kStepVec];
+#pragma unroll
+  for (int q = 0; q < kStepVec; q++) {
+    const float gq = g4[q] * coef;
+    float p = p4[q], m = m4[q], v = v4[q];
+    adamw(gq, p, m, v, k, d);
+    p4[q] = p;
+    m4[q] = m;
+    v4[q] = v;
+    b[q] = AMP ? f2h(p) : to_bf16(p);
+  }
+  __builtin_nontemporal_store(p4, reinterpret_cast<f32x4*>(master + e));
+  __builtin_nontemporal_store(m4, reinterpret_cast<f32x4*>(mom1 + e));
+  __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(mom2 + e));
+  u32x2 pk;
+  pk.x = b[0] | (b[1] << 16);
+  pk.y = b[2] | (b[3] << 16);
+  __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(param + e));
+}
+
 template <int M>
 hipError_t launch_sumsq_f16_m(const GradPtrs& g, int64_t shard_len, double* partials,
-                              const AmpState* st, hipStream_t stream) {
+                              const AmpState* st, float* stage, hipStream_t stream) {
   const int64_t p1 = (shard_len + kNormTile - 1) / kNormTile;
-  hipLaunchKernelGGL((sumsq_f16_kernel<M>), dim3((unsigned)p1), dim3(kThreads), 0, stream, g,
-                     shard_len, partials, st);
+  if (stage)
+    hipLaunchKernelGGL((sumsq_f16_kernel<M, true>), dim3((unsigned)p1), dim3(kThreads), 0, stream,
+                       g, shard_len, partials, st, stage);
+  else
+    hipLaunchKernelGGL((sumsq_f16_kernel<M, false>), dim3((unsigned)p1), dim3(kThreads), 0,
+                       stream, g, shard_len, partials, st, stage);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t p2 = (p1 + kLevel2 - 1) / kLevel2;
@@ -506,11 +575,15 @@ hipError_t launch_step_m(bool use_clip, const GradPtrs& g, float* master, float*
 }
 
 template <int M>
-hipError_t launch_sumsq_m(const GradPtrs& g, int64_t shard_len, double* partials,
+hipError_t launch_sumsq_m(const GradPtrs& g, int64_t shard_len, double* partials, float* stage,
                           hipStream_t stream) {
   const int64_t p1 = (shard_len + kNormTile - 1) / kNormTile;
-  hipLaunchKernelGGL((sumsq_kernel<M>), dim3((unsigned)p1), dim3(kThreads), 0, stream, g,
-                     shard_len, partials);
+  if (stage)
+    hipLaunchKernelGGL((sumsq_kernel<M, true>), dim3((unsigned)p1), dim3(kThreads), 0, stream, g,
+                       shard_len, partials, stage);
+  else
+    hipLaunchKernelGGL((sumsq_kernel<M, false>), dim3((unsigned)p1), dim3(kThreads), 0, stream,
+                       g, shard_len, partials, stage);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t p2 = (p1 + kLevel2 - 1) / kLevel2;
@@ -572,9 +645,9 @@ hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, f
 }
 
 hipError_t launch_sumsq(int M, const GradPtrs& g, int64_t shard_len, double* partials,
-                        hipStream_t stream) {
+                        float* stage, hipStream_t stream) {
   if (shard_len <= 0 || level1_partials(shard_len) > 0x7fffffff) return hipErrorInvalidValue;
-#define ZS_CALL_SUMSQ(X) launch_sumsq_m<X>(g, shard_len, partials, stream)
+#define ZS_CALL_SUMSQ(X) launch_sumsq_m<X>(g, shard_len, partials, stage, stream)
   ZS_DISPATCH_M(M, ZS_CALL_SUMSQ)
 #undef ZS_CALL_SUMSQ
 }
@@ -598,9 +671,9 @@ hipError_t launch_state_copy(bool do_export, bool param_f16, const Piece* pieces
 }
 
 hipError_t launch_sumsq_f16(int M, const GradPtrs& g, int64_t shard_len, double* partials,
-                            const AmpState* st, hipStream_t stream) {
+                            const AmpState* st, float* stage, hipStream_t stream) {
   if (shard_len <= 0 || level1_partials(shard_len) > 0x7fffffff) return hipErrorInvalidValue;
-#define ZS_CALL_SUMSQ16(X) launch_sumsq_f16_m<X>(g, shard_len, partials, st, stream)
+#define ZS_CALL_SUMSQ16(X) launch_sumsq_f16_m<X>(g, shard_len, partials, st, stage, stream)
   ZS_DISPATCH_M(M, ZS_CALL_SUMSQ16)
 #undef ZS_CALL_SUMSQ16
 }
@@ -624,6 +697,23 @@ hipError_t launch_step_f16(int M, const GradPtrs& g, float* master, float* m, fl
   launch_step_f16_m<X>(g, master, m, v, param, shard_len, runs, n_runs, clip, k, lds, stream)
   ZS_DISPATCH_M(M, ZS_CALL_STEP16)
 #undef ZS_CALL_STEP16
+}
+
+hipError_t launch_step_staged(bool amp, const float* stage, float* master, float* m, float* v,
+                              uint16_t* param, int64_t shard_len, const Run* runs, int32_t n_runs,
+                              const ClipScalars* clip, const StepConsts& kh, const StepConsts* kd,
+                              int32_t waves_per_cu, hipStream_t stream) {
+  if (shard_len <= 0) return hipSuccess;
+  if ((shard_len + kTile - 1) / kTile > 0x7fffffff || n_runs < 1) return hipErrorInvalidValue;
+  const size_t lds = waves_per_cu > 0 ? (kLdsPerCu / (size_t)waves_per_cu) & ~(size_t)255 : 0;
+  const dim3 grid((unsigned)((shard_len + kTile - 1) / kTile)), block(kStepLanes);
+  if (amp)
+    hipLaunchKernelGGL((step_staged_kernel<true>), grid, block, lds, stream, stage, master, m, v,
+                       param, shard_len, runs, n_runs, clip, kh, kd);
+  else
+    hipLaunchKernelGGL((step_staged_kernel<false>), grid, block, lds, stream, stage, master, m, v,
+                       param, shard_len, runs, n_runs, clip, kh, kd);
+  return hipGetLastError();
 }
 
 hipError_t launch_amp_state_init(AmpState* st, float scale, hipStream_t stream) {

@@ -69,8 +69,12 @@ def test_init_and_step_argument_errors_before_any_device_call():
             zs.zero_shard_init(p, 4, 16, 16, 16, 16, 128, ws)        # workspace alignment
         with pytest.raises(zs.ZeroShardError):
             zs.zero_shard_init(p, 4, 16, 16, 16, 16, 256, ws - 1)    # workspace size
-        with pytest.raises(zs.ZeroShardError):
-            zs.zero_shard_init(p, 4, 16, 16, 16, 16, 256, ws, flags=2)
+        with pytest.raises(zs.ZeroShardError) as e:
+            zs.zero_shard_init(p, 4, 16, 16, 16, 16, 256, ws, flags=0x80)   # unknown flag
+        assert e.value.code == zs.ZS_EINVAL and "flag" in str(e.value)
+        with pytest.raises(zs.ZeroShardError) as e:   # staging needs the larger workspace
+            zs.zero_shard_init(p, 4, 16, 16, 16, 16, 256, ws, flags=zs.ZS_STAGE_AVERAGE)
+        assert e.value.code == zs.ZS_EINVAL and "workspace" in str(e.value)
         with pytest.raises(zs.ZeroShardError):
             zs.zero_shard_step(0, [16] * 4, 1e-3, 0.9, 0.95, 1e-8, 0.1, 1)
     finally:
@@ -83,5 +87,17 @@ def test_empty_plan():
     try:
         q = zs.zs_plan_query(p)
         assert q == dict(shard_len=0, n_segments=0, n_runs=0, padded_total=0, n_buckets=0)
+    finally:
+        zs.zs_plan_destroy(p)
+
+
+def test_workspace_grows_by_the_staging_area():
+    p = zs.zs_plan_create([1000, 77, 4097], [1, 0, 1], 3, 2)
+    try:
+        S = zs.zs_plan_query(p)["shard_len"]
+        base = zs.zs_workspace_bytes(p, 4)
+        staged = zs.zs_workspace_bytes(p, 4, zs.ZS_STAGE_AVERAGE)
+        assert staged - base == (4 * S + 255) // 256 * 256
+        assert zs.zs_workspace_bytes(p, 4, zs.ZS_FP16 | zs.ZS_SKIP_NONFINITE) == base
     finally:
         zs.zs_plan_destroy(p)

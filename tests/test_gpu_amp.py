@@ -35,14 +35,15 @@ def _eq(a, b):
     return np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("stage", [False, True])
 @pytest.mark.parametrize("clip", [0.0, 2.0])
-def test_amp_sequence_matches_oracle(clip):
-    log(f"test_amp_sequence_matches_oracle clip={clip}")
+def test_amp_sequence_matches_oracle(clip, stage):
+    log(f"test_amp_sequence_matches_oracle clip={clip} stage={stage}")
     numel = [70_001, 64, 5, 130_000, 333]
     decay = [1, 0, 0, 1, 0]
     N, rank, M = 3, 1, 3
     lay = L.plan(numel, decay, N, rank, 25_000_000, 64)
-    z = ZeroShard(numel, decay, N, rank, M, fp16=True)
+    z = ZeroShard(numel, decay, N, rank, M, fp16=True, flags=zsm.ZS_STAGE_AVERAGE if stage else 0)
     S = z.shard_len
     pad = lay.padding_ranges()
     master = synth.host_normal_f32(S, synth.key(77, 0), 0.02)
