@@ -529,6 +529,14 @@ __global__ __launch_bounds__(kStepLanes) void step_staged_kernel(
   __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(param + e));
 }
 
+// The LDS reservation that caps a single-wave step kernel at waves_per_cu
+// resident waves per CU (0: no cap).  Caps below 3 would reserve more than a
+// workgroup may hold, so they mean no cap as well.
+size_t step_lds(int32_t waves_per_cu) {
+  if (waves_per_cu < 3) return 0;
+  return (kLdsPerCu / (size_t)waves_per_cu) & ~(size_t)255;
+}
+
 template <int M>
 hipError_t launch_sumsq_f16_m(const GradPtrs& g, int64_t shard_len, double* partials,
                               const AmpState* st, float* stage, hipStream_t stream) {
@@ -637,7 +645,7 @@ hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, f
                        int32_t waves_per_cu, hipStream_t stream) {
   if (shard_len <= 0) return hipSuccess;
   if ((shard_len + kTile - 1) / kTile > 0x7fffffff || n_runs < 1) return hipErrorInvalidValue;
-  const size_t lds = waves_per_cu > 0 ? (kLdsPerCu / (size_t)waves_per_cu) & ~(size_t)255 : 0;
+  const size_t lds = step_lds(waves_per_cu);
 #define ZS_CALL_STEP(X) \
   launch_step_m<X>(use_clip, g, master, m, v, param, shard_len, runs, n_runs, clip, k, lds, stream)
   ZS_DISPATCH_M(M, ZS_CALL_STEP)
@@ -692,7 +700,7 @@ hipError_t launch_step_f16(int M, const GradPtrs& g, float* master, float* m, fl
                            hipStream_t stream) {
   if (shard_len <= 0) return hipSuccess;
   if ((shard_len + kTile - 1) / kTile > 0x7fffffff || n_runs < 1) return hipErrorInvalidValue;
-  const size_t lds = waves_per_cu > 0 ? (kLdsPerCu / (size_t)waves_per_cu) & ~(size_t)255 : 0;
+  const size_t lds = step_lds(waves_per_cu);
 #define ZS_CALL_STEP16(X) \
   launch_step_f16_m<X>(g, master, m, v, param, shard_len, runs, n_runs, clip, k, lds, stream)
   ZS_DISPATCH_M(M, ZS_CALL_STEP16)
@@ -705,7 +713,7 @@ hipError_t launch_step_staged(bool amp, const float* stage, float* master, float
                               int32_t waves_per_cu, hipStream_t stream) {
   if (shard_len <= 0) return hipSuccess;
   if ((shard_len + kTile - 1) / kTile > 0x7fffffff || n_runs < 1) return hipErrorInvalidValue;
-  const size_t lds = waves_per_cu > 0 ? (kLdsPerCu / (size_t)waves_per_cu) & ~(size_t)255 : 0;
+  const size_t lds = step_lds(waves_per_cu);
   const dim3 grid((unsigned)((shard_len + kTile - 1) / kTile)), block(kStepLanes);
   if (amp)
     hipLaunchKernelGGL((step_staged_kernel<true>), grid, block, lds, stream, stage, master, m, v,
