@@ -254,6 +254,73 @@ int zero_shard_step_amp(zs_ctx *ctx, const void *const *grads, float lr, float b
                         zs_amp_state *state_dev, float growth_factor, float backoff_factor,
                         int32_t growth_interval, double *grad_norm_out);
 
+/* ------------------------------------------- the step on host cores (offload) */
+
+/*
+ * Optimizer offload: the fp32 master, exp_avg and exp_avg_sq of the shard live
+ * in host memory and host cores run the Adam step, so the GPU keeps only the
+ * 16-bit params and gradients; the reduced gradient goes down and the params
+ * come back over PCIe (大模型基础设施工程 06: §3.3 and §9.3 on ZeRO-Offload,
+ * the optimizer offload to pinned CPU memory in the DeepSpeed configuration of
+ * §11.3, FAQ Q5 on its throughput).  The arithmetic is the step's, operation
+ * for operation, so results equal zero_shard_step's bit for bit.
+ *
+ * zs_host_adamw: the update alone, on host arrays of n elements holding shard
+ *   elements [shard_off, shard_off + n) of the plan's shard: grad_avg is the
+ *   averaged (M-way reduced) fp32 gradient, coef the clip coefficient (1 for
+ *   none); master, exp_avg, exp_avg_sq are read and written, param_bf16
+ *   receives bf16_rne(master).  Decay flags come from the plan.  n_threads host
+ *   threads (0: every CPU this process may run on) are started for the call.
+ *   Synchronous.  Errors: ZS_EINVAL, ZS_ENOMEM.
+ */
+int zs_host_adamw(const zs_plan *plan, int64_t shard_off, int64_t n, const float *grad_avg,
+                  float coef, float *master, float *exp_avg, float *exp_avg_sq,
+                  uint16_t *param_bf16, float lr, float beta1, float beta2, float eps,
+                  float weight_decay, int64_t step, int32_t n_threads);
+
+typedef struct zs_offload zs_offload;
+
+/* Pinned host staging a context needs for chunks of chunk_elems elements (a
+ * positive multiple of 64), in bytes; 0 for an invalid chunk size. */
+size_t zs_offload_staging_bytes(int64_t chunk_elems);
+
+/*
+ * Binds an offload context: param_bf16 is device memory (shard_len bf16, written
+ * by every step); master, exp_avg, exp_avg_sq are host memory (shard_len fp32
+ * each; the caller initialises them as for zero_shard_init); workspace is device
+ * memory of zs_workspace_bytes(plan, M, ZS_STAGE_AVERAGE) bytes, 256-byte
+ * aligned; staging is pinned host memory (allocated pinned, e.g. hipHostMalloc)
+ * of zs_offload_staging_bytes(chunk_elems) bytes, 256-byte aligned.  The
+ * caller owns all of it.  n_threads host threads (0: every CPU this process may
+ * run on) are started and kept until destroy; two copy streams at the default
+ * priority are created.  flags: ZS_SKIP_NONFINITE or 0.
+ * Errors: ZS_EINVAL, ZS_ENOMEM, ZS_EHIP.
+ */
+int zero_offload_init(zs_offload **out, const zs_plan *plan, int32_t M, void *param_bf16,
+                      float *master, float *exp_avg, float *exp_avg_sq, void *workspace,
+                      size_t workspace_bytes, void *staging, size_t staging_bytes,
+                      int64_t chunk_elems, int32_t n_threads, void *stream, uint32_t flags);
+
+/*
+ * One offloaded step, same arguments and results as zero_shard_step.  The norm
+ * pass runs on the context's stream after the caller's earlier work; the
+ * averages come to the host chunk by chunk while the host updates the previous
+ * chunk and the one before goes back as bf16.  Returns when the host state is
+ * updated; the param copies are still in flight, and later work on the
+ * context's stream waits for them.  The norm is always available, so
+ * grad_norm_out costs no extra wait.  On ZS_EHIP the host state may be
+ * partly updated.  Errors: ZS_EINVAL, ZS_EHIP.
+ */
+int zero_offload_step(zs_offload *ctx, const void *const *grads, float lr, float beta1,
+                      float beta2, float eps, float weight_decay, int64_t step,
+                      float max_grad_norm, double *grad_norm_out);
+
+/* Later offload steps enqueue their device work on `stream`. */
+int zero_offload_set_stream(zs_offload *ctx, void *stream);
+
+/* Waits for the context's copies, stops its threads and frees it. */
+void zero_offload_destroy(zs_offload *ctx);
+
 /* The bf16 parameter shard (the all-gather send buffer) and its length. */
 int zero_shard_params(zs_ctx *ctx, const void **param_bf16, int64_t *shard_len);
 

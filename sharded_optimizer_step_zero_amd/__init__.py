@@ -82,6 +82,15 @@ _sig("zero_shard_params", ctypes.c_int, _vp, _P(_vp), _P(_i64))
 _sig("zero_shard_set_stream", ctypes.c_int, _vp, _vp)
 _sig("zero_shard_destroy", None, _vp)
 _sig("zero_shard_last_error", ctypes.c_char_p)
+_sig("zs_host_adamw", ctypes.c_int, _vp, _i64, _i64, _vp, _f32, _vp, _vp, _vp, _vp, _f32, _f32,
+     _f32, _f32, _f32, _i64, _i32)
+_sig("zs_offload_staging_bytes", _sz, _i64)
+_sig("zero_offload_init", ctypes.c_int, _P(_vp), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
+     _sz, _i64, _i32, _vp, _u32)
+_sig("zero_offload_step", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _i64, _f32,
+     _P(_f64))
+_sig("zero_offload_set_stream", ctypes.c_int, _vp, _vp)
+_sig("zero_offload_destroy", None, _vp)
 
 EXPORTED = ["zs_plan_create", "zs_plan_query", "zs_plan_tensor_slice", "zs_plan_segment",
             "zs_plan_bucket", "zs_plan_run", "zs_plan_state_bytes", "zs_plan_destroy",
@@ -89,7 +98,9 @@ EXPORTED = ["zs_plan_create", "zs_plan_query", "zs_plan_tensor_slice", "zs_plan_
             "zero_shard_step_global_norm", "zero_shard_amp_state_init", "zero_shard_step_amp",
             "zero_shard_export_state", "zero_shard_import_state",
             "zero_shard_params", "zero_shard_set_stream",
-            "zero_shard_destroy", "zero_shard_last_error"]
+            "zero_shard_destroy", "zero_shard_last_error", "zs_host_adamw",
+            "zs_offload_staging_bytes", "zero_offload_init", "zero_offload_step",
+            "zero_offload_set_stream", "zero_offload_destroy"]
 
 
 class ZeroShardError(RuntimeError):
@@ -266,6 +277,55 @@ def zero_shard_destroy(ctx: int) -> None:
     _lib.zero_shard_destroy(ctx)
 
 
+# ------------------------------------------------- the step on host cores
+
+
+def zs_host_adamw(plan: int, shard_off: int, n: int, grad_avg: int, coef: float, master: int,
+                  exp_avg: int, exp_avg_sq: int, param_bf16: int, lr: float, beta1: float,
+                  beta2: float, eps: float, weight_decay: float, step: int,
+                  n_threads: int = 0) -> None:
+    """The update alone on host arrays (addresses of n-element host arrays)."""
+    _check(_lib.zs_host_adamw(plan, shard_off, n, grad_avg or None, coef, master or None,
+                              exp_avg or None, exp_avg_sq or None, param_bf16 or None, lr,
+                              beta1, beta2, eps, weight_decay, step, n_threads))
+
+
+def zs_offload_staging_bytes(chunk_elems: int) -> int:
+    return int(_lib.zs_offload_staging_bytes(chunk_elems))
+
+
+def zero_offload_init(plan: int, M: int, param_bf16: int, master: int, exp_avg: int,
+                      exp_avg_sq: int, workspace: int, workspace_bytes: int, staging: int,
+                      staging_bytes: int, chunk_elems: int, n_threads: int = 0, stream: int = 0,
+                      flags: int = 0) -> int:
+    out = ctypes.c_void_p()
+    _check(_lib.zero_offload_init(ctypes.byref(out), plan, M, param_bf16, master, exp_avg,
+                                  exp_avg_sq, workspace, workspace_bytes, staging, staging_bytes,
+                                  chunk_elems, n_threads, stream or None, flags))
+    return out.value
+
+
+def zero_offload_step(ctx: int, grads: Sequence[int], lr: float, beta1: float, beta2: float,
+                      eps: float, weight_decay: float, step: int, max_grad_norm: float = 0.0,
+                      want_norm: bool = False, return_code: bool = False):
+    """One offloaded step (returns once the host state is updated); results as
+    zero_shard_step's."""
+    nrm = ctypes.c_double()
+    rc = _check(_lib.zero_offload_step(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
+                                       weight_decay, step, max_grad_norm,
+                                       ctypes.byref(nrm) if want_norm else None))
+    norm = nrm.value if want_norm else None
+    return (rc, norm) if return_code else norm
+
+
+def zero_offload_set_stream(ctx: int, stream: int) -> None:
+    _check(_lib.zero_offload_set_stream(ctx, stream or None))
+
+
+def zero_offload_destroy(ctx: int) -> None:
+    _lib.zero_offload_destroy(ctx)
+
+
 # ----------------------------------------------------- convenience owner
 
 
@@ -350,6 +410,66 @@ class ZeroShard:
     def close(self):
         if getattr(self, "ctx", None):
             zero_shard_destroy(self.ctx)
+            self.ctx = None
+        if getattr(self, "plan", None):
+            zs_plan_destroy(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class ZeroOffload:
+    """One rank's shard with the optimizer state in host memory: plan, device
+    param and workspace, host master/m/v and pinned staging (all torch-allocated),
+    and the bound offload context."""
+
+    def __init__(self, numel, decay, world_size=1, rank=0, M=1, device=None, bucket_cap=25_000_000,
+                 align=64, flags=0, stream=None, chunk_elems=1 << 22, n_threads=0):
+        import torch
+        self.device = torch.device(device if device is not None else "cuda")
+        self.M = M
+        self.plan = zs_plan_create(numel, decay, world_size, rank, bucket_cap, align)
+        q = zs_plan_query(self.plan)
+        self.shard_len = S = q["shard_len"]
+        n = max(S, 8)
+        self.param = torch.zeros(n, dtype=torch.bfloat16, device=self.device)
+        self.master = torch.zeros(n, dtype=torch.float32)
+        self.exp_avg = torch.zeros(n, dtype=torch.float32)
+        self.exp_avg_sq = torch.zeros(n, dtype=torch.float32)
+        self.ws_bytes = zs_workspace_bytes(self.plan, M, ZS_STAGE_AVERAGE)
+        self.workspace = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
+        self.chunk = chunk_elems
+        self.staging_bytes = zs_offload_staging_bytes(chunk_elems)
+        self.staging = torch.empty(max(self.staging_bytes, 256), dtype=torch.uint8, pin_memory=True)
+        s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
+        self.ctx = zero_offload_init(self.plan, M, self.param.data_ptr(), self.master.data_ptr(),
+                                     self.exp_avg.data_ptr(), self.exp_avg_sq.data_ptr(),
+                                     self.workspace.data_ptr(), self.ws_bytes,
+                                     self.staging.data_ptr(), self.staging_bytes, chunk_elems,
+                                     n_threads, s, flags)
+
+    def set_stream(self, stream: int):
+        zero_offload_set_stream(self.ctx, stream)
+
+    def step(self, grads, *, lr, beta1, beta2, eps, weight_decay, step, max_grad_norm=0.0,
+             want_norm=False, return_code=False):
+        ptrs = [g if isinstance(g, int) else g.data_ptr() for g in grads]
+        if len(ptrs) != self.M:
+            raise ValueError(f"expected {self.M} gradient contributions")
+        return zero_offload_step(self.ctx, ptrs, lr, beta1, beta2, eps, weight_decay, step,
+                                 max_grad_norm, want_norm, return_code)
+
+    def segments(self):
+        n = zs_plan_query(self.plan)["n_segments"]
+        return [zs_plan_segment(self.plan, i) for i in range(n)]
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            zero_offload_destroy(self.ctx)
             self.ctx = None
         if getattr(self, "plan", None):
             zs_plan_destroy(self.plan)

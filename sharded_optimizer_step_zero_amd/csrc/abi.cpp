@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../include/zeroshard.h"
+#include "abi_internal.h"
 #include "internal.h"
 
 namespace zs {
@@ -61,11 +62,47 @@ zs::WorkspaceLayout workspace_layout(int64_t n_runs, int64_t n_pieces, int64_t n
   return l;
 }
 
-zs::WorkspaceLayout plan_workspace(const zs_plan* plan, uint32_t flags) {
+}  // namespace
+
+// Helpers the other ABI translation unit (offload.cpp) shares; abi_internal.h.
+namespace zs {
+
+WorkspaceLayout plan_workspace(const zs_plan* plan, uint32_t flags) {
   return workspace_layout((int64_t)plan->runs.size(), (int64_t)plan->pieces.size(),
                           zs::sumsq_partials(plan->shard_len),
                           (flags & ZS_STAGE_AVERAGE) ? plan->shard_len : 0);
 }
+
+int einval(const char* msg) {
+  zs::set_error(msg);
+  return ZS_EINVAL;
+}
+
+int ehip(const char* where, hipError_t e) {
+  zs::set_error(std::string(where) + ": " + hipGetErrorString(e));
+  return ZS_EHIP;
+}
+
+int check_hparams(float lr, float beta1, float beta2, float eps, float wd, int64_t step) {
+  if (!(isfinite(lr) && isfinite(beta1) && isfinite(beta2) && isfinite(eps) && isfinite(wd)))
+    return einval("zero_shard_step: hyper-parameters must be finite");
+  if (lr < 0.0f) return einval("zero_shard_step: lr must be >= 0");
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return einval("zero_shard_step: beta1 and beta2 must lie in [0, 1)");
+  if (!(eps > 0.0f)) return einval("zero_shard_step: eps must be > 0");
+  if (wd < 0.0f) return einval("zero_shard_step: weight_decay must be >= 0");
+  if (step < 1) return einval("zero_shard_step: step is 1-based and must be >= 1");
+  return ZS_OK;
+}
+
+}  // namespace zs
+
+using zs::check_hparams;
+using zs::ehip;
+using zs::einval;
+using zs::plan_workspace;
+
+namespace {
 
 // Resident-wave cap of the step kernel per CU, measured on MI355X: fewer
 // contributions leave each wave less in flight, so more waves pay off.
@@ -80,15 +117,7 @@ int32_t default_waves_per_cu(int32_t M) {
   return 12;
 }
 
-int einval(const char* msg) {
-  zs::set_error(msg);
-  return ZS_EINVAL;
-}
 
-int ehip(const char* where, hipError_t e) {
-  zs::set_error(std::string(where) + ": " + hipGetErrorString(e));
-  return ZS_EHIP;
-}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -96,17 +125,6 @@ zs::StepConsts step_consts(float lr, float beta1, float beta2, float eps, float 
   return zs::step_consts(lr, beta1, beta2, eps, wd, t);
 }
 
-int check_hparams(float lr, float beta1, float beta2, float eps, float wd, int64_t step) {
-  if (!(isfinite(lr) && isfinite(beta1) && isfinite(beta2) && isfinite(eps) && isfinite(wd)))
-    return einval("zero_shard_step: hyper-parameters must be finite");
-  if (lr < 0.0f) return einval("zero_shard_step: lr must be >= 0");
-  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
-    return einval("zero_shard_step: beta1 and beta2 must lie in [0, 1)");
-  if (!(eps > 0.0f)) return einval("zero_shard_step: eps must be > 0");
-  if (wd < 0.0f) return einval("zero_shard_step: weight_decay must be >= 0");
-  if (step < 1) return einval("zero_shard_step: step is 1-based and must be >= 1");
-  return ZS_OK;
-}
 
 int gather_grads(const zs_ctx* ctx, const void* const* grads, zs::GradPtrs* out) {
   if (!grads) return einval("zero_shard_step: grads is NULL");

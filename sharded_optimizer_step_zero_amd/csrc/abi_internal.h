@@ -1,0 +1,24 @@
+// abi_internal.h -- helpers shared by the two C-ABI translation units (abi.cpp,
+// offload.cpp): workspace layout, error reporting, hyper-parameter checks.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "internal.h"
+
+namespace zs {
+
+// Workspace layout of a plan for these init flags (see zs_workspace_bytes).
+WorkspaceLayout plan_workspace(const zs_plan* plan, uint32_t flags);
+// The thread's last error message (zero_shard_last_error).
+void set_error(const std::string& msg);
+// Record the message as the thread's last error and return ZS_EINVAL / ZS_EHIP.
+int einval(const char* msg);
+int ehip(const char* where, hipError_t e);
+// ZS_OK or ZS_EINVAL for the AdamW hyper-parameters and the 1-based step.
+int check_hparams(float lr, float beta1, float beta2, float eps, float wd, int64_t step);
+
+}  // namespace zs

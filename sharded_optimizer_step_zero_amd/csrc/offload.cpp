@@ -1,0 +1,332 @@
+// offload.cpp -- the optimizer step on host cores with PCIe staging, and the
+// host update alone (see include/zeroshard.h, "optimizer step on host cores").
+//
+// One step: the device's norm pass reduces the M contributions and stages each
+// element's fp32 average in the workspace (and gives the norm and clip scalars);
+// the averages come to pinned host memory chunk by chunk on one copy stream,
+// host threads update the fp32 state in host memory, and each chunk's bf16
+// params go back on a second copy stream, so the two PCIe directions and the
+// host work overlap.  Two staging buffers per direction; the host waits only on
+// events of its own copies.
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <memory>
+#include <new>
+#include <string>
+#include <system_error>
+#include <vector>
+
+#include "../../include/zeroshard.h"
+#include "abi_internal.h"
+#include "host.h"
+#include "internal.h"
+
+namespace {
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Pinned staging: 256 bytes for the clip scalars, two fp32 gradient buffers and
+// two bf16 param buffers of chunk elements each.
+struct StagingLayout {
+  size_t g_off[2], p_off[2], total;
+};
+
+StagingLayout staging_layout(int64_t chunk) {
+  StagingLayout s{};
+  size_t off = 256;
+  for (int b = 0; b < 2; b++) {
+    s.g_off[b] = off;
+    off += round256((size_t)chunk * sizeof(float));
+  }
+  for (int b = 0; b < 2; b++) {
+    s.p_off[b] = off;
+    off += round256((size_t)chunk * sizeof(uint16_t));
+  }
+  s.total = off;
+  return s;
+}
+
+zs::HostConsts host_consts(const zs::StepConsts& k) {
+  zs::HostConsts h;
+  h.beta1 = k.beta1;
+  h.beta2 = k.beta2;
+  h.c1 = k.c1;
+  h.c2 = k.c2;
+  h.alpha = k.alpha;
+  h.bhat = k.bhat;
+  h.eps = k.eps;
+  h.decay_mul = k.decay_mul;
+  return h;
+}
+
+// The plan's runs followed by a sentinel at the shard length.
+std::vector<zs::HostRun> host_runs(const zs_plan* plan) {
+  std::vector<zs::HostRun> t;
+  t.reserve(plan->runs.size() + 2);
+  for (const zs::Run& r : plan->runs) t.push_back({r.start, r.flags, 0});
+  if (t.empty()) t.push_back({0, 0, 0});
+  t.push_back({plan->shard_len, 0, 0});
+  return t;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int enomem(const char* msg) {
+  zs::set_error(msg);
+  return ZS_ENOMEM;
+}
+
+}  // namespace
+
+struct zs_offload {
+  int32_t M = 0;
+  uint32_t flags = 0;
+  int64_t shard_len = 0, chunk = 0;
+  std::vector<zs::HostRun> runs;
+  uint16_t* param = nullptr;
+  float* master = nullptr;
+  float* m = nullptr;
+  float* v = nullptr;
+  char* ws = nullptr;
+  zs::WorkspaceLayout lay{};
+  char* staging = nullptr;
+  StagingLayout sl{};
+  hipStream_t stream = nullptr, d2h = nullptr, h2d = nullptr;
+  hipEvent_t ready = nullptr, scalars = nullptr, done = nullptr;
+  hipEvent_t g_ready[2] = {nullptr, nullptr}, p_sent[2] = {nullptr, nullptr};
+  std::unique_ptr<zs::HostPool> pool;
+
+  ~zs_offload() {
+    // teardown: nothing left to report an error to
+    if (d2h) (void)hipStreamSynchronize(d2h);
+    if (h2d) (void)hipStreamSynchronize(h2d);
+    for (hipEvent_t e : {ready, scalars, done, g_ready[0], g_ready[1], p_sent[0], p_sent[1]})
+      if (e) (void)hipEventDestroy(e);
+    if (d2h) (void)hipStreamDestroy(d2h);
+    if (h2d) (void)hipStreamDestroy(h2d);
+  }
+};
+
+extern "C" size_t zs_offload_staging_bytes(int64_t chunk_elems) {
+  if (chunk_elems < 64 || chunk_elems % 64) return 0;
+  return staging_layout(chunk_elems).total;
+}
+
+extern "C" int zero_offload_init(zs_offload** out, const zs_plan* plan, int32_t M, void* param_bf16,
+                                 float* master, float* exp_avg, float* exp_avg_sq, void* workspace,
+                                 size_t workspace_bytes, void* staging, size_t staging_bytes,
+                                 int64_t chunk_elems, int32_t n_threads, void* stream,
+                                 uint32_t flags) {
+  using zs::einval;
+  if (!out) return einval("zero_offload_init: out is NULL");
+  *out = nullptr;
+  if (!plan) return einval("zero_offload_init: plan is NULL");
+  if (M < 1 || M > ZS_MAX_M) return einval("zero_offload_init: M must lie in [1, 16]");
+  if (flags & ~(ZS_SKIP_NONFINITE | ZS_STAGE_AVERAGE))
+    return einval("zero_offload_init: flags may hold only ZS_SKIP_NONFINITE (staging is implied)");
+  if (chunk_elems < 64 || chunk_elems % 64)
+    return einval("zero_offload_init: chunk_elems must be a positive multiple of 64");
+  if (n_threads < 0 || n_threads > 1024)
+    return einval("zero_offload_init: n_threads must lie in [0, 1024]");
+  if (!param_bf16 || !master || !exp_avg || !exp_avg_sq || !workspace || !staging)
+    return einval("zero_offload_init: NULL buffer");
+  if (!aligned(param_bf16, 16) || !aligned(master, 16) || !aligned(exp_avg, 16) ||
+      !aligned(exp_avg_sq, 16))
+    return einval("zero_offload_init: buffers must be 16-byte aligned");
+  if (!aligned(workspace, 256) || !aligned(staging, 256))
+    return einval("zero_offload_init: workspace and staging must be 256-byte aligned");
+  const zs::WorkspaceLayout lay = zs::plan_workspace(plan, flags | ZS_STAGE_AVERAGE);
+  if (workspace_bytes < lay.total)
+    return einval("zero_offload_init: workspace smaller than "
+                  "zs_workspace_bytes(plan, M, ZS_STAGE_AVERAGE)");
+  const StagingLayout sl = staging_layout(chunk_elems);
+  if (staging_bytes < sl.total)
+    return einval("zero_offload_init: staging smaller than zs_offload_staging_bytes(chunk_elems)");
+
+  std::unique_ptr<zs_offload> c(new (std::nothrow) zs_offload);
+  if (!c) return enomem("zero_offload_init: out of host memory");
+  c->M = M;
+  c->flags = flags;
+  c->shard_len = plan->shard_len;
+  c->chunk = chunk_elems;
+  c->param = static_cast<uint16_t*>(param_bf16);
+  c->master = master;
+  c->m = exp_avg;
+  c->v = exp_avg_sq;
+  c->ws = static_cast<char*>(workspace);
+  c->lay = lay;
+  c->staging = static_cast<char*>(staging);
+  c->sl = sl;
+  c->stream = static_cast<hipStream_t>(stream);
+  try {
+    c->runs = host_runs(plan);
+    c->pool.reset(new zs::HostPool(n_threads > 0 ? n_threads : zs::default_host_threads()));
+  } catch (const std::bad_alloc&) {
+    return enomem("zero_offload_init: out of host memory");
+  } catch (const std::system_error&) {
+    return enomem("zero_offload_init: could not start the host threads");
+  }
+  // copy streams at the default priority; they order themselves against the
+  // caller's stream through events
+  hipError_t e = hipStreamCreateWithFlags(&c->d2h, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->h2d, hipStreamNonBlocking);
+  for (hipEvent_t* ev : {&c->ready, &c->scalars, &c->done, &c->g_ready[0], &c->g_ready[1],
+                         &c->p_sent[0], &c->p_sent[1]})
+    if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+  // both param buffers start out free: their events complete on an empty stream
+  for (int b = 0; b < 2 && e == hipSuccess; b++) e = hipEventRecord(c->p_sent[b], c->h2d);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->h2d);
+  if (e != hipSuccess) return zs::ehip("zero_offload_init: streams and events", e);
+  *out = c.release();
+  return ZS_OK;
+}
+
+namespace {
+
+// After a failed HIP call inside a step: let the copies already queued finish
+// (they target the staging buffers) before reporting.
+int fail(zs_offload* c, const char* where, hipError_t e) {
+  (void)hipStreamSynchronize(c->d2h);
+  (void)hipStreamSynchronize(c->h2d);
+  return zs::ehip(where, e);
+}
+
+}  // namespace
+
+extern "C" int zero_offload_step(zs_offload* c, const void* const* grads, float lr, float beta1,
+                                 float beta2, float eps, float weight_decay, int64_t step,
+                                 float max_grad_norm, double* grad_norm_out) {
+  using zs::einval;
+  if (!c) return einval("zero_offload_step: ctx is NULL");
+  int rc = zs::check_hparams(lr, beta1, beta2, eps, weight_decay, step);
+  if (rc) return rc;
+  if (isnan(max_grad_norm) || isinf(max_grad_norm))
+    return einval("zero_offload_step: max_grad_norm must be finite");
+  if (!grads) return einval("zero_offload_step: grads is NULL");
+  zs::GradPtrs g;
+  memset(&g, 0, sizeof g);
+  for (int j = 0; j < c->M; j++) {
+    if (!grads[j] || !aligned(grads[j], 16))
+      return einval("zero_offload_step: every grads[j] must be a non-NULL 16-byte-aligned pointer");
+    g.p[j] = static_cast<const uint16_t*>(grads[j]);
+  }
+  if (c->shard_len == 0) {
+    if (grad_norm_out) *grad_norm_out = 0.0;
+    return ZS_OK;
+  }
+  const int64_t S = c->shard_len;
+  const bool clip = max_grad_norm > 0.0f;
+  const zs::HostConsts k =
+      host_consts(zs::step_consts(lr, beta1, beta2, eps, weight_decay, step));
+  float* stage = reinterpret_cast<float*>(c->ws + c->lay.stage_off);
+  double* partials = reinterpret_cast<double*>(c->ws + c->lay.partials_off);
+  zs::ClipScalars* sc_dev = reinterpret_cast<zs::ClipScalars*>(c->ws + c->lay.scalars_off);
+  volatile zs::ClipScalars* sc_host = reinterpret_cast<zs::ClipScalars*>(c->staging);
+
+  // the device part: reduce, stage the averages, norm and clip scalars
+  hipError_t e = zs::launch_sumsq(c->M, g, S, partials, stage, c->stream);
+  if (e == hipSuccess)
+    e = zs::launch_finalize(partials + zs::level1_partials(S), zs::final_partials(S), nullptr,
+                            max_grad_norm, clip ? 1 : 0,
+                            (c->flags & ZS_SKIP_NONFINITE) ? 1 : 0, sc_dev, c->stream);
+  if (e != hipSuccess) return zs::ehip("zero_offload_step: norm pass", e);
+  // both copy streams start after everything the caller queued before this step
+  e = hipEventRecord(c->ready, c->stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(c->d2h, c->ready, 0);
+  if (e == hipSuccess) e = hipStreamWaitEvent(c->h2d, c->ready, 0);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync((void*)sc_host, sc_dev, sizeof(zs::ClipScalars), hipMemcpyDeviceToHost,
+                       c->d2h);
+  if (e == hipSuccess) e = hipEventRecord(c->scalars, c->d2h);
+  if (e != hipSuccess) return fail(c, "zero_offload_step: queueing the copies", e);
+
+  const int64_t n_chunks = (S + c->chunk - 1) / c->chunk;
+  auto gbuf = [&](int b) { return reinterpret_cast<float*>(c->staging + c->sl.g_off[b]); };
+  auto pbuf = [&](int b) { return reinterpret_cast<uint16_t*>(c->staging + c->sl.p_off[b]); };
+  auto fetch = [&](int64_t ci) {  // queue chunk ci's averages into gradient buffer ci % 2
+    const int64_t off = ci * c->chunk, len = std::min(c->chunk, S - off);
+    const int b = (int)(ci & 1);
+    hipError_t r = hipMemcpyAsync(gbuf(b), stage + off, (size_t)len * sizeof(float),
+                                  hipMemcpyDeviceToHost, c->d2h);
+    if (r == hipSuccess) r = hipEventRecord(c->g_ready[b], c->d2h);
+    return r;
+  };
+  for (int64_t ci = 0; ci < std::min<int64_t>(2, n_chunks) && e == hipSuccess; ci++) e = fetch(ci);
+  if (e == hipSuccess) e = hipEventSynchronize(c->scalars);
+  if (e != hipSuccess) return fail(c, "zero_offload_step: gradient copies", e);
+  const double norm = sc_host->norm;
+  const float coef = sc_host->coef;
+  const bool skip = sc_host->skip != 0;
+  if (grad_norm_out) *grad_norm_out = norm;
+  const int done_rc = (grad_norm_out && !isfinite(norm)) ? ZS_NONFINITE : ZS_OK;
+  if (skip) {  // non-finite norm with ZS_SKIP_NONFINITE: the state stays as it is
+    e = hipStreamSynchronize(c->d2h);
+    return e == hipSuccess ? done_rc : fail(c, "zero_offload_step: draining copies", e);
+  }
+
+  const int32_t n_runs = (int32_t)c->runs.size() - 1;
+  for (int64_t ci = 0; ci < n_chunks; ci++) {
+    const int64_t off = ci * c->chunk, len = std::min(c->chunk, S - off);
+    const int b = (int)(ci & 1);
+    e = hipEventSynchronize(c->g_ready[b]);           // this chunk's averages have landed
+    if (e == hipSuccess) e = hipEventSynchronize(c->p_sent[b]);  // param buffer b is free again
+    if (e != hipSuccess) return fail(c, "zero_offload_step: waiting for a copy", e);
+    zs::host_adamw(*c->pool, c->runs.data(), n_runs, off, len, gbuf(b), coef, c->master + off,
+                   c->m + off, c->v + off, pbuf(b), k);
+    if (ci + 2 < n_chunks) e = fetch(ci + 2);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(c->param + off, pbuf(b), (size_t)len * sizeof(uint16_t),
+                         hipMemcpyHostToDevice, c->h2d);
+    if (e == hipSuccess) e = hipEventRecord(c->p_sent[b], c->h2d);
+    if (e != hipSuccess) return fail(c, "zero_offload_step: param copies", e);
+  }
+  // later work on the caller's stream sees the new params
+  e = hipEventRecord(c->done, c->h2d);
+  if (e == hipSuccess) e = hipStreamWaitEvent(c->stream, c->done, 0);
+  if (e != hipSuccess) return fail(c, "zero_offload_step: ordering the caller's stream", e);
+  return done_rc;
+}
+
+extern "C" int zero_offload_set_stream(zs_offload* c, void* stream) {
+  if (!c) return zs::einval("zero_offload_set_stream: ctx is NULL");
+  c->stream = static_cast<hipStream_t>(stream);
+  return ZS_OK;
+}
+
+extern "C" void zero_offload_destroy(zs_offload* c) { delete c; }
+
+extern "C" int zs_host_adamw(const zs_plan* plan, int64_t shard_off, int64_t n,
+                             const float* grad_avg, float coef, float* master, float* exp_avg,
+                             float* exp_avg_sq, uint16_t* param_bf16, float lr, float beta1,
+                             float beta2, float eps, float weight_decay, int64_t step,
+                             int32_t n_threads) {
+  using zs::einval;
+  if (!plan) return einval("zs_host_adamw: plan is NULL");
+  int rc = zs::check_hparams(lr, beta1, beta2, eps, weight_decay, step);
+  if (rc) return rc;
+  if (shard_off < 0 || n < 0 || shard_off > plan->shard_len || n > plan->shard_len - shard_off)
+    return einval("zs_host_adamw: [shard_off, shard_off + n) must lie inside the shard");
+  if (!isfinite(coef)) return einval("zs_host_adamw: coef must be finite");
+  if (n_threads < 0 || n_threads > 1024)
+    return einval("zs_host_adamw: n_threads must lie in [0, 1024]");
+  if (n == 0) return ZS_OK;
+  if (!grad_avg || !master || !exp_avg || !exp_avg_sq || !param_bf16)
+    return einval("zs_host_adamw: NULL array");
+  const zs::HostConsts k =
+      host_consts(zs::step_consts(lr, beta1, beta2, eps, weight_decay, step));
+  try {
+    const std::vector<zs::HostRun> runs = host_runs(plan);
+    zs::HostPool pool(n_threads > 0 ? n_threads : zs::default_host_threads());
+    zs::host_adamw(pool, runs.data(), (int32_t)runs.size() - 1, shard_off, n, grad_avg, coef,
+                   master, exp_avg, exp_avg_sq, param_bf16, k);
+  } catch (const std::bad_alloc&) {
+    return enomem("zs_host_adamw: out of host memory");
+  } catch (const std::system_error&) {
+    return enomem("zs_host_adamw: could not start the host threads");
+  }
+  return ZS_OK;
+}

@@ -1,0 +1,136 @@
+"""GPU + host: the offloaded step (zero_offload_step) against the oracle, bit for
+bit -- host master/m/v and the bf16 params that come back to the device -- on
+multi-tensor layouts with many chunks and ragged tails, with clip, with a
+non-finite gradient under ZS_SKIP_NONFINITE, on the GPT-1.3B shard, and against
+the all-device step on the same inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sharded_optimizer_step_zero_amd as zsm
+from oracle import layout as L
+from sharded_optimizer_step_zero_amd import ZeroOffload, ZeroShard
+from synth.device_case import DeviceCase
+from synth.workloads import scaled, workload
+
+from _gpu import log, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(a):
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+class Off:
+    def __init__(self, w, chunk, flags=0, n_threads=0):
+        self.w = w
+        self.lay = L.plan(w.numel, w.decay, w.world_size, w.rank, w.bucket_cap, w.align)
+        self.z = ZeroOffload(w.numel, w.decay, w.world_size, w.rank, w.M, bucket_cap=w.bucket_cap,
+                             align=w.align, flags=flags, chunk_elems=chunk, n_threads=n_threads)
+        self.S = self.z.shard_len
+        assert self.S == self.lay.shard_len
+        self.case = DeviceCase(w, self.S, self.lay.padding_ranges(), self.z.device)
+        self.z.master[:self.S] = torch.from_numpy(self.case.host_master())
+
+    def hp(self):
+        w = self.w
+        return dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+
+    def state(self):
+        S = self.S
+        torch.cuda.synchronize()
+        return [self.z.master[:S].numpy().copy(), self.z.exp_avg[:S].numpy().copy(),
+                self.z.exp_avg_sq[:S].numpy().copy(), to_host(self.z.param)[:S].copy()]
+
+
+def _run_vs_oracle(w, steps, chunk, n_threads=0):
+    o = Off(w, chunk, n_threads=n_threads)
+    S = o.S
+    p, m, v, b = o.case.host_master(), np.zeros(S, np.float32), np.zeros(S, np.float32), \
+        np.zeros(S, np.uint16)
+    mask = o.lay.decay_mask()
+    for s in range(steps):
+        grads = o.case.fill_grads(s)
+        norm = o.z.step(grads, step=s + 1, max_grad_norm=w.max_grad_norm, want_norm=True,
+                        **o.hp())
+        g = o.case.host_grads(s)
+        want = float(np.sqrt(oracle.grad_sumsq(g)))
+        assert abs(norm - want) <= 1e-12 * max(want, 1e-300)
+        coef = oracle.coef_from_norm(norm, w.max_grad_norm) if w.max_grad_norm > 0 else None
+        oracle.step_f32(g, p, m, v, b, mask, step=s + 1, coef=coef, **o.hp())
+        for x, y in zip(o.state(), (p, m, v, b)):
+            assert np.array_equal(_bits(x), _bits(y)), s
+    o.z.close()
+
+
+CASES = [
+    # (numel, decay, N, rank, M, clip, chunk)
+    ([1, 63, 64, 65, 1000, 0, 4097, 12_345, 7, 300_001, 3], None, 3, 1, 3, 0.0, 4096),
+    ([5000] * 7 + [1], None, 8, 7, 8, 0.05, 64),
+    ([70_001, 64, 5, 2 ** 17 + 8], [1, 0, 0, 1], 1, 0, 5, 0.0, 1 << 20),
+    ([33_333] * 5, [0, 1, 0, 1, 0], 2, 0, 16, 1e-4, 12_288),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_offload_matches_oracle(case):
+    numel, decay, N, rank, M, clip, chunk = CASES[case]
+    w = scaled(workload(1), numel, decay, world_size=N, rank=rank, M=M, name=f"offload{case}")
+    w.max_grad_norm = clip
+    log(f"test_offload_matches_oracle[{case}]: tensors={len(numel)} N={N} M={M} clip={clip} "
+        f"chunk={chunk}")
+    _run_vs_oracle(w, 4, chunk, n_threads=[0, 1, 5, 16][case])
+
+
+def test_gpt13b_shard_offload():
+    w = workload(2)
+    log(f"test_gpt13b_shard_offload: {w.description}, 3 steps, chunk 4M")
+    _run_vs_oracle(w, 3, 1 << 22)
+
+
+def test_offload_equals_device_step_and_skips_nonfinite():
+    log("test_offload_equals_device_step_and_skips_nonfinite")
+    w = scaled(workload(1), [5000, 64, 130_001, 7], [1, 0, 1, 0], world_size=2, rank=1, M=4,
+               name="offload-vs-device")
+    o = Off(w, 8192, flags=zsm.ZS_SKIP_NONFINITE)
+    d = ZeroShard(w.numel, w.decay, 2, 1, 4, flags=zsm.ZS_SKIP_NONFINITE)
+    d.master.copy_(o.z.master.to(d.master.device))
+    for s in range(4):
+        grads = o.case.fill_grads(s)
+        if s == 2:
+            grads[3][999] = torch.tensor(float("inf"), dtype=torch.bfloat16)
+        ro = o.z.step(grads, step=s + 1, max_grad_norm=0.7, want_norm=True, return_code=True,
+                      **o.hp())
+        rd = d.step(grads, step=s + 1, max_grad_norm=0.7, want_norm=True, return_code=True,
+                    **o.hp())
+        assert ro[0] == rd[0] and (ro[1] == rd[1] or (np.isnan(ro[1]) and np.isnan(rd[1])))
+        if s == 2:
+            assert ro[0] == zsm.ZS_NONFINITE
+        got = o.state()
+        S = o.S
+        want = [to_host(x)[:S] for x in (d.master, d.exp_avg, d.exp_avg_sq, d.param)]
+        for x, y in zip(got, want):
+            assert np.array_equal(_bits(x), _bits(y)), s
+    d.close()
+    o.z.close()
+
+
+def test_params_visible_on_the_stream():
+    """Work queued on the context's stream after a step sees the new params
+    without any host synchronisation."""
+    log("test_params_visible_on_the_stream")
+    w = scaled(workload(1), [200_000], [1], world_size=1, rank=0, M=1, name="offload-stream")
+    o = Off(w, 1 << 14)
+    out = torch.empty_like(o.z.param)
+    for s in range(3):
+        grads = o.case.fill_grads(s)
+        o.z.step(grads, step=s + 1, **o.hp())
+        out.copy_(o.z.param)             # queued on the current stream right away
+    torch.cuda.synchronize()
+    b = to_host(o.z.param)
+    assert np.array_equal(to_host(out), b)
+    p = o.z.master[:o.S].numpy()
+    assert np.array_equal(b[:o.S], oracle.f32_to_bf16(p))
+    o.z.close()
