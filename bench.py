@@ -12,7 +12,7 @@ using the algorithmic bytes 2M+12 read + 14 written per parameter;
 `cpu_baseline` times the CPU oracle on a bounded slab of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload 1..5] [--no-cpu-baseline]
-                    [--checkpoint] [--amp]
+                    [--checkpoint] [--amp] [--offload] [--cold]
 """
 from __future__ import annotations
 
@@ -205,6 +205,96 @@ def time_amp(w, pad, dev, stream, steps: int, warmup: int, stage: bool = False,
                        + ("zs::step_staged_kernel<true>" if stage else "zs::step_f16_kernel")}
 
 
+def time_offload(w, pad, dev, stream, steps: int, warmup: int, chunk: int = 1 << 24) -> dict:
+    """The optimizer step on host cores (zero_offload_step) on the same shard:
+    device reduce + norm, the fp32 averages to pinned host memory (4 B/param),
+    the AdamW update of host fp32 state (30 B/param of host memory traffic), the
+    bf16 params back (2 B/param); chunks overlap.  Also times its parts: pinned
+    copies each way, the host update alone, and a host STREAM-add of 3 arrays,
+    so the figure can be read against the slowest of them."""
+    import numpy as np
+    import torch
+
+    import sharded_optimizer_step_zero_amd as zsm
+    from sharded_optimizer_step_zero_amd import ZeroOffload
+    from synth.device_case import DeviceCase
+
+    zo = ZeroOffload(w.numel, w.decay, w.world_size, w.rank, w.M, device=dev,
+                     bucket_cap=w.bucket_cap, align=w.align, chunk_elems=chunk)
+    zo.set_stream(stream.cuda_stream)
+    S = zo.shard_len
+    case = DeviceCase(w, S, pad, dev)
+    zo.master[:S] = torch.from_numpy(case.host_master())
+    grads = case.fill_grads(0)
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+              max_grad_norm=w.max_grad_norm)
+    for s in range(warmup):
+        zo.step(grads, step=s + 1, **hp)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        zo.step(grads, step=warmup + s + 1, **hp)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    # the host update alone, over the whole shard
+    g = np.full(S, 1e-4, np.float32)
+    p = zo.master[:S].numpy().copy()
+    m = np.zeros(S, np.float32)
+    v = np.zeros(S, np.float32)
+    b = np.zeros(S, np.uint16)
+    reps = 3
+    for t in range(reps + 1):           # the first pass also faults the pages in, untimed
+        if t == 1:
+            t0 = time.perf_counter()
+        zsm.zs_host_adamw(zo.plan, 0, S, g.ctypes.data, 1.0, p.ctypes.data, m.ctypes.data,
+                          v.ctypes.data, b.ctypes.data, lr=w.lr, beta1=w.beta1, beta2=w.beta2,
+                          eps=w.eps, weight_decay=w.weight_decay, step=t + 1)
+    host_s = (time.perf_counter() - t0) / reps
+    del g, p, m, v, b
+
+    # pinned copies of 1 GiB each way
+    n = 1 << 28
+    h = torch.empty(n, dtype=torch.float32, pin_memory=True)
+    d = torch.empty(n, dtype=torch.float32, device=dev)
+    bw = {}
+    for name, dst, src_ in (("d2h", h, d), ("h2d", d, h)):
+        dst.copy_(src_, non_blocking=True)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            dst.copy_(src_, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        bw[name] = 3 * 4 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del h, d
+
+    # host memory reference: c = a + b over 3 x 1 GiB with the intra-op threads
+    a = torch.ones(n)
+    b2 = torch.ones(n)
+    c = torch.empty(n)
+    torch.add(a, b2, out=c)
+    t0 = time.perf_counter()
+    for _ in range(3):
+        torch.add(a, b2, out=c)
+    stream_gbs = 3 * 3 * 4 * n / (time.perf_counter() - t0) / 1e9
+    del a, b2, c
+    zo.close()
+    del grads
+    return {"ms_per_step": ms, "params_per_s": S / (ms * 1e-3), "chunk_elems": chunk,
+            "pcie_bytes_per_param": {"d2h": 4, "h2d": 2},
+            "pcie_d2h_gbs": bw["d2h"], "pcie_h2d_gbs": bw["h2d"],
+            "host_update_params_per_s": S / host_s,
+            "host_update_gbs": 30 * S / host_s / 1e9,
+            "host_stream_add_gbs": stream_gbs,
+            "host_threads": len(os.sched_getaffinity(0)),
+            "stream_add_threads": torch.get_num_threads(),
+            "bound_params_per_s": min(bw["d2h"] * 1e9 / 4, bw["h2d"] * 1e9 / 2, S / host_s),
+            "note": "wall clock; the whole offloaded step incl. PCIe (never the headline value)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +311,10 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="also time steps with the Infinity Cache evicted (default for the tiny "
                          "workload)")
+    ap.add_argument("--offload", action="store_true",
+                    help="also time the optimizer step on host cores with PCIe staging")
+    ap.add_argument("--offload-chunk", type=int, default=1 << 24,
+                    help="elements per staged chunk of the offloaded step (multiple of 64)")
     ap.add_argument("--cpu-slab", type=int, default=1 << 25)
     ap.add_argument("--calibrate-copy-gib", type=float, default=1.0,
                     help="size of the plain copy run once before timing (counter calibration)")
@@ -354,6 +448,9 @@ def main():
     if args.amp:
         out["amp_fp16"] = time_amp(w, pad, dev, stream, args.steps, args.warmup)
         out["amp_fp16_staged"] = time_amp(w, pad, dev, stream, args.steps, args.warmup, True)
+    if args.offload:
+        out["offload"] = time_offload(w, pad, dev, stream, max(3, args.steps // 20), 2,
+                                      args.offload_chunk)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_slab, S))
     print(json.dumps(out), flush=True)

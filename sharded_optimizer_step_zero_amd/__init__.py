@@ -428,7 +428,7 @@ class ZeroOffload:
     and the bound offload context."""
 
     def __init__(self, numel, decay, world_size=1, rank=0, M=1, device=None, bucket_cap=25_000_000,
-                 align=64, flags=0, stream=None, chunk_elems=1 << 22, n_threads=0):
+                 align=64, flags=0, stream=None, chunk_elems=1 << 24, n_threads=0):
         import torch
         self.device = torch.device(device if device is not None else "cuda")
         self.M = M

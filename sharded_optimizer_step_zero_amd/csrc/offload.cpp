@@ -18,6 +18,7 @@
 #include <new>
 #include <string>
 #include <system_error>
+#include <utility>
 #include <vector>
 
 #include "../../include/zeroshard.h"
@@ -73,6 +74,31 @@ std::vector<zs::HostRun> host_runs(const zs_plan* plan) {
   return t;
 }
 
+// The pipeline's chunks (offset, length): they start at chunk/8 and double up to
+// chunk, and the tail is halved down again, so the host starts after a short
+// first copy and the last copy back is short too.  Lengths are multiples of 64
+// except the shard's own ragged end.
+std::vector<std::pair<int64_t, int64_t>> chunk_schedule(int64_t S, int64_t chunk) {
+  std::vector<std::pair<int64_t, int64_t>> out;
+  const int64_t small = std::max<int64_t>(64, chunk / 8 / 64 * 64);
+  int64_t off = 0, ramp = std::min(small, chunk);
+  while (off < S) {
+    const int64_t r = S - off;
+    int64_t len;
+    if (r <= small) {
+      len = r;
+    } else if (r <= 2 * chunk) {
+      len = std::max(small, (r / 2 + 63) / 64 * 64);  // halve the tail
+    } else {
+      len = ramp;
+      ramp = std::min(2 * ramp, chunk);  // stops at chunk: no overflow however many chunks
+    }
+    out.emplace_back(off, len);
+    off += len;
+  }
+  return out;
+}
+
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 int enomem(const char* msg) {
@@ -87,6 +113,7 @@ struct zs_offload {
   uint32_t flags = 0;
   int64_t shard_len = 0, chunk = 0;
   std::vector<zs::HostRun> runs;
+  std::vector<std::pair<int64_t, int64_t>> chunks;
   uint16_t* param = nullptr;
   float* master = nullptr;
   float* m = nullptr;
@@ -164,6 +191,7 @@ extern "C" int zero_offload_init(zs_offload** out, const zs_plan* plan, int32_t 
   c->stream = static_cast<hipStream_t>(stream);
   try {
     c->runs = host_runs(plan);
+    c->chunks = chunk_schedule(plan->shard_len, chunk_elems);
     c->pool.reset(new zs::HostPool(n_threads > 0 ? n_threads : zs::default_host_threads()));
   } catch (const std::bad_alloc&) {
     return enomem("zero_offload_init: out of host memory");
@@ -244,11 +272,11 @@ extern "C" int zero_offload_step(zs_offload* c, const void* const* grads, float 
   if (e == hipSuccess) e = hipEventRecord(c->scalars, c->d2h);
   if (e != hipSuccess) return fail(c, "zero_offload_step: queueing the copies", e);
 
-  const int64_t n_chunks = (S + c->chunk - 1) / c->chunk;
+  const int64_t n_chunks = (int64_t)c->chunks.size();
   auto gbuf = [&](int b) { return reinterpret_cast<float*>(c->staging + c->sl.g_off[b]); };
   auto pbuf = [&](int b) { return reinterpret_cast<uint16_t*>(c->staging + c->sl.p_off[b]); };
   auto fetch = [&](int64_t ci) {  // queue chunk ci's averages into gradient buffer ci % 2
-    const int64_t off = ci * c->chunk, len = std::min(c->chunk, S - off);
+    const int64_t off = c->chunks[ci].first, len = c->chunks[ci].second;
     const int b = (int)(ci & 1);
     hipError_t r = hipMemcpyAsync(gbuf(b), stage + off, (size_t)len * sizeof(float),
                                   hipMemcpyDeviceToHost, c->d2h);
@@ -270,7 +298,7 @@ extern "C" int zero_offload_step(zs_offload* c, const void* const* grads, float 
 
   const int32_t n_runs = (int32_t)c->runs.size() - 1;
   for (int64_t ci = 0; ci < n_chunks; ci++) {
-    const int64_t off = ci * c->chunk, len = std::min(c->chunk, S - off);
+    const int64_t off = c->chunks[ci].first, len = c->chunks[ci].second;
     const int b = (int)(ci & 1);
     e = hipEventSynchronize(c->g_ready[b]);           // this chunk's averages have landed
     if (e == hipSuccess) e = hipEventSynchronize(c->p_sent[b]);  // param buffer b is free again
