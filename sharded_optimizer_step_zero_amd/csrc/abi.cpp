@@ -6,6 +6,7 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
 #include <new>
 #include <string>
 #include <vector>
@@ -45,14 +46,16 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // The scalars block is 256 bytes: ClipScalars at 0, the device-computed
 // StepConsts at 64.  The staging area (ZS_STAGE_AVERAGE) comes last.
-zs::WorkspaceLayout workspace_layout(int64_t n_runs, int64_t n_pieces, int64_t n_partials,
-                                     int64_t stage_elems) {
+zs::WorkspaceLayout workspace_layout(int64_t shard_len, int64_t n_runs, int64_t n_pieces,
+                                     int64_t n_partials, int64_t stage_elems) {
   static_assert(sizeof(zs::ClipScalars) <= 64 && sizeof(zs::StepConsts) <= 192,
                 "scalars block overflow");
   zs::WorkspaceLayout l{};
   l.runs_off = 0;
   l.runs_bytes = (size_t)(n_runs + 1) * sizeof(zs::Run);
-  l.pieces_off = round256(l.runs_bytes);
+  l.tflags_off = round256(l.runs_bytes);
+  l.tflags_bytes = (size_t)zs::tile_flag_words(shard_len, n_runs) * sizeof(uint32_t);
+  l.pieces_off = l.tflags_off + round256(l.tflags_bytes);
   l.pieces_bytes = (size_t)n_pieces * sizeof(zs::Piece);
   l.partials_off = l.pieces_off + round256(l.pieces_bytes);
   l.scalars_off = l.partials_off + round256((size_t)n_partials * sizeof(double));
@@ -68,8 +71,8 @@ zs::WorkspaceLayout workspace_layout(int64_t n_runs, int64_t n_pieces, int64_t n
 namespace zs {
 
 WorkspaceLayout plan_workspace(const zs_plan* plan, uint32_t flags) {
-  return workspace_layout((int64_t)plan->runs.size(), (int64_t)plan->pieces.size(),
-                          zs::sumsq_partials(plan->shard_len),
+  return workspace_layout(plan->shard_len, (int64_t)plan->runs.size(),
+                          (int64_t)plan->pieces.size(), zs::sumsq_partials(plan->shard_len),
                           (flags & ZS_STAGE_AVERAGE) ? plan->shard_len : 0);
 }
 
@@ -152,8 +155,33 @@ double* partials(zs_ctx* ctx) { return reinterpret_cast<double*>(ctx->ws + ctx->
 const double* final_partials(zs_ctx* ctx) {
   return partials(ctx) + zs::level1_partials(ctx->shard_len);
 }
-const zs::Run* run_table(zs_ctx* ctx) {
-  return reinterpret_cast<const zs::Run*>(ctx->ws + ctx->lay.runs_off);
+zs::RunTable run_table(zs_ctx* ctx) {
+  zs::RunTable rt;
+  rt.runs = reinterpret_cast<const zs::Run*>(ctx->ws + ctx->lay.runs_off);
+  rt.tile_flags = ctx->lay.tflags_bytes
+                      ? reinterpret_cast<const uint32_t*>(ctx->ws + ctx->lay.tflags_off)
+                      : nullptr;
+  rt.n_runs = ctx->n_runs;
+  return rt;
+}
+
+// The tile-flag table of a run table (with its sentinel): per 256-element tile,
+// 2 bits -- the decay flag of a tile inside one run, or 2 for a tile that
+// straddles a run boundary.
+std::vector<uint32_t> tile_flags(const std::vector<zs::Run>& table, int64_t shard_len) {
+  const int64_t n_runs = (int64_t)table.size() - 1;
+  std::vector<uint32_t> w((size_t)zs::tile_flag_words(shard_len, n_runs), 0u);
+  if (w.empty()) return w;
+  const int64_t tiles = (shard_len + zs::kStepTileElems - 1) / zs::kStepTileElems;
+  size_t r = 0;  // the run holding the tile's first element
+  for (int64_t t = 0; t < tiles; t++) {
+    const int64_t lo = t * zs::kStepTileElems;
+    const int64_t hi = std::min(shard_len, lo + zs::kStepTileElems);
+    while (table[r + 1].start <= lo) r++;
+    const uint32_t f = table[r + 1].start < hi ? 2u : (uint32_t)(table[r].flags & 1);
+    w[(size_t)(t >> 4)] |= f << ((t & 15) * 2);
+  }
+  return w;
 }
 
 }  // namespace
@@ -185,10 +213,12 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   if (workspace_bytes < lay.total)
     return einval("zero_shard_init: workspace smaller than zs_workspace_bytes(plan, M, flags)");
   std::vector<zs::Run> table;
+  std::vector<uint32_t> tflags;
   try {
     table = plan->runs;
     if (table.empty()) table.push_back({0, 0, 0});
     table.push_back({plan->shard_len, 0, 0});  // sentinel: starts past every element
+    tflags = tile_flags(table, plan->shard_len);
   } catch (const std::bad_alloc&) {
     zs::set_error("zero_shard_init: out of host memory");
     return ZS_ENOMEM;
@@ -220,6 +250,9 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
     hipError_t e = hipMemcpyAsync(c->ws + lay.runs_off, table.data(),
                                   table.size() * sizeof(zs::Run), hipMemcpyHostToDevice,
                                   c->stream);
+    if (e == hipSuccess && lay.tflags_bytes)
+      e = hipMemcpyAsync(c->ws + lay.tflags_off, tflags.data(), lay.tflags_bytes,
+                         hipMemcpyHostToDevice, c->stream);
     if (e == hipSuccess && lay.pieces_bytes)
       e = hipMemcpyAsync(c->ws + lay.pieces_off, plan->pieces.data(), lay.pieces_bytes,
                          hipMemcpyHostToDevice, c->stream);
@@ -254,11 +287,11 @@ int enqueue_step(zs_ctx* ctx, const zs::GradPtrs& g, const zs::StepConsts& k, bo
   }
   if (stage)
     e = zs::launch_step_staged(false, stage, ctx->master, ctx->m, ctx->v, ctx->param,
-                               ctx->shard_len, run_table(ctx), ctx->n_runs, sc, k, nullptr,
+                               ctx->shard_len, run_table(ctx), sc, k, nullptr,
                                ctx->waves_per_cu_staged, ctx->stream);
   else
     e = zs::launch_step(ctx->M, need_norm, g, ctx->master, ctx->m, ctx->v, ctx->param,
-                        ctx->shard_len, run_table(ctx), ctx->n_runs, sc, k, ctx->waves_per_cu,
+                        ctx->shard_len, run_table(ctx), sc, k, ctx->waves_per_cu,
                         ctx->stream);
   if (e != hipSuccess) return ehip("zero_shard_step: step kernel", e);
   return ZS_OK;
@@ -420,12 +453,12 @@ extern "C" int zero_shard_step_amp(zs_ctx* ctx, const void* const* grads, float 
   if (e != hipSuccess) return ehip("zero_shard_step_amp: finalize", e);
   if (stage)
     e = zs::launch_step_staged(true, stage, ctx->master, ctx->m, ctx->v, ctx->param,
-                               ctx->shard_len, run_table(ctx), ctx->n_runs, scalars(ctx),
+                               ctx->shard_len, run_table(ctx), scalars(ctx),
                                zs::StepConsts{}, device_consts(ctx), ctx->waves_per_cu_staged,
                                ctx->stream);
   else
     e = zs::launch_step_f16(ctx->M, g, ctx->master, ctx->m, ctx->v, ctx->param, ctx->shard_len,
-                            run_table(ctx), ctx->n_runs, scalars(ctx), device_consts(ctx),
+                            run_table(ctx), scalars(ctx), device_consts(ctx),
                             ctx->waves_per_cu, ctx->stream);
   if (e != hipSuccess) return ehip("zero_shard_step_amp: step kernel", e);
   if (grad_norm_out) {

@@ -11,13 +11,34 @@ namespace zs {
 
 // A run of the shard with one weight-decay flag (padding joins a neighbouring
 // run; it is zero in every array and stays zero under either flag).  The step
-// kernel finds the run of each element by binary search over `start`.
+// kernels take a tile's flag from the tile-flag table (RunTable) and search the
+// runs by `start` only inside tiles that straddle a boundary.
 struct Run {
   int64_t start;  // shard offset, a multiple of 8 elements
   int32_t flags;  // bit 0: weight decay applies
   int32_t pad;
 };
 static_assert(sizeof(Run) == 16, "run descriptor is 16 bytes");
+
+// Elements per step-kernel tile (one single-wave workgroup each).
+constexpr int64_t kStepTileElems = 256;
+
+// The decay runs as the step kernels read them: the run table (n_runs entries
+// and a sentinel) and, when n_runs > 1, 2 bits per tile, 16 tiles per word:
+// bit 0 is the decay flag of a tile inside one run, bit 1 marks a tile that
+// straddles a run boundary (its lanes then look the run up themselves).
+struct RunTable {
+  const Run* runs;
+  const uint32_t* tile_flags;  // null when n_runs == 1
+  int32_t n_runs;
+};
+
+// Words of the tile-flag table of a shard (0 when there is one run).
+inline int64_t tile_flag_words(int64_t shard_len, int64_t n_runs) {
+  if (n_runs <= 1) return 0;
+  const int64_t tiles = (shard_len + kStepTileElems - 1) / kStepTileElems;
+  return (tiles + 15) / 16;
+}
 
 struct Segment {
   int64_t shard_off, len, tensor, tensor_off;
@@ -67,6 +88,7 @@ struct GradPtrs {
 // Device workspace layout (offsets in bytes from the workspace base).
 struct WorkspaceLayout {
   size_t runs_off, runs_bytes;  // n_runs + 1 Run entries (the last is a sentinel)
+  size_t tflags_off, tflags_bytes;  // tile_flag_words(shard_len, n_runs) words
   size_t pieces_off, pieces_bytes;  // n_pieces Piece entries
   size_t partials_off;          // sumsq_partials(shard_len) doubles
   size_t scalars_off;           // 256-byte block: ClipScalars, then StepConsts at +64
@@ -145,14 +167,14 @@ hipError_t launch_amp_finalize(const double* partials, int32_t n_partials, AmpSt
                                const AmpParams& p, ClipScalars* out, StepConsts* kout,
                                hipStream_t stream);
 hipError_t launch_step_f16(int M, const GradPtrs& g, float* master, float* m, float* v,
-                           uint16_t* param, int64_t shard_len, const Run* runs, int32_t n_runs,
+                           uint16_t* param, int64_t shard_len, const RunTable& rt,
                            const ClipScalars* clip, const StepConsts* k, int32_t waves_per_cu,
                            hipStream_t stream);
 hipError_t launch_amp_state_init(AmpState* st, float scale, hipStream_t stream);
 // The step on the averages a norm pass staged (amp: constants *kd and an fp16
 // param; otherwise kh and a bf16 param).
 hipError_t launch_step_staged(bool amp, const float* stage, float* master, float* m, float* v,
-                              uint16_t* param, int64_t shard_len, const Run* runs, int32_t n_runs,
+                              uint16_t* param, int64_t shard_len, const RunTable& rt,
                               const ClipScalars* clip, const StepConsts& kh, const StepConsts* kd,
                               int32_t waves_per_cu, hipStream_t stream);
 
@@ -165,9 +187,9 @@ hipError_t launch_state_copy(bool do_export, bool param_f16, const Piece* pieces
                              int64_t n_pieces, float* master, float* m, float* v, uint16_t* param,
                              float* c_master, float* c_m, float* c_v, hipStream_t stream);
 hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, float* m,
-                       float* v, uint16_t* param, int64_t shard_len, const Run* runs,
-                       int32_t n_runs, const ClipScalars* clip, const StepConsts& k,
-                       int32_t waves_per_cu, hipStream_t stream);
+                       float* v, uint16_t* param, int64_t shard_len, const RunTable& rt,
+                       const ClipScalars* clip, const StepConsts& k, int32_t waves_per_cu,
+                       hipStream_t stream);
 
 }  // namespace zs
 

@@ -142,6 +142,20 @@ __device__ __forceinline__ void store8(float* p, const float (&s)[8]) {
   __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p + 4));
 }
 
+// Decay flag (0 or 1) of element e of the tile starting at tile0 (tile index
+// blockIdx.x).  One uniform load of the tile's 2 bits; only a tile that
+// straddles a run boundary looks the run up per lane, from a uniform binary
+// search for the tile's first run (runs[n_runs] is a sentinel past the shard).
+__device__ __forceinline__ uint32_t decay_flag(const RunTable& rt, int64_t tile0, int64_t e) {
+  if (rt.n_runs == 1) return (uint32_t)rt.runs[0].flags & 1u;
+  const uint32_t t = blockIdx.x;
+  const uint32_t f = (rt.tile_flags[t >> 4] >> ((t & 15u) * 2u)) & 3u;
+  if (!(f & 2u)) return f;
+  int32_t r = find_run(rt.runs, rt.n_runs, tile0);
+  while (rt.runs[r + 1].start <= e) r++;
+  return (uint32_t)rt.runs[r].flags & 1u;
+}
+
 // LDS per CU on gfx950; reserving lds_cu / waves_per_cu bytes per single-wave
 // workgroup lets at most waves_per_cu of them reside on a CU.
 constexpr size_t kLdsPerCu = 160 * 1024;
@@ -149,14 +163,15 @@ constexpr size_t kLdsPerCu = 160 * 1024;
 constexpr int kStepLanes = 64;   // one wave64 per workgroup
 constexpr int kStepVec = 4;      // elements per lane
 constexpr int kTile = kStepLanes * kStepVec;
+static_assert(kTile == kStepTileElems, "tile-flag table and step tiles agree");
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int M, bool CLIP>
 __global__ __launch_bounds__(kStepLanes) void step_kernel(
     GradPtrs g, float* __restrict__ master, float* __restrict__ mom1, float* __restrict__ mom2,
-    uint16_t* __restrict__ param, int64_t n, const Run* __restrict__ runs, int32_t n_runs,
-    const ClipScalars* __restrict__ clip, StepConsts k) {
+    uint16_t* __restrict__ param, int64_t n, RunTable rt, const ClipScalars* __restrict__ clip,
+    StepConsts k) {
   const int64_t tile0 = (int64_t)blockIdx.x * kTile;
   const int64_t e = tile0 + (int64_t)threadIdx.x * kStepVec;
   if (e >= n) return;  // n is a multiple of 8: a lane's 4 elements are all in or all out
@@ -170,15 +185,8 @@ __global__ __launch_bounds__(kStepLanes) void step_kernel(
   f32x4 m4 = ld_stream(reinterpret_cast<const f32x4*>(mom1 + e));
   f32x4 v4 = ld_stream(reinterpret_cast<const f32x4*>(mom2 + e));
 
-  // the tile's decay flag (uniform search; per lane only where a run starts inside the tile)
-  int32_t r = 0;
-  if (n_runs > 1) {
-    r = find_run(runs, n_runs, tile0);
-    if (runs[r + 1].start < tile0 + kTile) {
-      while (runs[r + 1].start <= e) r++;  // runs[n_runs] is a sentinel past the shard
-    }
-  }
-  const float d = (runs[r].flags & 1) ? k.decay_mul : 1.0f;
+  // the tile's decay flag, issued after the vector loads
+  const float d = decay_flag(rt, tile0, e) ? k.decay_mul : 1.0f;
   float coef = 1.0f;
   if (CLIP) {
     if (clip->skip) return;  // uniform: the whole grid leaves the state untouched
@@ -418,8 +426,8 @@ __global__ __launch_bounds__(kThreads) void amp_finalize_kernel(
 template <int M>
 __global__ __launch_bounds__(kStepLanes) void step_f16_kernel(
     GradPtrs g, float* __restrict__ master, float* __restrict__ mom1, float* __restrict__ mom2,
-    uint16_t* __restrict__ param, int64_t n, const Run* __restrict__ runs, int32_t n_runs,
-    const ClipScalars* __restrict__ clip, const StepConsts* __restrict__ kp) {
+    uint16_t* __restrict__ param, int64_t n, RunTable rt, const ClipScalars* __restrict__ clip,
+    const StepConsts* __restrict__ kp) {
   const int64_t tile0 = (int64_t)blockIdx.x * kTile;
   const int64_t e = tile0 + (int64_t)threadIdx.x * kStepVec;
   if (e >= n) return;
@@ -429,17 +437,11 @@ __global__ __launch_bounds__(kStepLanes) void step_f16_kernel(
   f32x4 p4 = ld_stream(reinterpret_cast<const f32x4*>(master + e));
   f32x4 m4 = ld_stream(reinterpret_cast<const f32x4*>(mom1 + e));
   f32x4 v4 = ld_stream(reinterpret_cast<const f32x4*>(mom2 + e));
-  int32_t r = 0;
-  if (n_runs > 1) {
-    r = find_run(runs, n_runs, tile0);
-    if (runs[r + 1].start < tile0 + kTile) {
-      while (runs[r + 1].start <= e) r++;
-    }
-  }
+  const uint32_t dflag = decay_flag(rt, tile0, e);
   if (clip->skip) return;  // found-inf: uniform over the grid
   const StepConsts k = *kp;
   const float inv = clip->inv_scale, coef = clip->coef;
-  const float d = (runs[r].flags & 1) ? k.decay_mul : 1.0f;
+  const float d = dflag ? k.decay_mul : 1.0f;
   float s[kStepVec];
   s[0] = h2f(w[0].x); s[1] = h2f(w[0].x >> 16);
   s[2] = h2f(w[0].y); s[3] = h2f(w[0].y >> 16);
@@ -488,9 +490,8 @@ __global__ void amp_state_init_kernel(AmpState* st, float scale) {
 template <bool AMP>
 __global__ __launch_bounds__(kStepLanes) void step_staged_kernel(
     const float* __restrict__ stage, float* __restrict__ master, float* __restrict__ mom1,
-    float* __restrict__ mom2, uint16_t* __restrict__ param, int64_t n,
-    const Run* __restrict__ runs, int32_t n_runs, const ClipScalars* __restrict__ clip,
-    StepConsts kh, const StepConsts* __restrict__ kd) {
+    float* __restrict__ mom2, uint16_t* __restrict__ param, int64_t n, RunTable rt,
+    const ClipScalars* __restrict__ clip, StepConsts kh, const StepConsts* __restrict__ kd) {
   const int64_t tile0 = (int64_t)blockIdx.x * kTile;
   const int64_t e = tile0 + (int64_t)threadIdx.x * kStepVec;
   if (e >= n) return;
@@ -498,17 +499,11 @@ __global__ __launch_bounds__(kStepLanes) void step_staged_kernel(
   f32x4 p4 = ld_stream(reinterpret_cast<const f32x4*>(master + e));
   f32x4 m4 = ld_stream(reinterpret_cast<const f32x4*>(mom1 + e));
   f32x4 v4 = ld_stream(reinterpret_cast<const f32x4*>(mom2 + e));
-  int32_t r = 0;
-  if (n_runs > 1) {
-    r = find_run(runs, n_runs, tile0);
-    if (runs[r + 1].start < tile0 + kTile) {
-      while (runs[r + 1].start <= e) r++;
-    }
-  }
+  const uint32_t dflag = decay_flag(rt, tile0, e);
   if (clip->skip) return;  // uniform over the grid
   const StepConsts k = AMP ? *kd : kh;
   const float coef = clip->coef;  // 1 when the call does not clip
-  const float d = (runs[r].flags & 1) ? k.decay_mul : 1.0f;
+  const float d = dflag ? k.decay_mul : 1.0f;
   uint32_t b[kStepVec];
 #pragma unroll
   for (int q = 0; q < kStepVec; q++) {
@@ -557,28 +552,28 @@ hipError_t launch_sumsq_f16_m(const GradPtrs& g, int64_t shard_len, double* part
 
 template <int M>
 hipError_t launch_step_f16_m(const GradPtrs& g, float* master, float* m, float* v,
-                             uint16_t* param, int64_t n, const Run* runs, int32_t n_runs,
+                             uint16_t* param, int64_t n, const RunTable& rt,
                              const ClipScalars* clip, const StepConsts* k, size_t lds,
                              hipStream_t stream) {
   const int64_t tiles = (n + kTile - 1) / kTile;
   hipLaunchKernelGGL((step_f16_kernel<M>), dim3((unsigned)tiles), dim3(kStepLanes), lds, stream,
-                     g, master, m, v, param, n, runs, n_runs, clip, k);
+                     g, master, m, v, param, n, rt, clip, k);
   return hipGetLastError();
 }
 
 template <int M>
 hipError_t launch_step_m(bool use_clip, const GradPtrs& g, float* master, float* m, float* v,
-                         uint16_t* param, int64_t n, const Run* runs, int32_t n_runs,
+                         uint16_t* param, int64_t n, const RunTable& rt,
                          const ClipScalars* clip, const StepConsts& k, size_t lds,
                          hipStream_t stream) {
   const int64_t tiles = (n + kTile - 1) / kTile;
   const dim3 grid((unsigned)tiles), block(kStepLanes);
   if (use_clip)
     hipLaunchKernelGGL((step_kernel<M, true>), grid, block, lds, stream, g, master, m, v, param,
-                       n, runs, n_runs, clip, k);
+                       n, rt, clip, k);
   else
     hipLaunchKernelGGL((step_kernel<M, false>), grid, block, lds, stream, g, master, m, v, param,
-                       n, runs, n_runs, clip, k);
+                       n, rt, clip, k);
   return hipGetLastError();
 }
 
@@ -639,15 +634,22 @@ int32_t final_partials(int64_t shard_len) {
     default: return hipErrorInvalidValue; \
   }
 
+// A step launch must fit the grid limit and have its run data: a run table,
+// and the tile flags when there is more than one run.
+static bool step_args_ok(int64_t shard_len, const RunTable& rt) {
+  return (shard_len + kTile - 1) / kTile <= 0x7fffffff && rt.n_runs >= 1 && rt.runs &&
+         (rt.n_runs == 1 || rt.tile_flags);
+}
+
 hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, float* m,
-                       float* v, uint16_t* param, int64_t shard_len, const Run* runs,
-                       int32_t n_runs, const ClipScalars* clip, const StepConsts& k,
-                       int32_t waves_per_cu, hipStream_t stream) {
+                       float* v, uint16_t* param, int64_t shard_len, const RunTable& rt,
+                       const ClipScalars* clip, const StepConsts& k, int32_t waves_per_cu,
+                       hipStream_t stream) {
   if (shard_len <= 0) return hipSuccess;
-  if ((shard_len + kTile - 1) / kTile > 0x7fffffff || n_runs < 1) return hipErrorInvalidValue;
+  if (!step_args_ok(shard_len, rt)) return hipErrorInvalidValue;
   const size_t lds = step_lds(waves_per_cu);
 #define ZS_CALL_STEP(X) \
-  launch_step_m<X>(use_clip, g, master, m, v, param, shard_len, runs, n_runs, clip, k, lds, stream)
+  launch_step_m<X>(use_clip, g, master, m, v, param, shard_len, rt, clip, k, lds, stream)
   ZS_DISPATCH_M(M, ZS_CALL_STEP)
 #undef ZS_CALL_STEP
 }
@@ -695,32 +697,32 @@ hipError_t launch_amp_finalize(const double* partials, int32_t n_partials, AmpSt
 }
 
 hipError_t launch_step_f16(int M, const GradPtrs& g, float* master, float* m, float* v,
-                           uint16_t* param, int64_t shard_len, const Run* runs, int32_t n_runs,
+                           uint16_t* param, int64_t shard_len, const RunTable& rt,
                            const ClipScalars* clip, const StepConsts* k, int32_t waves_per_cu,
                            hipStream_t stream) {
   if (shard_len <= 0) return hipSuccess;
-  if ((shard_len + kTile - 1) / kTile > 0x7fffffff || n_runs < 1) return hipErrorInvalidValue;
+  if (!step_args_ok(shard_len, rt)) return hipErrorInvalidValue;
   const size_t lds = step_lds(waves_per_cu);
 #define ZS_CALL_STEP16(X) \
-  launch_step_f16_m<X>(g, master, m, v, param, shard_len, runs, n_runs, clip, k, lds, stream)
+  launch_step_f16_m<X>(g, master, m, v, param, shard_len, rt, clip, k, lds, stream)
   ZS_DISPATCH_M(M, ZS_CALL_STEP16)
 #undef ZS_CALL_STEP16
 }
 
 hipError_t launch_step_staged(bool amp, const float* stage, float* master, float* m, float* v,
-                              uint16_t* param, int64_t shard_len, const Run* runs, int32_t n_runs,
+                              uint16_t* param, int64_t shard_len, const RunTable& rt,
                               const ClipScalars* clip, const StepConsts& kh, const StepConsts* kd,
                               int32_t waves_per_cu, hipStream_t stream) {
   if (shard_len <= 0) return hipSuccess;
-  if ((shard_len + kTile - 1) / kTile > 0x7fffffff || n_runs < 1) return hipErrorInvalidValue;
+  if (!step_args_ok(shard_len, rt)) return hipErrorInvalidValue;
   const size_t lds = step_lds(waves_per_cu);
   const dim3 grid((unsigned)((shard_len + kTile - 1) / kTile)), block(kStepLanes);
   if (amp)
     hipLaunchKernelGGL((step_staged_kernel<true>), grid, block, lds, stream, stage, master, m, v,
-                       param, shard_len, runs, n_runs, clip, kh, kd);
+                       param, shard_len, rt, clip, kh, kd);
   else
     hipLaunchKernelGGL((step_staged_kernel<false>), grid, block, lds, stream, stage, master, m, v,
-                       param, shard_len, runs, n_runs, clip, kh, kd);
+                       param, shard_len, rt, clip, kh, kd);
   return hipGetLastError();
 }
 
