@@ -372,9 +372,12 @@ class ZeroShard:
                                max_grad_norm, want_norm, return_code)
 
     def amp_init(self, init_scale=65536.0):
-        """Allocate and initialise the device loss-scaler state {scale, 0, 0}."""
+        """(Re)initialise the device loss-scaler state to {scale, 0, 0}.  The 16-byte
+        buffer is allocated once and keeps its address, so graphs captured with it
+        stay valid."""
         import torch
-        self.amp_state = torch.zeros(2, dtype=torch.int64, device=self.device)
+        if self.amp_state is None:
+            self.amp_state = torch.zeros(2, dtype=torch.int64, device=self.device)
         zero_shard_amp_state_init(self.ctx, self.amp_state.data_ptr(), init_scale)
 
     def amp_read(self):
