@@ -31,11 +31,28 @@ METRIC = "fused reduce+AdamW shard step: params/s and HBM GB/s as % of MI355X pe
 PEAK_HBM_GBS = 8000.0
 
 
-def kernel_source_hash() -> str:
+def _code_only(text: str) -> str:
+    """Source text without // comments, trailing blanks and empty lines."""
+    out = []
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            out.append(code)
+    return "\n".join(out)
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the step kernel's code (comments ignored): counters taken on one
+    version of the code stay valid across comment edits, not across code edits."""
     h = hashlib.sha256()
     for f in ("kernels.hip", "internal.h"):
-        with open(os.path.join(ROOT, "sharded_optimizer_step_zero_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        path = os.path.join(ROOT, "sharded_optimizer_step_zero_amd", "csrc", f)
+        if read is None:
+            with open(path, encoding="utf-8") as fh:
+                text = fh.read()
+        else:
+            text = read(f)
+        h.update(_code_only(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -10,14 +10,18 @@
 // elements, one tile per single-wave workgroup, each lane owning 4 consecutive
 // elements (one 8-byte load per bf16 stream, one 16-byte load per fp32
 // stream; loads and stores non-temporal).  Small, short-lived workgroups
-// dispatched in order keep the waves
-// in flight on a compact window of every stream, and a cap of a few waves per
-// CU (set through an LDS reservation the kernel never touches) keeps the
-// outstanding requests near what HBM serves best; both beat a persistent
-// grid-stride loop, which spreads concurrent accesses over the whole array.
-// The tile's weight-decay flag comes from the plan's run table by a
-// wave-uniform (scalar-memory) binary search issued after the vector loads,
-// so it overlaps their latency.
+// dispatched in order keep the waves in flight on a compact window of every
+// stream, and a cap of a few waves per CU (set through an LDS reservation the
+// kernel never touches) keeps the outstanding requests near what HBM serves
+// best; both beat a persistent grid-stride loop, which spreads concurrent
+// accesses over the whole array.  The tile's weight-decay flag is one
+// wave-uniform load from a 2-bit-per-tile table, issued after the vector loads
+// so it overlaps their latency; only a tile that straddles a run boundary
+// looks its runs up per lane.
+//
+// Variants on the same design: the loss-scaled fp16 step (fp16 loads, unscale,
+// device-side skip and step constants, fp16 re-cast) and the staged step that
+// reads the fp32 average a norm pass stored instead of the M contributions.
 //
 // Arithmetic per element (each operation one fp32 rounding, the build uses
 // -ffp-contract=off and correctly rounded division and square root):
