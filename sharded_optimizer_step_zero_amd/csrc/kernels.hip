@@ -314,29 +314,84 @@ __global__ __launch_bounds__(kThreads) void sumsq_total_kernel(const double* __r
   if (threadIdx.x == 0) *out = t;
 }
 
-// State export/import: one workgroup per piece (at most 65536 elements), the
-// lanes striding over it; the canonical side has no alignment guarantee, so
-// accesses are 4 bytes wide (still coalesced 256 B per wave).
+// State export/import: kCopySplit short-lived workgroups per piece (a piece
+// holds at most 65536 elements), each over its 1024-element part, the lanes
+// striding over it.  A piece whose six (seven on import) addresses are
+// all 16-byte aligned -- every piece when tensor sizes are multiples of 4 --
+// moves 4 elements per lane with 16-byte accesses; any other piece, and a
+// piece's last len % 4 elements, take the 4-byte path (still coalesced, 256 B
+// per wave).  The choice is per piece, so uniform over the workgroup.
+constexpr int32_t kCopyPart = 1024;
+constexpr int32_t kCopySplit = (int32_t)(kPieceElems / kCopyPart);
+
+template <bool EXPORT, bool F16>
+__device__ __forceinline__ void copy_one(int64_t s, int64_t c, float* __restrict__ master,
+                                         float* __restrict__ mom1, float* __restrict__ mom2,
+                                         uint16_t* __restrict__ param, float* __restrict__ c_master,
+                                         float* __restrict__ c_m, float* __restrict__ c_v) {
+  if (EXPORT) {
+    c_master[c] = master[s];
+    c_m[c] = mom1[s];
+    c_v[c] = mom2[s];
+  } else {
+    const float p = c_master[c];
+    master[s] = p;
+    mom1[s] = c_m[c];
+    mom2[s] = c_v[c];
+    param[s] = (uint16_t)(F16 ? f2h(p) : to_bf16(p));
+  }
+}
+
+__device__ __forceinline__ bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
 template <bool EXPORT, bool F16>
 __global__ __launch_bounds__(kThreads) void state_copy_kernel(
     const Piece* __restrict__ pieces, float* __restrict__ master, float* __restrict__ mom1,
     float* __restrict__ mom2, uint16_t* __restrict__ param, float* __restrict__ c_master,
     float* __restrict__ c_m, float* __restrict__ c_v) {
-  const Piece pc = pieces[blockIdx.x];
-  for (int32_t i = threadIdx.x; i < pc.len; i += kThreads) {
-    const int64_t s = pc.shard_off + i, c = pc.canon_off + i;
-    if (EXPORT) {
-      c_master[c] = master[s];
-      c_m[c] = mom1[s];
-      c_v[c] = mom2[s];
-    } else {
-      const float p = c_master[c];
-      master[s] = p;
-      mom1[s] = c_m[c];
-      mom2[s] = c_v[c];
-      param[s] = (uint16_t)(F16 ? f2h(p) : to_bf16(p));
+  const Piece whole = pieces[blockIdx.x / kCopySplit];
+  const int32_t part = (int32_t)(blockIdx.x % kCopySplit) * kCopyPart;
+  if (part >= whole.len) return;
+  Piece pc = whole;
+  pc.shard_off += part;
+  pc.canon_off += part;
+  pc.len = min(kCopyPart, whole.len - part);
+  const int64_t s0 = pc.shard_off, c0 = pc.canon_off;
+  const bool vec = al16(master + s0) && al16(mom1 + s0) && al16(mom2 + s0) &&
+                   al16(c_master + c0) && al16(c_m + c0) && al16(c_v + c0) &&
+                   (EXPORT || ((uintptr_t)(param + s0) & 7u) == 0);
+  int32_t done = 0;
+  if (vec) {
+    const int32_t quads = pc.len >> 2;
+    for (int32_t q = threadIdx.x; q < quads; q += kThreads) {
+      const int64_t s = s0 + 4 * (int64_t)q, c = c0 + 4 * (int64_t)q;
+      if (EXPORT) {
+        const f32x4 a = ld_stream(reinterpret_cast<const f32x4*>(master + s));
+        const f32x4 b = ld_stream(reinterpret_cast<const f32x4*>(mom1 + s));
+        const f32x4 d = ld_stream(reinterpret_cast<const f32x4*>(mom2 + s));
+        __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(c_master + c));
+        __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(c_m + c));
+        __builtin_nontemporal_store(d, reinterpret_cast<f32x4*>(c_v + c));
+      } else {
+        const f32x4 p = ld_stream(reinterpret_cast<const f32x4*>(c_master + c));
+        const f32x4 a = ld_stream(reinterpret_cast<const f32x4*>(c_m + c));
+        const f32x4 d = ld_stream(reinterpret_cast<const f32x4*>(c_v + c));
+        __builtin_nontemporal_store(p, reinterpret_cast<f32x4*>(master + s));
+        __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(mom1 + s));
+        __builtin_nontemporal_store(d, reinterpret_cast<f32x4*>(mom2 + s));
+        uint32_t b[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) b[k] = F16 ? f2h(p[k]) : to_bf16(p[k]);
+        u32x2 pk;
+        pk.x = b[0] | (b[1] << 16);
+        pk.y = b[2] | (b[3] << 16);
+        __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(param + s));
+      }
     }
+    done = quads << 2;
   }
+  for (int32_t i = done + threadIdx.x; i < pc.len; i += kThreads)
+    copy_one<EXPORT, F16>(s0 + i, c0 + i, master, mom1, mom2, param, c_master, c_m, c_v);
 }
 
 // ------------------------------------------------- loss-scaled fp16 path
@@ -670,8 +725,8 @@ hipError_t launch_state_copy(bool do_export, bool param_f16, const Piece* pieces
                              int64_t n_pieces, float* master, float* m, float* v, uint16_t* param,
                              float* c_master, float* c_m, float* c_v, hipStream_t stream) {
   if (n_pieces <= 0) return hipSuccess;
-  if (n_pieces > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)n_pieces), block(kThreads);
+  if (n_pieces > 0x7fffffff / kCopySplit) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(n_pieces * kCopySplit)), block(kThreads);
   if (do_export)
     hipLaunchKernelGGL((state_copy_kernel<true, false>), grid, block, 0, stream, pieces, master, m,
                        v, param, c_master, c_m, c_v);
