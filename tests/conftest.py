@@ -28,4 +28,7 @@ def _libraries_built():
     if not _built("sharded_optimizer_step_zero_amd/libzeroshard.so"):
         import __graft_entry__
         __graft_entry__.build_product()
+    if not _built("tests/c_abi/abi_check"):
+        from c_abi import build as c_abi_build
+        c_abi_build.build()
     yield
