@@ -107,17 +107,23 @@ using zs::plan_workspace;
 
 namespace {
 
-// Resident-wave cap of the step kernel per CU, measured on MI355X: fewer
-// contributions leave each wave less in flight, so more waves pay off.
-// ZS_WAVES_PER_CU overrides it (0: no cap).
-int32_t default_waves_per_cu(int32_t M) {
+// Resident-wave cap of the step kernels per CU (0: no cap), by M and shard size.
+// Measured on MI355X: caps 7..14 swept for each M on 164M- and 1G-element
+// shards, two rounds on the same buffers (repeatable to 0.3%).  Fewer
+// contributions leave each wave less in flight, so more waves pay off; larger
+// shards favour slightly fewer.  M without a measurement takes its neighbour's
+// cap.  ZS_WAVES_PER_CU overrides the table.
+int32_t default_waves_per_cu(int32_t M, int64_t shard_len) {
   const char* env = getenv("ZS_WAVES_PER_CU");
   if (env && *env) {
     const long v = strtol(env, nullptr, 10);
     if (v == 0 || (v >= 3 && v <= 64)) return (int32_t)v;
   }
-  if (M >= 6) return 9;
-  return 12;
+  //                                   M: 0   1   2   3   4   5   6   7   8   9  10  11  12  13  14  15  16
+  static const int8_t kSmall[ZS_MAX_M + 1] = {0, 12, 12, 11, 11, 11, 11, 10, 10, 10, 10, 9, 9, 9, 8, 8, 8};
+  static const int8_t kLarge[ZS_MAX_M + 1] = {0, 11, 11, 11, 10, 10, 10, 9, 9, 9, 9, 9, 9, 8, 8, 7, 7};
+  if (M < 1 || M > ZS_MAX_M) return 0;
+  return shard_len <= (int64_t(1) << 28) ? kSmall[M] : kLarge[M];
 }
 
 
@@ -237,8 +243,9 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   c->n_runs = (int32_t)(table.size() - 1);
   c->n_pieces = (int64_t)plan->pieces.size();
   c->canon_len = plan->total_params;
-  c->waves_per_cu = default_waves_per_cu(M);
-  c->waves_per_cu_staged = default_waves_per_cu(2);  // 16 B of gradient per lane, like M = 2
+  c->waves_per_cu = default_waves_per_cu(M, plan->shard_len);
+  // the staged step reads 16 B of gradient per lane, as many bytes as M = 2
+  c->waves_per_cu_staged = default_waves_per_cu(2, plan->shard_len);
   c->param = static_cast<uint16_t*>(param_bf16);
   c->master = master;
   c->m = exp_avg;
