@@ -12,7 +12,12 @@ using the algorithmic bytes 2M+12 read + 14 written per parameter;
 `cpu_baseline` times the CPU oracle on a bounded slab of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload 1..5] [--no-cpu-baseline]
-                    [--checkpoint] [--amp] [--offload] [--cold]
+                    [--checkpoint] [--amp] [--offload] [--cold] [--no-extras]
+
+On the default workload the line also carries the checkpoint export/import, the
+loss-scaled fp16 step (fused and staged) and the offloaded step on host cores
+("checkpoint", "amp_fp16", "amp_fp16_staged", "offload"), each timed after the
+headline step; --no-extras leaves them out.
 """
 from __future__ import annotations
 
@@ -321,6 +326,9 @@ def main():
                     help="1 tiny, 2 GPT-1.3B 1/8 shard (default), 3 Llama-6.7B, "
                          "4 Llama-70B 1/16 shard, 5 stress with clip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline step: skip the checkpoint, loss-scaled and "
+                         "offload legs that the default run adds on the GPT shard")
     ap.add_argument("--checkpoint", action="store_true",
                     help="also time the state export/import used for checkpoints and resharding")
     ap.add_argument("--amp", action="store_true",
@@ -460,12 +468,14 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if args.checkpoint:
+    # the default run on the GPT shard adds the follow-on paths' legs
+    extras = not args.no_extras and args.workload == 2
+    if args.checkpoint or extras:
         out["checkpoint"] = time_checkpoint(zs, w, stream)
-    if args.amp:
+    if args.amp or extras:
         out["amp_fp16"] = time_amp(w, pad, dev, stream, args.steps, args.warmup)
         out["amp_fp16_staged"] = time_amp(w, pad, dev, stream, args.steps, args.warmup, True)
-    if args.offload:
+    if args.offload or extras:
         out["offload"] = time_offload(w, pad, dev, stream, max(3, args.steps // 20), 2,
                                       args.offload_chunk)
     if not args.no_cpu_baseline:
