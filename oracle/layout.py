@@ -7,7 +7,10 @@ The layout, written out plainly:
 1. Tensors are flattened in forward order into buckets.  Inside a bucket each
    tensor starts at the next multiple of `align` elements.  A bucket is closed
    when the next tensor would end beyond `bucket_cap` elements; a tensor larger
-   than the cap sits alone in its bucket.  (Gradient buckets: 大模型基础设施工程
+   than the cap sits alone in its bucket.  Only a bucket that holds elements is
+   closed, and only by a tensor that has elements (reading: a bucket holds
+   elements; otherwise leading empty tensors, or an empty tensor after an
+   oversize one, would leave a bucket with nothing in it).  (Gradient buckets: 大模型基础设施工程
    06, §6.1 on DDP buckets and §11.3 on reduce_bucket_size /
    contiguous_gradients; flattening into one contiguous buffer before cutting:
    Lecture04 notes, ZeRO-3 / FSDP section on the flattened parameter.)
@@ -141,7 +144,7 @@ def plan(numel, decay, world_size: int, rank: int, bucket_cap: int = 25_000_000,
     start, fill, cur = 0, 0, []
     for t, n in enumerate(numel):
         pos = _align_up(fill, align)
-        if cur and pos + n > bucket_cap:
+        if cur and fill > 0 and n > 0 and pos + n > bucket_cap:
             length = _align_up(fill, world_size * align)
             buckets.append((start, length))
             members.append(cur)

@@ -4,7 +4,9 @@
 //  1. Tensors are placed in forward order into buckets, each at the next
 //     multiple of `align` elements from its bucket's start; a bucket closes
 //     when the next tensor would end past `bucket_cap`; a larger tensor sits
-//     alone (gradient buckets: 大模型基础设施工程 06, §6.1; contiguous flat
+//     alone; a bucket closes only once it holds elements, and a tensor with
+//     no elements never closes one, so no bucket is left empty (gradient
+//     buckets: 大模型基础设施工程 06, §6.1; contiguous flat
 //     gradient buffers: same page, §11.3).
 //  2. A bucket's length is padded to a multiple of world_size * align, so
 //     its world_size slices are equal and aligned ("padded to the shard
@@ -112,7 +114,9 @@ extern "C" int zs_plan_create(const int64_t* numel, const uint8_t* decay, int64_
     bool open = false;
     for (int64_t t = 0; t < n_tensors; t++) {
       int64_t pos = align_up(fill, align);
-      if (open && pos + numel[t] > bucket_cap) {
+      // only a bucket that holds elements closes, and only for a tensor that has
+      // some: no bucket is ever left empty
+      if (open && fill > 0 && numel[t] > 0 && pos + numel[t] > bucket_cap) {
         int64_t len = align_up(fill, pad_to);
         p->bucket_off.push_back(start);
         p->bucket_len.push_back(len);

@@ -80,3 +80,18 @@ def test_random_lists(seed):
     cap = int(rng.choice([1000, 8192, 40_000]))
     for r in {0, N - 1, int(rng.integers(0, N))}:
         _compare(numel, decay, N, r, cap, align)
+
+
+@pytest.mark.parametrize("numel", [[5000, 0, 7000], [0, 0, 5000, 0, 0, 7000, 0], [300, 5000, 0, 0, 6000],
+                                   [0], [0, 0], [5000, 0]])
+def test_empty_tensors_leave_no_empty_bucket(numel):
+    """A tensor without elements joins the open bucket: with a cap below the
+    tensors, an empty tensor after an oversize one must not open a bucket that the
+    next tensor closes empty."""
+    decay = [1] * len(numel)
+    for N, r in ((1, 0), (4, 3)):
+        _compare(numel, decay, N, r, 4096, 64)
+        lay = L.plan(numel, decay, N, r, 4096, 64)
+        if sum(numel):
+            assert all(ln > 0 for _, ln in lay.buckets), lay.buckets
+        assert len(lay.buckets) == max(1, sum(1 for n in numel if n > 0)) or sum(numel) == 0
