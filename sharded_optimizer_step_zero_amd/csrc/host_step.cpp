@@ -21,7 +21,15 @@ namespace {
 // no flush-to-zero, no denormals-are-zero.
 constexpr unsigned kDefaultMxcsr = 0x1F80u;
 
-__attribute__((target_clones("avx512f", "avx2", "default"))) void adamw_span(
+// ZS_HOST_ONE_ISA builds one baseline version instead (for ThreadSanitizer
+// builds: the clones' load-time resolver runs before that runtime starts).
+#ifdef ZS_HOST_ONE_ISA
+#define ZS_ISA_CLONES
+#else
+#define ZS_ISA_CLONES __attribute__((target_clones("avx512f", "avx2", "default")))
+#endif
+
+ZS_ISA_CLONES void adamw_span(
     int64_t n, const float* __restrict g, float coef, float* __restrict p, float* __restrict m,
     float* __restrict v, uint16_t* __restrict out, float beta1, float beta2, float c1, float c2,
     float alpha, float bhat, float eps, float d) {
