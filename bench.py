@@ -122,6 +122,33 @@ def cpu_baseline(w, slab: int, min_seconds: float = 10.0) -> dict:
                       f"{threads} threads; then {steps1} steps on one thread, {el1:.1f} s"}
 
 
+def time_graph(zs, grads, w, hp, steps: int, step0: int) -> dict:
+    """The same steps captured once into a HIP graph (step numbers step0.. baked in)
+    and replayed: launch gaps disappear, which matters where a step is a few
+    microseconds.  The step queues kernels only, so it captures as it is."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        zs.set_stream(torch.cuda.current_stream().cuda_stream)
+        for s in range(steps):
+            zs.step(grads, step=step0 + s, max_grad_norm=w.max_grad_norm, **hp)
+    cur = torch.cuda.current_stream()
+    zs.set_stream(cur.cuda_stream)
+    g.replay()                                   # warm-up replay
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    g.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del g
+    return {"ms_per_step": ms, "params_per_s": zs.shard_len / (ms * 1e-3), "steps": steps}
+
+
 def time_checkpoint(zs, w, stream, reps: int = 10) -> dict:
     """Export and import of this rank's fp32 state to/from the canonical order:
     12 B read + 12 B written per shard parameter (import also writes the 2-byte
@@ -340,6 +367,9 @@ def main():
                     help="also time the optimizer step on host cores with PCIe staging")
     ap.add_argument("--offload-chunk", type=int, default=1 << 24,
                     help="elements per staged chunk of the offloaded step (multiple of 64)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the steps replayed from one HIP graph (default for the tiny "
+                         "workload, which is launch-bound)")
     ap.add_argument("--cpu-slab", type=int, default=1 << 25)
     ap.add_argument("--calibrate-copy-gib", type=float, default=1.0,
                     help="size of the plain copy run once before timing (counter calibration)")
@@ -468,6 +498,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.graph or w.name.startswith("tiny"):
+        out["graph"] = time_graph(zs, grads, w, hp, args.steps, args.warmup + args.steps + 1)
     # the default run on the GPT shard adds the follow-on paths' legs
     extras = not args.no_extras and args.workload == 2
     if args.checkpoint or extras:
