@@ -157,3 +157,32 @@ def test_rejected_arguments_leave_state_untouched(bad):
     for x, y in zip(_state(sh.zs), pre):
         assert np.array_equal(_bits(x), _bits(y))
     sh.close()
+
+
+def test_two_contexts_on_two_streams_concurrently():
+    """Contexts share no library state: two shards stepping at once on two streams
+    give the same bits as each stepping alone."""
+    log("test_two_contexts_on_two_streams_concurrently")
+    wa = _small(M=3)
+    wb = _small(numel=(70_001, 3, 4096), decay=(1, 0, 1), N=1, rank=0, M=5)
+    wa.max_grad_norm = 0.4
+    runs = {}
+    for concurrent in (False, True):
+        a, b = Shard(wa), Shard(wb)
+        sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+        a.zs.set_stream(sa.cuda_stream)
+        b.zs.set_stream(sb.cuda_stream)
+        ga = [[g.clone() for g in a.case.fill_grads(s)] for s in range(3)]
+        gb = [[g.clone() for g in b.case.fill_grads(s)] for s in range(3)]
+        torch.cuda.synchronize()
+        for s in range(3):
+            a.zs.step(ga[s], step=s + 1, max_grad_norm=0.4, **a.hp())
+            if not concurrent:
+                torch.cuda.synchronize()
+            b.zs.step(gb[s], step=s + 1, max_grad_norm=0.0, **b.hp())
+        torch.cuda.synchronize()
+        runs[concurrent] = (_state(a.zs), _state(b.zs))
+        a.close()
+        b.close()
+    for x, y in zip(runs[False][0] + runs[False][1], runs[True][0] + runs[True][1]):
+        assert np.array_equal(_bits(x), _bits(y))

@@ -134,3 +134,26 @@ def test_params_visible_on_the_stream():
     p = o.z.master[:o.S].numpy()
     assert np.array_equal(b[:o.S], oracle.f32_to_bf16(p))
     o.z.close()
+
+
+def test_offload_rejected_arguments_leave_state_untouched():
+    log("test_offload_rejected_arguments_leave_state_untouched")
+    w = scaled(workload(1), [5000, 64], [1, 0], world_size=1, rank=0, M=2, name="offload-args")
+    o = Off(w, 1024)
+    grads = o.case.fill_grads(0)
+    o.z.step(grads, step=1, **o.hp())
+    before = o.state()
+    hp = o.hp()
+    bad = [dict(step=0), dict(step=2, lr=-1.0), dict(step=2, beta1=1.0), dict(step=2, eps=0.0),
+           dict(step=2, max_grad_norm=float("inf"))]
+    for kw in bad:
+        args = dict(hp, max_grad_norm=0.0)
+        args.update(kw)
+        with pytest.raises(zsm.ZeroShardError) as e:
+            o.z.step(grads, **args)
+        assert e.value.code == zsm.ZS_EINVAL
+    with pytest.raises(zsm.ZeroShardError):     # a misaligned gradient pointer
+        o.z.step([grads[0].data_ptr() + 2, grads[1].data_ptr()], step=2, **hp)
+    for x, y in zip(o.state(), before):
+        assert np.array_equal(_bits(x), _bits(y))
+    o.z.close()
