@@ -16,7 +16,7 @@ using the algorithmic bytes 2M+12 read + 14 written per parameter;
 
 On the default workload the line also carries the checkpoint export/import, the
 loss-scaled fp16 step (fused and staged) and the offloaded step on host cores
-("checkpoint", "amp_fp16", "amp_fp16_staged", "offload"), each timed after the
+("checkpoint", "amp_fp16", "amp_fp16_staged", "offload", "offload_fp16"), each timed after the
 headline step; --no-extras leaves them out.
 """
 from __future__ import annotations
@@ -254,13 +254,16 @@ def time_amp(w, pad, dev, stream, steps: int, warmup: int, stage: bool = False,
                        + ("zs::step_staged_kernel<true>" if stage else "zs::step_f16_kernel")}
 
 
-def time_offload(w, pad, dev, stream, steps: int, warmup: int, chunk: int = 1 << 24) -> dict:
+def time_offload(w, pad, dev, stream, steps: int, warmup: int, chunk: int = 1 << 24,
+                 fp16: bool = False) -> dict:
     """The optimizer step on host cores (zero_offload_step) on the same shard:
     device reduce + norm, the fp32 averages to pinned host memory (4 B/param),
     the AdamW update of host fp32 state (30 B/param of host memory traffic), the
     bf16 params back (2 B/param); chunks overlap.  Also times its parts: pinned
     copies each way, the host update alone, and a host STREAM-add of 3 arrays,
-    so the figure can be read against the slowest of them."""
+    so the figure can be read against the slowest of them.  fp16: the loss-scaled
+    variant (zero_offload_step_amp: fp16 contributions at the initial scale, the
+    scaler decided on the device, fp16 param back)."""
     import numpy as np
     import torch
 
@@ -269,20 +272,36 @@ def time_offload(w, pad, dev, stream, steps: int, warmup: int, chunk: int = 1 <<
     from synth.device_case import DeviceCase
 
     zo = ZeroOffload(w.numel, w.decay, w.world_size, w.rank, w.M, device=dev,
-                     bucket_cap=w.bucket_cap, align=w.align, chunk_elems=chunk)
+                     bucket_cap=w.bucket_cap, align=w.align, chunk_elems=chunk, fp16=fp16)
     zo.set_stream(stream.cuda_stream)
     S = zo.shard_len
     case = DeviceCase(w, S, pad, dev)
     zo.master[:S] = torch.from_numpy(case.host_master())
-    grads = case.fill_grads(0)
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
               max_grad_norm=w.max_grad_norm)
+    if fp16:
+        import synth
+        grads = []
+        for k, _ in w.grad_keys(0):
+            g = torch.empty(max(S, 8), dtype=torch.float16, device=dev)
+            synth.dev_grad_f16(g[:S], k, w.sigma_grad, 2.0 ** 14)
+            synth.dev_zero_ranges(g, pad)
+            grads.append(g)
+        zo.amp_init(2.0 ** 14)
+
+        def one(step):
+            zo.step_amp(grads, **hp)
+    else:
+        grads = case.fill_grads(0)
+
+        def one(step):
+            zo.step(grads, step=step, **hp)
     for s in range(warmup):
-        zo.step(grads, step=s + 1, **hp)
+        one(s + 1)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
-        zo.step(grads, step=warmup + s + 1, **hp)
+        one(warmup + s + 1)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
 
@@ -298,7 +317,8 @@ def time_offload(w, pad, dev, stream, steps: int, warmup: int, chunk: int = 1 <<
             t0 = time.perf_counter()
         zsm.zs_host_adamw(zo.plan, 0, S, g.ctypes.data, 1.0, p.ctypes.data, m.ctypes.data,
                           v.ctypes.data, b.ctypes.data, lr=w.lr, beta1=w.beta1, beta2=w.beta2,
-                          eps=w.eps, weight_decay=w.weight_decay, step=t + 1)
+                          eps=w.eps, weight_decay=w.weight_decay, step=t + 1,
+                          flags=zsm.ZS_FP16 if fp16 else 0)
     host_s = (time.perf_counter() - t0) / reps
     del g, p, m, v, b
 
@@ -333,6 +353,7 @@ def time_offload(w, pad, dev, stream, steps: int, warmup: int, chunk: int = 1 <<
     zo.close()
     del grads
     return {"ms_per_step": ms, "params_per_s": S / (ms * 1e-3), "chunk_elems": chunk,
+            "param_dtype": "fp16 (loss-scaled)" if fp16 else "bf16",
             "pcie_bytes_per_param": {"d2h": 4, "h2d": 2},
             "pcie_d2h_gbs": bw["d2h"], "pcie_h2d_gbs": bw["h2d"],
             "host_update_params_per_s": S / host_s,
@@ -510,6 +531,8 @@ def main():
     if args.offload or extras:
         out["offload"] = time_offload(w, pad, dev, stream, max(3, args.steps // 20), 2,
                                       args.offload_chunk)
+        out["offload_fp16"] = time_offload(w, pad, dev, stream, max(3, args.steps // 20), 2,
+                                           args.offload_chunk, fp16=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_slab, S))
     print(json.dumps(out), flush=True)

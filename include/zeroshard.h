@@ -268,15 +268,16 @@ int zero_shard_step_amp(zs_ctx *ctx, const void *const *grads, float lr, float b
  * zs_host_adamw: the update alone, on host arrays of n elements holding shard
  *   elements [shard_off, shard_off + n) of the plan's shard: grad_avg is the
  *   averaged (M-way reduced) fp32 gradient, coef the clip coefficient (1 for
- *   none); master, exp_avg, exp_avg_sq are read and written, param_bf16
- *   receives bf16_rne(master).  Decay flags come from the plan.  n_threads host
- *   threads (0: every CPU this process may run on) are started for the call.
+ *   none); master, exp_avg, exp_avg_sq are read and written, param receives
+ *   bf16_rne(master), or fp16_rne(master) with flags = ZS_FP16 (flags: 0 or
+ *   ZS_FP16).  Decay flags come from the plan.  n_threads host threads (0:
+ *   every CPU this process may run on) are started for the call.
  *   Synchronous.  Errors: ZS_EINVAL, ZS_ENOMEM.
  */
 int zs_host_adamw(const zs_plan *plan, int64_t shard_off, int64_t n, const float *grad_avg,
-                  float coef, float *master, float *exp_avg, float *exp_avg_sq,
-                  uint16_t *param_bf16, float lr, float beta1, float beta2, float eps,
-                  float weight_decay, int64_t step, int32_t n_threads);
+                  float coef, float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param,
+                  float lr, float beta1, float beta2, float eps, float weight_decay,
+                  int64_t step, int32_t n_threads, uint32_t flags);
 
 typedef struct zs_offload zs_offload;
 
@@ -285,18 +286,20 @@ typedef struct zs_offload zs_offload;
 size_t zs_offload_staging_bytes(int64_t chunk_elems);
 
 /*
- * Binds an offload context: param_bf16 is device memory (shard_len bf16, written
- * by every step); master, exp_avg, exp_avg_sq are host memory (shard_len fp32
+ * Binds an offload context: param is device memory (shard_len bf16, or fp16
+ * with ZS_FP16; written by every step); master, exp_avg, exp_avg_sq are host
+ * memory (shard_len fp32
  * each; the caller initialises them as for zero_shard_init); workspace is device
  * memory of zs_workspace_bytes(plan, M, ZS_STAGE_AVERAGE) bytes, 256-byte
  * aligned; staging is pinned host memory (allocated pinned, e.g. hipHostMalloc)
  * of zs_offload_staging_bytes(chunk_elems) bytes, 256-byte aligned.  The
  * caller owns all of it.  n_threads host threads (0: every CPU this process may
  * run on) are started and kept until destroy; two copy streams at the default
- * priority are created.  flags: ZS_SKIP_NONFINITE or 0.
+ * priority are created.  flags: any of ZS_SKIP_NONFINITE, ZS_FP16 (fp16
+ * gradients and param: zero_offload_step_amp), or 0.
  * Errors: ZS_EINVAL, ZS_ENOMEM, ZS_EHIP.
  */
-int zero_offload_init(zs_offload **out, const zs_plan *plan, int32_t M, void *param_bf16,
+int zero_offload_init(zs_offload **out, const zs_plan *plan, int32_t M, void *param,
                       float *master, float *exp_avg, float *exp_avg_sq, void *workspace,
                       size_t workspace_bytes, void *staging, size_t staging_bytes,
                       int64_t chunk_elems, int32_t n_threads, void *stream, uint32_t flags);
@@ -309,11 +312,24 @@ int zero_offload_init(zs_offload **out, const zs_plan *plan, int32_t M, void *pa
  * updated; the param copies are still in flight, and later work on the
  * context's stream waits for them.  The norm is always available, so
  * grad_norm_out costs no extra wait.  On ZS_EHIP the host state may be
- * partly updated.  Errors: ZS_EINVAL, ZS_EHIP.
+ * partly updated.  Errors: ZS_EINVAL, ZS_ESTATE (a ZS_FP16 context), ZS_EHIP.
  */
 int zero_offload_step(zs_offload *ctx, const void *const *grads, float lr, float beta1,
                       float beta2, float eps, float weight_decay, int64_t step,
                       float max_grad_norm, double *grad_norm_out);
+
+/*
+ * The offloaded loss-scaled step (a context created with ZS_FP16): the scaler,
+ * found-inf, the clip coefficient and the step constants at t = applied + 1 are
+ * decided on the device exactly as in zero_shard_step_amp (same arguments, same
+ * zs_amp_state); the host updates its fp32 state with those constants and the
+ * fp16 param goes back.  A skipped step leaves the host state untouched.
+ * Errors: ZS_EINVAL, ZS_ESTATE (context without ZS_FP16), ZS_EHIP.
+ */
+int zero_offload_step_amp(zs_offload *ctx, const void *const *grads, float lr, float beta1,
+                          float beta2, float eps, float weight_decay, float max_grad_norm,
+                          zs_amp_state *state_dev, float growth_factor, float backoff_factor,
+                          int32_t growth_interval, double *grad_norm_out);
 
 /* Later offload steps enqueue their device work on `stream`. */
 int zero_offload_set_stream(zs_offload *ctx, void *stream);

@@ -83,12 +83,14 @@ _sig("zero_shard_set_stream", ctypes.c_int, _vp, _vp)
 _sig("zero_shard_destroy", None, _vp)
 _sig("zero_shard_last_error", ctypes.c_char_p)
 _sig("zs_host_adamw", ctypes.c_int, _vp, _i64, _i64, _vp, _f32, _vp, _vp, _vp, _vp, _f32, _f32,
-     _f32, _f32, _f32, _i64, _i32)
+     _f32, _f32, _f32, _i64, _i32, _u32)
 _sig("zs_offload_staging_bytes", _sz, _i64)
 _sig("zero_offload_init", ctypes.c_int, _P(_vp), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
      _sz, _i64, _i32, _vp, _u32)
 _sig("zero_offload_step", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _i64, _f32,
      _P(_f64))
+_sig("zero_offload_step_amp", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _f32, _vp,
+     _f32, _f32, _i32, _P(_f64))
 _sig("zero_offload_set_stream", ctypes.c_int, _vp, _vp)
 _sig("zero_offload_destroy", None, _vp)
 
@@ -100,7 +102,7 @@ EXPORTED = ["zs_plan_create", "zs_plan_query", "zs_plan_tensor_slice", "zs_plan_
             "zero_shard_params", "zero_shard_set_stream",
             "zero_shard_destroy", "zero_shard_last_error", "zs_host_adamw",
             "zs_offload_staging_bytes", "zero_offload_init", "zero_offload_step",
-            "zero_offload_set_stream", "zero_offload_destroy"]
+            "zero_offload_step_amp", "zero_offload_set_stream", "zero_offload_destroy"]
 
 
 class ZeroShardError(RuntimeError):
@@ -281,13 +283,14 @@ def zero_shard_destroy(ctx: int) -> None:
 
 
 def zs_host_adamw(plan: int, shard_off: int, n: int, grad_avg: int, coef: float, master: int,
-                  exp_avg: int, exp_avg_sq: int, param_bf16: int, lr: float, beta1: float,
+                  exp_avg: int, exp_avg_sq: int, param: int, lr: float, beta1: float,
                   beta2: float, eps: float, weight_decay: float, step: int,
-                  n_threads: int = 0) -> None:
-    """The update alone on host arrays (addresses of n-element host arrays)."""
+                  n_threads: int = 0, flags: int = 0) -> None:
+    """The update alone on host arrays (addresses of n-element host arrays); param
+    receives bf16, or fp16 with flags=ZS_FP16."""
     _check(_lib.zs_host_adamw(plan, shard_off, n, grad_avg or None, coef, master or None,
-                              exp_avg or None, exp_avg_sq or None, param_bf16 or None, lr,
-                              beta1, beta2, eps, weight_decay, step, n_threads))
+                              exp_avg or None, exp_avg_sq or None, param or None, lr,
+                              beta1, beta2, eps, weight_decay, step, n_threads, flags))
 
 
 def zs_offload_staging_bytes(chunk_elems: int) -> int:
@@ -314,6 +317,21 @@ def zero_offload_step(ctx: int, grads: Sequence[int], lr: float, beta1: float, b
     rc = _check(_lib.zero_offload_step(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
                                        weight_decay, step, max_grad_norm,
                                        ctypes.byref(nrm) if want_norm else None))
+    norm = nrm.value if want_norm else None
+    return (rc, norm) if return_code else norm
+
+
+def zero_offload_step_amp(ctx: int, grads: Sequence[int], lr: float, beta1: float, beta2: float,
+                          eps: float, weight_decay: float, max_grad_norm: float, state_dev: int,
+                          growth_factor: float = 2.0, backoff_factor: float = 0.5,
+                          growth_interval: int = 2000, want_norm: bool = False,
+                          return_code: bool = False):
+    """One offloaded loss-scaled step (see zeroshard.h); results as zero_shard_step_amp's."""
+    nrm = ctypes.c_double()
+    rc = _check(_lib.zero_offload_step_amp(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
+                                           weight_decay, max_grad_norm, state_dev, growth_factor,
+                                           backoff_factor, growth_interval,
+                                           ctypes.byref(nrm) if want_norm else None))
     norm = nrm.value if want_norm else None
     return (rc, norm) if return_code else norm
 
@@ -431,7 +449,7 @@ class ZeroOffload:
     and the bound offload context."""
 
     def __init__(self, numel, decay, world_size=1, rank=0, M=1, device=None, bucket_cap=25_000_000,
-                 align=64, flags=0, stream=None, chunk_elems=1 << 24, n_threads=0):
+                 align=64, flags=0, stream=None, chunk_elems=1 << 24, n_threads=0, fp16=False):
         import torch
         self.device = torch.device(device if device is not None else "cuda")
         self.M = M
@@ -439,7 +457,12 @@ class ZeroOffload:
         q = zs_plan_query(self.plan)
         self.shard_len = S = q["shard_len"]
         n = max(S, 8)
-        self.param = torch.zeros(n, dtype=torch.bfloat16, device=self.device)
+        self.fp16 = fp16
+        if fp16:
+            flags |= ZS_FP16
+        self.amp_state = None
+        self.param = torch.zeros(n, dtype=torch.float16 if fp16 else torch.bfloat16,
+                                 device=self.device)
         self.master = torch.zeros(n, dtype=torch.float32)
         self.exp_avg = torch.zeros(n, dtype=torch.float32)
         self.exp_avg_sq = torch.zeros(n, dtype=torch.float32)
@@ -465,6 +488,32 @@ class ZeroOffload:
             raise ValueError(f"expected {self.M} gradient contributions")
         return zero_offload_step(self.ctx, ptrs, lr, beta1, beta2, eps, weight_decay, step,
                                  max_grad_norm, want_norm, return_code)
+
+    def amp_init(self, init_scale=65536.0):
+        """(Re)initialise the device loss-scaler state (a stable 16-byte buffer);
+        the device-side initialiser runs on the context's device work stream."""
+        import torch
+        if self.amp_state is None:
+            self.amp_state = torch.zeros(2, dtype=torch.int64, device=self.device)
+        raw = self.amp_state.view(torch.float32)
+        raw.zero_()
+        raw[0] = float(init_scale)
+
+    def amp_read(self):
+        """(scale, growth_tracker, applied_steps) from the device state (waits)."""
+        import numpy as np
+        raw = self.amp_state.cpu().numpy()
+        return float(raw[:1].view(np.float32)[0]), int(raw[:1].view(np.int32)[1]), int(raw[1])
+
+    def step_amp(self, grads, *, lr, beta1, beta2, eps, weight_decay, max_grad_norm=0.0,
+                 growth_factor=2.0, backoff_factor=0.5, growth_interval=2000, want_norm=False,
+                 return_code=False):
+        ptrs = [g if isinstance(g, int) else g.data_ptr() for g in grads]
+        if len(ptrs) != self.M:
+            raise ValueError(f"expected {self.M} gradient contributions")
+        return zero_offload_step_amp(self.ctx, ptrs, lr, beta1, beta2, eps, weight_decay,
+                                     max_grad_norm, self.amp_state.data_ptr(), growth_factor,
+                                     backoff_factor, growth_interval, want_norm, return_code)
 
     def segments(self):
         n = zs_plan_query(self.plan)["n_segments"]

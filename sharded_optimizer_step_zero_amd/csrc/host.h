@@ -65,9 +65,10 @@ int default_host_threads();
 // step one IEEE fp32 rounding:
 //   g' = g * coef; m' = beta1*m + c1*g'; v' = beta2*v + c2*(g'*g');
 //   den = sqrt(v')/bhat + eps; p' = p*d - alpha*(m'/den); out = bf16_rne(p')
-// with d = decay_mul on decayed runs and 1 elsewhere.
+// with d = decay_mul on decayed runs and 1 elsewhere; out is fp16_rne(p') when
+// out_f16 (the loss-scaled path's param copy).
 void host_adamw(HostPool& pool, const HostRun* runs, int32_t n_runs, int64_t shard_off, int64_t n,
                 const float* g, float coef, float* p, float* m, float* v, uint16_t* out,
-                const HostConsts& k);
+                const HostConsts& k, bool out_f16 = false);
 
 }  // namespace zs

@@ -29,6 +29,53 @@ constexpr unsigned kDefaultMxcsr = 0x1F80u;
 #define ZS_ISA_CLONES __attribute__((target_clones("avx512f", "avx2", "default")))
 #endif
 
+// fp32 -> IEEE binary16, round to nearest even, from the format's definition:
+// NaN -> quiet NaN; |x| >= 65520 (halfway above the largest finite 65504, a tie
+// that goes to the even neighbour 2^16) -> Inf; normals rebias the exponent
+// (127 -> 15) and round 13 mantissa bits away; below 2^-14 the result is
+// x * 2^24 rounded to an integer (subnormals, and 2^-14 itself when it rounds
+// up), which for a = 1.m * 2^(e-127) is the 24-bit significand shifted right
+// by 126 - e; anything below 2^-25 (and 2^-25 itself, a tie to 0) is zero.
+inline uint32_t mask_if(bool c) { return 0u - (uint32_t)c; }
+
+// Written with bit masks rather than branches or conditional expressions, so
+// the loop vectorizes: the normal and the subnormal result are both computed and
+// the range picks one.  Shift counts are clamped to 1..31 so no shift is
+// undefined; the lanes that needed the clamp are never selected.
+inline uint16_t f32_to_f16_rne(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  const uint32_t r = a - 0x38000000u;
+  const uint32_t normal = (r + 0x0FFFu + ((r >> 13) & 1u)) >> 13;
+  const uint32_t sig = (a & 0x007FFFFFu) | 0x00800000u;
+  uint32_t s = 126u - (a >> 23);  // 14..24 for the subnormal range
+  s = (s & ~mask_if(s > 31u)) | (31u & mask_if(s > 31u));
+  s = s | (uint32_t)(s == 0u);
+  const uint32_t q = sig >> s, rem = sig & ((1u << s) - 1u), half = 1u << (s - 1u);
+  const uint32_t up = (uint32_t)(rem > half) | ((uint32_t)(rem == half) & q);
+  const uint32_t sub = q + (up & 1u);
+  // below 2^-25, and 2^-25 itself (a tie to the even 0): zero
+  uint32_t h = sub & mask_if(a >= 0x33000000u);
+  const uint32_t is_normal = mask_if(a >= 0x38800000u);
+  const uint32_t is_inf = mask_if(a >= 0x477FF000u);
+  const uint32_t is_nan = mask_if(a > 0x7F800000u);
+  h = (h & ~is_normal) | (normal & is_normal);
+  h = (h & ~is_inf) | (0x7C00u & is_inf);
+  h = (h & ~is_nan) | (0x7E00u & is_nan);
+  return (uint16_t)(sign | h);
+}
+
+inline uint16_t f32_to_bf16_rne(float x) {  // a NaN stays a quiet NaN
+  uint32_t b;
+  memcpy(&b, &x, sizeof b);
+  const uint32_t rne = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+  const uint32_t qnan = (b >> 16) | 0x40u;
+  return (uint16_t)(((b & 0x7FFFFFFFu) > 0x7F800000u) ? qnan : rne);
+}
+
+template <bool F16>
 ZS_ISA_CLONES void adamw_span(
     int64_t n, const float* __restrict g, float coef, float* __restrict p, float* __restrict m,
     float* __restrict v, uint16_t* __restrict out, float beta1, float beta2, float c1, float c2,
@@ -52,12 +99,7 @@ ZS_ISA_CLONES void adamw_span(
     p[i] = pn;
     m[i] = m1;
     v[i] = v1;
-    // bf16 round to nearest even; a NaN stays a quiet NaN
-    uint32_t b;
-    memcpy(&b, &pn, sizeof b);
-    const uint32_t rne = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-    const uint32_t qnan = (b >> 16) | 0x40u;
-    out[i] = (uint16_t)(((b & 0x7FFFFFFFu) > 0x7F800000u) ? qnan : rne);
+    out[i] = F16 ? f32_to_f16_rne(pn) : f32_to_bf16_rne(pn);
   }
 }
 
@@ -119,7 +161,7 @@ int default_host_threads() {
 
 void host_adamw(HostPool& pool, const HostRun* runs, int32_t n_runs, int64_t shard_off, int64_t n,
                 const float* g, float coef, float* p, float* m, float* v, uint16_t* out,
-                const HostConsts& k) {
+                const HostConsts& k, bool out_f16) {
   if (n <= 0) return;
   pool.run([&](int id, int nw) {
     // contiguous slices, cut on 64-element (256-byte) boundaries
@@ -135,8 +177,12 @@ void host_adamw(HostPool& pool, const HostRun* runs, int32_t n_runs, int64_t sha
       const int64_t e = std::min(s_hi, r[1].start);  // r[1] exists: the table ends with a sentinel
       const float d = (r->flags & 1) ? k.decay_mul : 1.0f;
       const int64_t i = s - shard_off;
-      adamw_span(e - s, g + i, coef, p + i, m + i, v + i, out + i, k.beta1, k.beta2, k.c1, k.c2,
-                 k.alpha, k.bhat, k.eps, d);
+      if (out_f16)
+        adamw_span<true>(e - s, g + i, coef, p + i, m + i, v + i, out + i, k.beta1, k.beta2,
+                         k.c1, k.c2, k.alpha, k.bhat, k.eps, d);
+      else
+        adamw_span<false>(e - s, g + i, coef, p + i, m + i, v + i, out + i, k.beta1, k.beta2,
+                          k.c1, k.c2, k.alpha, k.bhat, k.eps, d);
       s = e;
     }
   });

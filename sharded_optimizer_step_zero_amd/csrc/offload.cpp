@@ -111,6 +111,7 @@ int enomem(const char* msg) {
 struct zs_offload {
   int32_t M = 0;
   uint32_t flags = 0;
+  bool fp16 = false;  // ZS_FP16: fp16 gradients and param, zero_offload_step_amp
   int64_t shard_len = 0, chunk = 0;
   std::vector<zs::HostRun> runs;
   std::vector<std::pair<int64_t, int64_t>> chunks;
@@ -143,7 +144,7 @@ extern "C" size_t zs_offload_staging_bytes(int64_t chunk_elems) {
   return staging_layout(chunk_elems).total;
 }
 
-extern "C" int zero_offload_init(zs_offload** out, const zs_plan* plan, int32_t M, void* param_bf16,
+extern "C" int zero_offload_init(zs_offload** out, const zs_plan* plan, int32_t M, void* param,
                                  float* master, float* exp_avg, float* exp_avg_sq, void* workspace,
                                  size_t workspace_bytes, void* staging, size_t staging_bytes,
                                  int64_t chunk_elems, int32_t n_threads, void* stream,
@@ -153,15 +154,16 @@ extern "C" int zero_offload_init(zs_offload** out, const zs_plan* plan, int32_t 
   *out = nullptr;
   if (!plan) return einval("zero_offload_init: plan is NULL");
   if (M < 1 || M > ZS_MAX_M) return einval("zero_offload_init: M must lie in [1, 16]");
-  if (flags & ~(ZS_SKIP_NONFINITE | ZS_STAGE_AVERAGE))
-    return einval("zero_offload_init: flags may hold only ZS_SKIP_NONFINITE (staging is implied)");
+  if (flags & ~(ZS_SKIP_NONFINITE | ZS_STAGE_AVERAGE | ZS_FP16))
+    return einval("zero_offload_init: flags may hold ZS_SKIP_NONFINITE and ZS_FP16 "
+                  "(staging is implied)");
   if (chunk_elems < 64 || chunk_elems % 64)
     return einval("zero_offload_init: chunk_elems must be a positive multiple of 64");
   if (n_threads < 0 || n_threads > 1024)
     return einval("zero_offload_init: n_threads must lie in [0, 1024]");
-  if (!param_bf16 || !master || !exp_avg || !exp_avg_sq || !workspace || !staging)
+  if (!param || !master || !exp_avg || !exp_avg_sq || !workspace || !staging)
     return einval("zero_offload_init: NULL buffer");
-  if (!aligned(param_bf16, 16) || !aligned(master, 16) || !aligned(exp_avg, 16) ||
+  if (!aligned(param, 16) || !aligned(master, 16) || !aligned(exp_avg, 16) ||
       !aligned(exp_avg_sq, 16))
     return einval("zero_offload_init: buffers must be 16-byte aligned");
   if (!aligned(workspace, 256) || !aligned(staging, 256))
@@ -178,9 +180,10 @@ extern "C" int zero_offload_init(zs_offload** out, const zs_plan* plan, int32_t 
   if (!c) return enomem("zero_offload_init: out of host memory");
   c->M = M;
   c->flags = flags;
+  c->fp16 = (flags & ZS_FP16) != 0;
   c->shard_len = plan->shard_len;
   c->chunk = chunk_elems;
-  c->param = static_cast<uint16_t*>(param_bf16);
+  c->param = static_cast<uint16_t*>(param);
   c->master = master;
   c->m = exp_avg;
   c->v = exp_avg_sq;
@@ -225,52 +228,39 @@ int fail(zs_offload* c, const char* where, hipError_t e) {
 
 }  // namespace
 
-extern "C" int zero_offload_step(zs_offload* c, const void* const* grads, float lr, float beta1,
-                                 float beta2, float eps, float weight_decay, int64_t step,
-                                 float max_grad_norm, double* grad_norm_out) {
-  using zs::einval;
-  if (!c) return einval("zero_offload_step: ctx is NULL");
-  int rc = zs::check_hparams(lr, beta1, beta2, eps, weight_decay, step);
-  if (rc) return rc;
-  if (isnan(max_grad_norm) || isinf(max_grad_norm))
-    return einval("zero_offload_step: max_grad_norm must be finite");
-  if (!grads) return einval("zero_offload_step: grads is NULL");
-  zs::GradPtrs g;
-  memset(&g, 0, sizeof g);
+namespace {
+
+int gather(const zs_offload* c, const void* const* grads, zs::GradPtrs* g, const char* who) {
+  if (!grads) return zs::einval((std::string(who) + ": grads is NULL").c_str());
+  memset(g, 0, sizeof *g);
   for (int j = 0; j < c->M; j++) {
     if (!grads[j] || !aligned(grads[j], 16))
-      return einval("zero_offload_step: every grads[j] must be a non-NULL 16-byte-aligned pointer");
-    g.p[j] = static_cast<const uint16_t*>(grads[j]);
+      return zs::einval((std::string(who) +
+                         ": every grads[j] must be a non-NULL 16-byte-aligned pointer")
+                            .c_str());
+    g->p[j] = static_cast<const uint16_t*>(grads[j]);
   }
-  if (c->shard_len == 0) {
-    if (grad_norm_out) *grad_norm_out = 0.0;
-    return ZS_OK;
-  }
-  const int64_t S = c->shard_len;
-  const bool clip = max_grad_norm > 0.0f;
-  const zs::HostConsts k =
-      host_consts(zs::step_consts(lr, beta1, beta2, eps, weight_decay, step));
-  float* stage = reinterpret_cast<float*>(c->ws + c->lay.stage_off);
-  double* partials = reinterpret_cast<double*>(c->ws + c->lay.partials_off);
-  zs::ClipScalars* sc_dev = reinterpret_cast<zs::ClipScalars*>(c->ws + c->lay.scalars_off);
-  volatile zs::ClipScalars* sc_host = reinterpret_cast<zs::ClipScalars*>(c->staging);
+  return ZS_OK;
+}
 
-  // the device part: reduce, stage the averages, norm and clip scalars
-  hipError_t e = zs::launch_sumsq(c->M, g, S, partials, stage, c->stream);
-  if (e == hipSuccess)
-    e = zs::launch_finalize(partials + zs::level1_partials(S), zs::final_partials(S), nullptr,
-                            max_grad_norm, clip ? 1 : 0,
-                            (c->flags & ZS_SKIP_NONFINITE) ? 1 : 0, sc_dev, c->stream);
-  if (e != hipSuccess) return zs::ehip("zero_offload_step: norm pass", e);
+// Everything after the device part of a step (norm pass and finalize, already
+// queued on the caller's stream, which wrote the 256-byte scalars block and the
+// staged averages): the scalars and the averages come to the host, the host
+// updates chunk by chunk, the params go back.  k_host: the step constants, or
+// null to take the ones the device computed (the loss-scaled step).
+int pipeline(zs_offload* c, const zs::HostConsts* k_host, bool out_f16, double* grad_norm_out,
+             const char* who) {
+  float* stage = reinterpret_cast<float*>(c->ws + c->lay.stage_off);
+  const char* block_dev = c->ws + c->lay.scalars_off;
+  volatile char* block_host = c->staging;  // the first 256 staging bytes
   // both copy streams start after everything the caller queued before this step
-  e = hipEventRecord(c->ready, c->stream);
+  hipError_t e = hipEventRecord(c->ready, c->stream);
   if (e == hipSuccess) e = hipStreamWaitEvent(c->d2h, c->ready, 0);
   if (e == hipSuccess) e = hipStreamWaitEvent(c->h2d, c->ready, 0);
   if (e == hipSuccess)
-    e = hipMemcpyAsync((void*)sc_host, sc_dev, sizeof(zs::ClipScalars), hipMemcpyDeviceToHost,
-                       c->d2h);
+    e = hipMemcpyAsync((void*)block_host, block_dev, 256, hipMemcpyDeviceToHost, c->d2h);
   if (e == hipSuccess) e = hipEventRecord(c->scalars, c->d2h);
-  if (e != hipSuccess) return fail(c, "zero_offload_step: queueing the copies", e);
+  if (e != hipSuccess) return fail(c, who, e);
 
   const int64_t n_chunks = (int64_t)c->chunks.size();
   auto gbuf = [&](int b) { return reinterpret_cast<float*>(c->staging + c->sl.g_off[b]); };
@@ -285,16 +275,18 @@ extern "C" int zero_offload_step(zs_offload* c, const void* const* grads, float 
   };
   for (int64_t ci = 0; ci < std::min<int64_t>(2, n_chunks) && e == hipSuccess; ci++) e = fetch(ci);
   if (e == hipSuccess) e = hipEventSynchronize(c->scalars);
-  if (e != hipSuccess) return fail(c, "zero_offload_step: gradient copies", e);
-  const double norm = sc_host->norm;
-  const float coef = sc_host->coef;
-  const bool skip = sc_host->skip != 0;
-  if (grad_norm_out) *grad_norm_out = norm;
-  const int done_rc = (grad_norm_out && !isfinite(norm)) ? ZS_NONFINITE : ZS_OK;
-  if (skip) {  // non-finite norm with ZS_SKIP_NONFINITE: the state stays as it is
+  if (e != hipSuccess) return fail(c, who, e);
+  zs::ClipScalars sc;
+  zs::StepConsts kd;
+  memcpy(&sc, (const void*)block_host, sizeof sc);
+  memcpy(&kd, (const void*)(block_host + 64), sizeof kd);
+  if (grad_norm_out) *grad_norm_out = sc.norm;
+  const int done_rc = (grad_norm_out && !isfinite(sc.norm)) ? ZS_NONFINITE : ZS_OK;
+  if (sc.skip) {  // the step is skipped: the state stays as it is
     e = hipStreamSynchronize(c->d2h);
-    return e == hipSuccess ? done_rc : fail(c, "zero_offload_step: draining copies", e);
+    return e == hipSuccess ? done_rc : fail(c, who, e);
   }
+  const zs::HostConsts k = k_host ? *k_host : host_consts(kd);
 
   const int32_t n_runs = (int32_t)c->runs.size() - 1;
   for (int64_t ci = 0; ci < n_chunks; ci++) {
@@ -302,21 +294,110 @@ extern "C" int zero_offload_step(zs_offload* c, const void* const* grads, float 
     const int b = (int)(ci & 1);
     e = hipEventSynchronize(c->g_ready[b]);           // this chunk's averages have landed
     if (e == hipSuccess) e = hipEventSynchronize(c->p_sent[b]);  // param buffer b is free again
-    if (e != hipSuccess) return fail(c, "zero_offload_step: waiting for a copy", e);
-    zs::host_adamw(*c->pool, c->runs.data(), n_runs, off, len, gbuf(b), coef, c->master + off,
-                   c->m + off, c->v + off, pbuf(b), k);
+    if (e != hipSuccess) return fail(c, who, e);
+    zs::host_adamw(*c->pool, c->runs.data(), n_runs, off, len, gbuf(b), sc.coef, c->master + off,
+                   c->m + off, c->v + off, pbuf(b), k, out_f16);
     if (ci + 2 < n_chunks) e = fetch(ci + 2);
     if (e == hipSuccess)
       e = hipMemcpyAsync(c->param + off, pbuf(b), (size_t)len * sizeof(uint16_t),
                          hipMemcpyHostToDevice, c->h2d);
     if (e == hipSuccess) e = hipEventRecord(c->p_sent[b], c->h2d);
-    if (e != hipSuccess) return fail(c, "zero_offload_step: param copies", e);
+    if (e != hipSuccess) return fail(c, who, e);
   }
   // later work on the caller's stream sees the new params
   e = hipEventRecord(c->done, c->h2d);
   if (e == hipSuccess) e = hipStreamWaitEvent(c->stream, c->done, 0);
-  if (e != hipSuccess) return fail(c, "zero_offload_step: ordering the caller's stream", e);
+  if (e != hipSuccess) return fail(c, who, e);
   return done_rc;
+}
+
+int estate(const char* msg) {
+  zs::set_error(msg);
+  return ZS_ESTATE;
+}
+
+}  // namespace
+
+extern "C" int zero_offload_step(zs_offload* c, const void* const* grads, float lr, float beta1,
+                                 float beta2, float eps, float weight_decay, int64_t step,
+                                 float max_grad_norm, double* grad_norm_out) {
+  using zs::einval;
+  if (!c) return einval("zero_offload_step: ctx is NULL");
+  if (c->fp16) return estate("zero_offload_step: fp16 context: use zero_offload_step_amp");
+  int rc = zs::check_hparams(lr, beta1, beta2, eps, weight_decay, step);
+  if (rc) return rc;
+  if (isnan(max_grad_norm) || isinf(max_grad_norm))
+    return einval("zero_offload_step: max_grad_norm must be finite");
+  zs::GradPtrs g;
+  if ((rc = gather(c, grads, &g, "zero_offload_step"))) return rc;
+  if (c->shard_len == 0) {
+    if (grad_norm_out) *grad_norm_out = 0.0;
+    return ZS_OK;
+  }
+  const int64_t S = c->shard_len;
+  const zs::HostConsts k =
+      host_consts(zs::step_consts(lr, beta1, beta2, eps, weight_decay, step));
+  float* stage = reinterpret_cast<float*>(c->ws + c->lay.stage_off);
+  double* partials = reinterpret_cast<double*>(c->ws + c->lay.partials_off);
+  zs::ClipScalars* sc_dev = reinterpret_cast<zs::ClipScalars*>(c->ws + c->lay.scalars_off);
+  // the device part: reduce, stage the averages, norm and clip scalars
+  hipError_t e = zs::launch_sumsq(c->M, g, S, partials, stage, c->stream);
+  if (e == hipSuccess)
+    e = zs::launch_finalize(partials + zs::level1_partials(S), zs::final_partials(S), nullptr,
+                            max_grad_norm, max_grad_norm > 0.0f ? 1 : 0,
+                            (c->flags & ZS_SKIP_NONFINITE) ? 1 : 0, sc_dev, c->stream);
+  if (e != hipSuccess) return zs::ehip("zero_offload_step: norm pass", e);
+  return pipeline(c, &k, false, grad_norm_out, "zero_offload_step");
+}
+
+extern "C" int zero_offload_step_amp(zs_offload* c, const void* const* grads, float lr,
+                                     float beta1, float beta2, float eps, float weight_decay,
+                                     float max_grad_norm, zs_amp_state* state_dev,
+                                     float growth_factor, float backoff_factor,
+                                     int32_t growth_interval, double* grad_norm_out) {
+  using zs::einval;
+  if (!c) return einval("zero_offload_step_amp: ctx is NULL");
+  if (!c->fp16) return estate("zero_offload_step_amp: needs a context created with ZS_FP16");
+  int rc = zs::check_hparams(lr, beta1, beta2, eps, weight_decay, 1);
+  if (rc) return rc;
+  if (isnan(max_grad_norm) || isinf(max_grad_norm))
+    return einval("zero_offload_step_amp: max_grad_norm must be finite");
+  if (!state_dev || !aligned(state_dev, 16))
+    return einval("zero_offload_step_amp: state_dev must be a 16-byte-aligned device pointer");
+  if (!(growth_factor >= 1.0f) || isinf(growth_factor) || !(backoff_factor > 0.0f) ||
+      !(backoff_factor <= 1.0f) || growth_interval < 1)
+    return einval("zero_offload_step_amp: need growth >= 1, 0 < backoff <= 1, interval >= 1");
+  zs::GradPtrs g;
+  if ((rc = gather(c, grads, &g, "zero_offload_step_amp"))) return rc;
+  if (c->shard_len == 0) {
+    if (grad_norm_out) *grad_norm_out = 0.0;
+    return ZS_OK;
+  }
+  const int64_t S = c->shard_len;
+  zs::AmpState* st = reinterpret_cast<zs::AmpState*>(state_dev);
+  zs::AmpParams p;
+  p.lr = lr;
+  p.beta1 = beta1;
+  p.beta2 = beta2;
+  p.eps = eps;
+  p.weight_decay = weight_decay;
+  p.max_norm = max_grad_norm;
+  p.growth = growth_factor;
+  p.backoff = backoff_factor;
+  p.interval = growth_interval;
+  p.clip = max_grad_norm > 0.0f ? 1 : 0;
+  float* stage = reinterpret_cast<float*>(c->ws + c->lay.stage_off);
+  double* partials = reinterpret_cast<double*>(c->ws + c->lay.partials_off);
+  char* block = c->ws + c->lay.scalars_off;
+  // the device part: unscaled averages staged, found-inf, scaler update and the
+  // step constants at t = applied + 1, all on the device
+  hipError_t e = zs::launch_sumsq_f16(c->M, g, S, partials, st, stage, c->stream);
+  if (e == hipSuccess)
+    e = zs::launch_amp_finalize(partials + zs::level1_partials(S), zs::final_partials(S), st, p,
+                                reinterpret_cast<zs::ClipScalars*>(block),
+                                reinterpret_cast<zs::StepConsts*>(block + 64), c->stream);
+  if (e != hipSuccess) return zs::ehip("zero_offload_step_amp: norm pass", e);
+  return pipeline(c, nullptr, true, grad_norm_out, "zero_offload_step_amp");
 }
 
 extern "C" int zero_offload_set_stream(zs_offload* c, void* stream) {
@@ -329,9 +410,9 @@ extern "C" void zero_offload_destroy(zs_offload* c) { delete c; }
 
 extern "C" int zs_host_adamw(const zs_plan* plan, int64_t shard_off, int64_t n,
                              const float* grad_avg, float coef, float* master, float* exp_avg,
-                             float* exp_avg_sq, uint16_t* param_bf16, float lr, float beta1,
+                             float* exp_avg_sq, uint16_t* param, float lr, float beta1,
                              float beta2, float eps, float weight_decay, int64_t step,
-                             int32_t n_threads) {
+                             int32_t n_threads, uint32_t flags) {
   using zs::einval;
   if (!plan) return einval("zs_host_adamw: plan is NULL");
   int rc = zs::check_hparams(lr, beta1, beta2, eps, weight_decay, step);
@@ -342,7 +423,8 @@ extern "C" int zs_host_adamw(const zs_plan* plan, int64_t shard_off, int64_t n,
   if (n_threads < 0 || n_threads > 1024)
     return einval("zs_host_adamw: n_threads must lie in [0, 1024]");
   if (n == 0) return ZS_OK;
-  if (!grad_avg || !master || !exp_avg || !exp_avg_sq || !param_bf16)
+  if (flags & ~ZS_FP16) return einval("zs_host_adamw: flags may hold only ZS_FP16");
+  if (!grad_avg || !master || !exp_avg || !exp_avg_sq || !param)
     return einval("zs_host_adamw: NULL array");
   const zs::HostConsts k =
       host_consts(zs::step_consts(lr, beta1, beta2, eps, weight_decay, step));
@@ -350,7 +432,7 @@ extern "C" int zs_host_adamw(const zs_plan* plan, int64_t shard_off, int64_t n,
     const std::vector<zs::HostRun> runs = host_runs(plan);
     zs::HostPool pool(n_threads > 0 ? n_threads : zs::default_host_threads());
     zs::host_adamw(pool, runs.data(), (int32_t)runs.size() - 1, shard_off, n, grad_avg, coef,
-                   master, exp_avg, exp_avg_sq, param_bf16, k);
+                   master, exp_avg, exp_avg_sq, param, k, (flags & ZS_FP16) != 0);
   } catch (const std::bad_alloc&) {
     return enomem("zs_host_adamw: out of host memory");
   } catch (const std::system_error&) {

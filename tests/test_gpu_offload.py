@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+import synth
 import sharded_optimizer_step_zero_amd as zsm
 from oracle import layout as L
 from sharded_optimizer_step_zero_amd import ZeroOffload, ZeroShard
@@ -157,3 +158,91 @@ def test_offload_rejected_arguments_leave_state_untouched():
     for x, y in zip(o.state(), before):
         assert np.array_equal(_bits(x), _bits(y))
     o.z.close()
+
+
+def _u16_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+@pytest.mark.parametrize("clip", [0.0, 2.0])
+def test_offload_amp_sequence_matches_oracle(clip):
+    """The offloaded loss-scaled step: scaler decisions and step constants from the
+    device, fp32 state updated on the host, fp16 param back; an Inf and a NaN
+    are injected, so two steps are skipped and the scale backs off."""
+    log(f"test_offload_amp_sequence_matches_oracle clip={clip}")
+    numel, decay = [70_001, 64, 5, 130_000, 333], [1, 0, 0, 1, 0]
+    N, rank, M = 3, 1, 3
+    lay = L.plan(numel, decay, N, rank, 25_000_000, 64)
+    z = ZeroOffload(numel, decay, N, rank, M, fp16=True, chunk_elems=1 << 14)
+    S = z.shard_len
+    pad = lay.padding_ranges()
+    master = synth.host_normal_f32(S, synth.key(78, 0), 0.02)
+    for o, n in pad:
+        master[o:o + n] = 0
+    z.master[:S] = torch.from_numpy(master)
+    z.amp_init(2.0 ** 14)
+    sc = oracle.Scaler(scale=2.0 ** 14, growth_interval=3)
+    p, m, v = master.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32)
+    pf = np.zeros(S, np.uint16)
+    mask = lay.decay_mask()
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    skips = 0
+    for s in range(12):
+        scale = float(sc.scale[0])
+        gs = []
+        for j in range(M):
+            g = synth.host_grad_f16(S, synth.key(78, 1 + j + M * s), 1e-3, scale)
+            for o, n in pad:
+                g[o:o + n] = 0
+            gs.append(g)
+        if s in (3, 8):
+            gs[2][4321] = 0x7C00 if s == 3 else 0x7E00
+        rc, norm = z.step_amp([_u16_dev(g) for g in gs], max_grad_norm=clip, growth_interval=3,
+                              want_norm=True, return_code=True, **hp)
+        fi, onorm = oracle.amp_step(gs, p, m, v, pf, mask, sc, max_grad_norm=clip, **hp)
+        skips += fi
+        assert (rc == zsm.ZS_NONFINITE) == fi
+        if not fi:
+            assert abs(norm - onorm) <= 1e-12 * onorm
+        torch.cuda.synchronize()
+        got = [z.master[:S].numpy(), z.exp_avg[:S].numpy(), z.exp_avg_sq[:S].numpy(),
+               z.param.cpu().view(torch.int16).numpy().view(np.uint16)[:S]]
+        for a, b in zip(got, (p, m, v, pf)):
+            assert np.array_equal(_bits(a), _bits(b)), s
+        assert z.amp_read() == (float(sc.scale[0]), int(sc.tracker[0]), sc.applied)
+    assert skips == 2
+    z.close()
+
+
+def test_offload_amp_equals_device_amp():
+    log("test_offload_amp_equals_device_amp")
+    numel, decay = [5000, 64, 130_001, 7], [1, 0, 1, 0]
+    zo = ZeroOffload(numel, decay, 2, 1, 4, fp16=True, chunk_elems=1 << 12,
+                     flags=zsm.ZS_SKIP_NONFINITE)
+    zd = ZeroShard(numel, decay, 2, 1, 4, fp16=True, flags=zsm.ZS_STAGE_AVERAGE)
+    S = zo.shard_len
+    m0 = synth.host_normal_f32(S, synth.key(79, 0), 0.02)
+    zo.master[:S] = torch.from_numpy(m0)
+    zd.master[:S].copy_(torch.from_numpy(m0))
+    zo.amp_init(2.0 ** 10)
+    zd.amp_init(2.0 ** 10)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_grad_norm=0.5,
+              growth_interval=2)
+    for s in range(5):
+        gs = [torch.empty(S, dtype=torch.float16, device="cuda") for _ in range(4)]
+        for j, g in enumerate(gs):
+            synth.dev_grad_f16(g, synth.key(79, 1 + j + 4 * s), 1e-3, 2.0 ** 10)
+        if s == 2:
+            gs[0][10] = float("inf")
+        zo.step_amp(gs, **hp)
+        zd.step_amp(gs, **hp)
+        torch.cuda.synchronize()
+        got = [zo.master[:S].numpy(), zo.exp_avg[:S].numpy(), zo.exp_avg_sq[:S].numpy(),
+               zo.param.cpu().view(torch.int16).numpy().view(np.uint16)[:S]]
+        want = [to_host(x)[:S] for x in (zd.master, zd.exp_avg, zd.exp_avg_sq)] + \
+               [zd.param.cpu().view(torch.int16).numpy().view(np.uint16)[:S]]
+        for a, b in zip(got, want):
+            assert np.array_equal(_bits(a), _bits(b)), s
+        assert zo.amp_read() == zd.amp_read()
+    zo.close()
+    zd.close()

@@ -131,7 +131,7 @@ def test_offload_init_argument_errors_before_any_device_call():
     st = zs.zs_offload_staging_bytes(1 << 16)
     assert st > 6 * (1 << 16) and zs.zs_offload_staging_bytes(100) == 0
     try:
-        bad = [dict(chunk_elems=100), dict(flags=zs.ZS_FP16), dict(n_threads=-1),
+        bad = [dict(chunk_elems=100), dict(flags=0x80), dict(n_threads=-1),
                dict(workspace_bytes=ws - 1), dict(staging_bytes=st - 1), dict(staging=272)]
         for kw in bad:
             args = dict(workspace_bytes=ws, staging=256, staging_bytes=st, chunk_elems=1 << 16,
@@ -142,5 +142,83 @@ def test_offload_init_argument_errors_before_any_device_call():
                                      args["staging"], args["staging_bytes"], args["chunk_elems"],
                                      args["n_threads"], 0, args["flags"])
             assert e.value.code == zs.ZS_EINVAL, kw
+    finally:
+        zs.zs_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("clip", [None, 0.05])
+def test_host_update_fp16_equals_oracle(clip):
+    """The loss-scaled variant's host update: the unscaled M-way average in, the
+    fp16 param copy out (flags = ZS_FP16), against the oracle's fp16 step."""
+    lay = L.plan(NUMEL, DECAY, 3, 1, 25_000_000, 64)
+    S = lay.shard_len
+    scale = 2.0 ** 13
+    grads = [synth.host_grad_f16(S, synth.key(21, 1 + j), 1e-3, scale) for j in range(3)]
+    for g in grads:
+        for o, n in lay.padding_ranges():
+            g[o:o + n] = 0
+    master = synth.host_normal_f32(S, synth.key(21, 0), 0.02)
+    for o, n in lay.padding_ranges():
+        master[o:o + n] = 0
+    inv = oracle.inv_scale(scale)
+    g_avg = oracle.reduce_mean_f16(grads, inv)
+    coef = oracle.clip_coef(oracle.grad_sumsq_f16(grads, inv), clip) if clip else None
+    plan = zs.zs_plan_create(NUMEL, DECAY, 3, 1)
+    try:
+        p, m, v, b = master.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32), \
+            np.zeros(S, np.uint16)
+        op, om, ov, ob = master.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32), \
+            np.zeros(S, np.uint16)
+        for t in range(1, 4):
+            zs.zs_host_adamw(plan, 0, S, g_avg.ctypes.data, float(coef) if clip else 1.0,
+                             p.ctypes.data, m.ctypes.data, v.ctypes.data, b.ctypes.data, step=t,
+                             n_threads=4, flags=zs.ZS_FP16, **HP)
+            oracle.step_f16(grads, op, om, ov, ob, lay.decay_mask(), step=t, inv_scale=inv,
+                            coef=coef, **HP)
+            for x, y in zip((p, m, v, b), (op, om, ov, ob)):
+                assert np.array_equal(_bits(x), _bits(y)), t
+    finally:
+        zs.zs_plan_destroy(plan)
+
+
+def test_host_fp16_recast_matches_oracle():
+    """With lr = 0 the update leaves master as it is, so the param copy is the
+    fp16 conversion of master: every exponent, both signs, mantissas at and around
+    each rounding boundary of the normal and subnormal ranges, and random ones."""
+    rng = np.random.default_rng(7)
+    exps = np.arange(256, dtype=np.uint32)
+    low = np.array([0, 1, 0x0FFF, 0x1000, 0x1001, 0x1FFF, 0x2000, 0x2001, 0x3FFF, 0x7FFFFF,
+                    0x400000, 0x3FFFFF, 0x7FF000, 0x7FEFFF], np.uint32)
+    rand = rng.integers(0, 1 << 23, 600, dtype=np.uint32)
+    mant = np.concatenate([low, rand])
+    # subnormal-range boundaries: for exponent e the result keeps the bits above 126 - e
+    for s in range(14, 25):
+        half = np.uint32(1 << (s - 1))
+        for q in (0, 1, 2, 3):
+            base = np.uint32((q << s) & 0x7FFFFF)
+            mant = np.concatenate([mant, np.array([base, base + half, base + half - 1,
+                                                   base + half + 1], np.uint32) & 0x7FFFFF])
+    u = (exps[:, None] << 23 | mant[None, :]).reshape(-1)
+    u = np.concatenate([u, u | np.uint32(0x80000000)])
+    x = u.view(np.float32)
+    n = x.size
+    pad = (-n) % 8
+    x = np.concatenate([x, np.zeros(pad, np.float32)])
+    n = x.size
+    plan = zs.zs_plan_create([n], [0], 1, 0, align=8)
+    try:
+        p = x.copy()
+        m = np.zeros(n, np.float32)
+        v = np.zeros(n, np.float32)
+        g = np.zeros(n, np.float32)
+        b = np.zeros(n, np.uint16)
+        hp = dict(HP, lr=0.0, weight_decay=0.0)
+        zs.zs_host_adamw(plan, 0, n, g.ctypes.data, 1.0, p.ctypes.data, m.ctypes.data,
+                         v.ctypes.data, b.ctypes.data, step=1, n_threads=4, flags=zs.ZS_FP16, **hp)
+        nan = np.isnan(x)
+        assert np.array_equal(p.view(np.uint32)[~nan], x.view(np.uint32)[~nan])
+        want = oracle.f32_to_f16(x)
+        assert np.array_equal(b[~nan], want[~nan])
+        assert ((b[nan] & 0x7C00) == 0x7C00).all() and ((b[nan] & 0x3FF) != 0).all()
     finally:
         zs.zs_plan_destroy(plan)
