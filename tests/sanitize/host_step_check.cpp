@@ -1,7 +1,8 @@
 // host_step_check.cpp -- the host update and its thread pool (host_step.cpp)
 // under sanitizers: AddressSanitizer + UndefinedBehaviorSanitizer for bounds
 // and undefined behaviour, ThreadSanitizer for races in the pool's hand-off.
-// The same update over a many-run table is run with 1..16 threads, repeatedly
+// The same update (bf16 and fp16 param out; masters include values across the
+// fp16 range) over a many-run table is run with 1..16 threads, repeatedly
 // and from pools created and destroyed in a loop; every result must equal the
 // one-thread result bit for bit.  Exit status 0 when all agree.
 #include <stdint.h>
@@ -30,9 +31,12 @@ int main() {
   std::vector<float> g(S), p0(S);
   for (int64_t i = 0; i < S; i++) {
     g[i] = 1e-3f * uniform_pm1();
-    p0[i] = 0.02f * uniform_pm1();
+    // masters over many magnitudes: fp16 subnormals, normals, overflow
+    const int k = (int)(i % 7);
+    p0[i] = uniform_pm1() * (k == 0 ? 1e-6f : k == 1 ? 3e-5f : k == 2 ? 7e4f : 0.02f);
   }
   const zs::HostConsts k = {0.9f, 0.95f, 0.1f, 0.05f, 1e-3f, 0.2236068f, 1e-8f, 0.9999f};
+  for (int f16 = 0; f16 < 2; f16++) {
   std::vector<float> rp, rm, rv;
   std::vector<uint16_t> rb;
   for (int threads : {1, 2, 3, 7, 16}) {
@@ -45,17 +49,19 @@ int main() {
         for (int64_t off = 0; off < S; off += 100000) {
           const int64_t n = off + 100000 <= S ? 100000 : S - off;
           zs::host_adamw(pool, runs.data(), n_runs, off, n, g.data() + off, 0.5f, p.data() + off,
-                         m.data() + off, v.data() + off, b.data() + off, k);
+                         m.data() + off, v.data() + off, b.data() + off, k, f16 != 0);
         }
       }
       if (rp.empty()) {
         rp = p, rm = m, rv = v, rb = b;
       } else if (memcmp(rp.data(), p.data(), S * 4) || memcmp(rm.data(), m.data(), S * 4) ||
                  memcmp(rv.data(), v.data(), S * 4) || memcmp(rb.data(), b.data(), S * 2)) {
-        fprintf(stderr, "threads=%d rep=%d: result differs from one thread\n", threads, rep);
+        fprintf(stderr, "f16=%d threads=%d rep=%d: result differs from one thread\n", f16,
+                threads, rep);
         return 1;
       }
     }
+  }
   }
   printf("host step check ok: %d runs, 1..16 threads, pools rebuilt, results identical\n", n_runs);
   return 0;
