@@ -138,3 +138,42 @@ def test_amp_rejects_wrong_context():
         y.step([torch.zeros(1000, dtype=torch.int16, device="cuda")], step=1, **HP)
     assert e.value.code == zsm.ZS_ESTATE
     y.close()
+
+
+@pytest.mark.parametrize("stage", [False, True])
+def test_gpt13b_shard_amp_full(stage):
+    """The loss-scaled step on the GPT-1.3B 1/8 shard (M = 8, the size the benchmark
+    times), whole-shard against the oracle for 3 steps, the second with an Inf."""
+    from synth.workloads import workload
+    w = workload(2)
+    log(f"test_gpt13b_shard_amp_full stage={stage}: {w.description}")
+    lay = L.plan(w.numel, w.decay, w.world_size, w.rank, w.bucket_cap, w.align)
+    z = ZeroShard(w.numel, w.decay, w.world_size, w.rank, w.M, bucket_cap=w.bucket_cap,
+                  align=w.align, fp16=True, flags=zsm.ZS_STAGE_AVERAGE if stage else 0)
+    S = z.shard_len
+    assert S == lay.shard_len
+    master = synth.host_normal_f32(S, w.master_key(), w.sigma_master)
+    z.master[:S].copy_(torch.from_numpy(master))
+    z.amp_init(2.0 ** 14)
+    sc = oracle.Scaler(scale=2.0 ** 14, growth_interval=2)
+    p, m, v = master, np.zeros(S, np.float32), np.zeros(S, np.float32)
+    pf = np.zeros(S, np.uint16)
+    mask = lay.decay_mask()
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+    for s in range(3):
+        scale = float(sc.scale[0])
+        gs = [synth.host_grad_f16(S, k, w.sigma_grad, scale) for k, _ in w.grad_keys(s)]
+        if s == 1:
+            gs[5][S // 2] = 0x7C00
+        dev = [_u16(g) for g in gs]
+        rc, norm = z.step_amp(dev, growth_interval=2, want_norm=True, return_code=True, **hp)
+        fi, onorm = oracle.amp_step(gs, p, m, v, pf, mask, sc, **hp)
+        assert (rc == zsm.ZS_NONFINITE) == fi and fi == (s == 1)
+        if not fi:
+            assert abs(norm - onorm) <= 1e-12 * onorm
+        for a, b in zip(_state(z), (p, m, v, pf)):
+            assert _eq(a, b), s
+        assert z.amp_read() == (float(sc.scale[0]), int(sc.tracker[0]), sc.applied)
+        del dev
+        log(f"  step {s + 1}: {'skipped' if fi else 'applied'}, bit-exact over {S:,} elements")
+    z.close()
