@@ -153,3 +153,56 @@ def test_checkpoint_file_roundtrip(tmp_path):
     for g, w in zip(got, want):
         assert _same(g, w)
     b.close()
+
+
+def test_llama67b_export_import_sampled():
+    """Export and import at the Llama-6.7B size (6.74G parameters: canonical
+    offsets beyond 2^32), checked on samples through device gathers: seeded
+    windows, the first and last elements of every tensor, and the last 4096
+    elements of the model."""
+    from synth.workloads import workload
+    from _gpu import Gather
+    w = workload(3)
+    log(f"test_llama67b_export_import_sampled: {w.description}")
+    torch.cuda.empty_cache()      # 94 GB of shard state and 81 GB of canonical arrays
+    lay = L.plan(w.numel, w.decay, 1, 0, w.bucket_cap, w.align)
+    z = ZeroShard(w.numel, w.decay, 1, 0, 1, bucket_cap=w.bucket_cap, align=w.align)
+    S = z.shard_len
+    synth.dev_normal_f32(z.master[:S], synth.key(SEED, 100), 0.02)
+    synth.dev_normal_f32(z.exp_avg[:S], synth.key(SEED, 101), 1e-3)
+    synth.dev_normal_f32(z.exp_avg_sq[:S], synth.key(SEED, 102), 1e-6)
+    total = w.total_params
+    assert total > (1 << 32)
+    canon = [torch.empty(total, dtype=torch.float32, device="cuda") for _ in range(3)]
+    z.export_state(*canon)
+    torch.cuda.synchronize()
+    co = lay.canonical_offsets()
+    rng = np.random.default_rng(33)
+    parts = [rng.integers(0, total - 64, 2048)[:, None] + np.arange(64)[None, :],
+             np.arange(total - 4096, total)]
+    for t, n in enumerate(w.numel):
+        if n:
+            parts += [np.array([co[t], co[t] + n - 1])]
+    cidx = np.unique(np.concatenate([np.ravel(x) for x in parts]).astype(np.int64))
+    # canonical index -> shard offset (N = 1: the tensor's flat offset + offset inside it)
+    starts = np.array(co, np.int64)
+    # the last tensor starting at or before each index (never an empty tensor)
+    t_of = np.searchsorted(starts, cidx, side="right") - 1
+    sidx = np.array(lay.tensor_flat_off, np.int64)[t_of] + (cidx - starts[t_of])
+    order = np.argsort(sidx)
+    gc, gs = Gather(cidx, "cuda"), Gather(sidx[order], "cuda")
+    for c, s in zip(canon, (z.master, z.exp_avg, z.exp_avg_sq)):
+        got = gc(c)[order]
+        want = gs(s)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # import into a zeroed shard: state back, param = bf16_rne(master)
+    for x in (z.master, z.exp_avg, z.exp_avg_sq, z.param):
+        x.zero_()
+    z.import_state(*canon)
+    torch.cuda.synchronize()
+    for c, s in zip(canon, (z.master, z.exp_avg, z.exp_avg_sq)):
+        assert np.array_equal(gc(c)[order].view(np.uint32), gs(s).view(np.uint32))
+    assert np.array_equal(gs(z.param), oracle.f32_to_bf16(gs(z.master)))
+    log(f"  {cidx.size:,} sampled elements, max canonical offset {int(cidx.max()):,}")
+    del canon
+    z.close()
