@@ -16,8 +16,9 @@ using the algorithmic bytes 2M+12 read + 14 written per parameter;
 
 On the default workload the line also carries the checkpoint export/import, the
 loss-scaled fp16 step (fused and staged) and the offloaded step on host cores
-("checkpoint", "amp_fp16", "amp_fp16_staged", "offload", "offload_fp16"), each timed after the
-headline step; --no-extras leaves them out.
+("checkpoint", "amp_fp16", "amp_fp16_staged", "offload", "offload_fp16") and the
+timed steps replayed from one HIP graph ("graph"), each timed after the headline
+step; --no-extras leaves them out.
 """
 from __future__ import annotations
 
@@ -519,7 +520,7 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if args.graph or w.name.startswith("tiny"):
+    if args.graph or w.name.startswith("tiny") or (not args.no_extras and args.workload == 2):
         out["graph"] = time_graph(zs, grads, w, hp, args.steps, args.warmup + args.steps + 1)
     # the default run on the GPT shard adds the follow-on paths' legs
     extras = not args.no_extras and args.workload == 2
