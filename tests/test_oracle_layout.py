@@ -58,12 +58,16 @@ def _check_structure(numel, decay, N, cap, align):
         bs, bl = lay0.buckets[b]
         off = lay0.tensor_flat_off[t]
         assert (off - bs) % align == 0 and bs <= off and off + n <= bs + bl
+        if n == 0 and t > 0:  # only a tensor with elements closes a bucket
+            assert b == lay0.tensor_bucket[t - 1]
     for b, (bs, bl) in enumerate(lay0.buckets):
         assert bl % (N * align) == 0
+        assert bl > 0 or sum(numel) == 0          # no bucket is left empty
         ts = [t for t in range(len(numel)) if lay0.tensor_bucket[t] == b]
         assert ts == list(range(ts[0], ts[-1] + 1))
         used = lay0.tensor_flat_off[ts[-1]] + numel[ts[-1]] - bs
-        assert used <= cap or len(ts) == 1
+        # only a bucket holding a single non-empty tensor may exceed the cap
+        assert used <= cap or sum(numel[t] > 0 for t in ts) == 1
         if b + 1 < len(lay0.buckets):  # closed because the next tensor did not fit
             nxt = ts[-1] + 1
             start_next = -(-used // align) * align
@@ -122,12 +126,40 @@ def test_layout_structure_random(seed):
     T = int(rng.integers(1, 40))
     numel = [int(x) for x in rng.integers(0, 5000, T)]
     if seed % 3 == 0:
-        numel[int(rng.integers(0, T))] = 25_000  # larger than the cap below
-    decay = [int(x) for x in rng.integers(0, 2, T)]
+        big = int(rng.integers(0, T))
+        numel[big] = 25_000  # larger than the cap below
+        if seed % 2 == 0:    # an empty tensor right after it, and leading empty tensors
+            numel.insert(big + 1, 0)
+            numel[0:0] = [0, 0]
+    decay_n = len(numel)
+    decay = [int(x) for x in rng.integers(0, 2, decay_n)]
     N = int(rng.choice([1, 2, 3, 4, 7, 8, 16]))
     align = int(rng.choice([8, 16, 64]))
     cap = int(rng.choice([4096, 10_000, 20_000]))
     _check_structure(numel, decay, N, cap, align)
+
+
+@pytest.mark.parametrize("numel", [[5000, 0, 7000], [0, 0, 5000, 0, 0, 7000, 0],
+                                   [300, 5000, 0, 0, 6000], [0], [0, 0], [5000, 0], [0, 5000]])
+def test_empty_tensors_structure(numel):
+    """Empty tensors before, between and after tensors larger than the cap."""
+    for N in (1, 4):
+        _check_structure(numel, [1] * len(numel), N, 4096, 64)
+        lay = L.plan(numel, [1] * len(numel), N, 0, 4096, 64)
+        assert len(lay.buckets) == max(1, sum(n > 0 for n in numel))
+
+
+def test_bucket_closes_only_beyond_the_cap():
+    """A tensor that ends exactly at the cap still joins the open bucket; one
+    element more and it opens the next."""
+    lay = L.plan([64, 64], [1, 1], 2, 0, 128, 64)
+    assert lay.buckets == [(0, 128)] and lay.tensor_bucket == [0, 0]
+    lay = L.plan([64, 65], [1, 1], 2, 0, 128, 64)
+    assert lay.buckets == [(0, 128), (128, 128)] and lay.tensor_bucket == [0, 1]
+    lay = L.plan([1, 64], [1, 1], 1, 0, 128, 64)  # alignment counts: 64 + 64 fits
+    assert lay.tensor_flat_off == [0, 64] and len(lay.buckets) == 1
+    lay = L.plan([1, 65], [1, 1], 1, 0, 128, 64)  # 64 + 65 does not
+    assert lay.tensor_flat_off == [0, 64] and len(lay.buckets) == 2
 
 
 def test_gpt_buckets():
