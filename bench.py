@@ -216,17 +216,15 @@ def time_amp(w, pad, dev, stream, steps: int, warmup: int, stage: bool = False,
 
     za = ZeroShard(w.numel, w.decay, w.world_size, w.rank, w.M, device=dev,
                    bucket_cap=w.bucket_cap, align=w.align, fp16=True,
-                   flags=ZS_STAGE_AVERAGE if stage else 0)
+                   flags=ZS_STAGE_AVERAGE if stage else 0, grad_buffers=True)
     za.set_stream(stream.cuda_stream)
     S = za.shard_len
     synth.dev_normal_f32(za.master[:S], w.master_key(), w.sigma_master)
     synth.dev_zero_ranges(za.master, pad)
-    grads = []
-    for k, _ in w.grad_keys(0):
-        g = torch.empty(max(S, 8), dtype=torch.float16, device=dev)
+    grads = za.grads
+    for (k, _), g in zip(w.grad_keys(0), grads):
         synth.dev_grad_f16(g[:S], k, w.sigma_grad, init_scale)
         synth.dev_zero_ranges(g, pad)
-        grads.append(g)
     za.amp_init(init_scale)
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
               max_grad_norm=w.max_grad_norm)
@@ -415,11 +413,11 @@ def main():
     w = workload(args.workload)
     t_setup = time.time()
     zs = ZeroShard(w.numel, w.decay, w.world_size, w.rank, w.M, device=dev,
-                   bucket_cap=w.bucket_cap, align=w.align)
+                   bucket_cap=w.bucket_cap, align=w.align, grad_buffers=True)
     segs = zs.segments()
     pad = [(o, n) for o, n, t, _, _ in segs if t < 0]
     special = special_ranges(w, [(o, n, t) for o, n, t, _, _ in segs])
-    case = DeviceCase(w, zs.shard_len, pad, dev, special)
+    case = DeviceCase(w, zs.shard_len, pad, dev, special, grads=zs.grads)
     case.fill_master(zs.master)
     grads = case.fill_grads(0)
     stream = torch.cuda.current_stream(dev)

@@ -66,6 +66,7 @@ _sig("zs_plan_run", ctypes.c_int, _vp, _i64, _P(_i64), _P(_i64), _P(_i32))
 _sig("zs_plan_state_bytes", ctypes.c_int, _vp, _i32, _P(_i64))
 _sig("zs_plan_destroy", None, _vp)
 _sig("zs_workspace_bytes", _sz, _vp, _i32, _u32)
+_sig("zs_slab_layout", ctypes.c_int, _vp, _i32, _u32, _i32, _P(_sz), _P(_sz))
 _sig("zero_shard_init", ctypes.c_int, _P(_vp), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
      _u32)
 _sig("zero_shard_step", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _i64, _f32,
@@ -96,7 +97,7 @@ _sig("zero_offload_destroy", None, _vp)
 
 EXPORTED = ["zs_plan_create", "zs_plan_query", "zs_plan_tensor_slice", "zs_plan_segment",
             "zs_plan_bucket", "zs_plan_run", "zs_plan_state_bytes", "zs_plan_destroy",
-            "zs_workspace_bytes", "zero_shard_init", "zero_shard_step", "zero_shard_grad_sumsq",
+            "zs_workspace_bytes", "zs_slab_layout", "zero_shard_init", "zero_shard_step", "zero_shard_grad_sumsq",
             "zero_shard_step_global_norm", "zero_shard_amp_state_init", "zero_shard_step_amp",
             "zero_shard_export_state", "zero_shard_import_state",
             "zero_shard_params", "zero_shard_set_stream",
@@ -192,6 +193,15 @@ def zs_plan_destroy(plan: int) -> None:
 
 def zs_workspace_bytes(plan: int, M: int, flags: int = 0) -> int:
     return int(_lib.zs_workspace_bytes(plan, M, flags))
+
+
+def zs_slab_layout(plan: int, M: int, flags: int = 0, n_grads: int = 0):
+    """(offsets, slab_bytes): byte offsets of param, master, exp_avg, exp_avg_sq,
+    n_grads gradient buffers and the workspace inside one slab."""
+    offs = (ctypes.c_size_t * (5 + max(0, min(int(n_grads), 16))))()
+    total = ctypes.c_size_t()
+    _check(_lib.zs_slab_layout(plan, M, flags, n_grads, offs, ctypes.byref(total)))
+    return [int(x) for x in offs], int(total.value)
 
 
 # ------------------------------------------------------------------ step
@@ -348,10 +358,18 @@ def zero_offload_destroy(ctx: int) -> None:
 
 
 class ZeroShard:
-    """One rank's shard: plan + torch-allocated device buffers + bound context."""
+    """One rank's shard: plan + torch-allocated device buffers + bound context.
+
+    The param, master, exp_avg, exp_avg_sq arrays and the workspace are views
+    into one device slab placed by zs_slab_layout (array starts staggered by
+    4 KiB past 2 MiB boundaries).  With grad_buffers=True the slab also holds the
+    M gradient contribution buffers, exposed as `grads` (16-bit, shard_len each;
+    the caller fills them before each step)."""
+
+    _PERIOD = 1 << 21
 
     def __init__(self, numel, decay, world_size=1, rank=0, M=1, device=None, bucket_cap=25_000_000,
-                 align=64, flags=0, stream=None, fp16=False):
+                 align=64, flags=0, stream=None, fp16=False, grad_buffers=False):
         import torch
         self.device = torch.device(device if device is not None else "cuda")
         self.M = M
@@ -359,21 +377,32 @@ class ZeroShard:
         q = zs_plan_query(self.plan)
         self.shard_len = q["shard_len"]
         self.n_runs = q["n_runs"]
-        S = max(self.shard_len, 8)
-        dev = self.device
-        self.master = torch.zeros(S, dtype=torch.float32, device=dev)
-        self.exp_avg = torch.zeros(S, dtype=torch.float32, device=dev)
-        self.exp_avg_sq = torch.zeros(S, dtype=torch.float32, device=dev)
         self.fp16 = fp16
         if fp16:
             flags |= ZS_FP16
-        self.param = torch.zeros(S, dtype=torch.float16 if fp16 else torch.bfloat16, device=dev)
-        self.amp_state = None
+        half = torch.float16 if fp16 else torch.bfloat16
+        n_grads = M if grad_buffers else 0
+        offs, total = zs_slab_layout(self.plan, M, flags, n_grads)
         self.ws_bytes = zs_workspace_bytes(self.plan, M, flags)
-        # torch's caching allocator returns 512-byte aligned blocks
-        self.workspace = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        # over-allocate one period so the slab can start on a 2 MiB boundary
+        self.slab = torch.zeros(total + self._PERIOD, dtype=torch.uint8, device=self.device)
+        base = (-self.slab.data_ptr()) % self._PERIOD
+        S = self.shard_len
+
+        def view(off, nbytes, dtype):
+            # an empty shard still gets a few elements: torch gives empty tensors no address
+            nbytes = max(nbytes, 8 * torch.empty(0, dtype=dtype).element_size())
+            return self.slab[base + off:base + off + nbytes].view(dtype)
+
+        self.param = view(offs[0], 2 * S, half)
+        self.master = view(offs[1], 4 * S, torch.float32)
+        self.exp_avg = view(offs[2], 4 * S, torch.float32)
+        self.exp_avg_sq = view(offs[3], 4 * S, torch.float32)
+        self.grads = [view(offs[4 + j], 2 * S, half) for j in range(n_grads)]
+        self.workspace = view(offs[4 + n_grads], self.ws_bytes, torch.uint8)
+        self.amp_state = None
         self._stream = stream
-        s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+        s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
         self.ctx = zero_shard_init(self.plan, M, self.param.data_ptr(), self.master.data_ptr(),
                                    self.exp_avg.data_ptr(), self.exp_avg_sq.data_ptr(),
                                    self.workspace.data_ptr(), self.ws_bytes, s, flags)

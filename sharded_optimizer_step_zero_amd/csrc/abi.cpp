@@ -51,17 +51,19 @@ zs::WorkspaceLayout workspace_layout(int64_t shard_len, int64_t n_runs, int64_t 
   static_assert(sizeof(zs::ClipScalars) <= 64 && sizeof(zs::StepConsts) <= 192,
                 "scalars block overflow");
   zs::WorkspaceLayout l{};
-  l.runs_off = 0;
+  // the staged averages first, so that they start where the workspace starts
+  // (zs_slab_layout staggers that start against the other streamed arrays)
+  l.stage_off = 0;
+  l.stage_bytes = round256((size_t)stage_elems * sizeof(float));
+  l.runs_off = l.stage_bytes;
   l.runs_bytes = (size_t)(n_runs + 1) * sizeof(zs::Run);
-  l.tflags_off = round256(l.runs_bytes);
+  l.tflags_off = l.runs_off + round256(l.runs_bytes);
   l.tflags_bytes = (size_t)zs::tile_flag_words(shard_len, n_runs) * sizeof(uint32_t);
   l.pieces_off = l.tflags_off + round256(l.tflags_bytes);
   l.pieces_bytes = (size_t)n_pieces * sizeof(zs::Piece);
   l.partials_off = l.pieces_off + round256(l.pieces_bytes);
   l.scalars_off = l.partials_off + round256((size_t)n_partials * sizeof(double));
-  l.stage_off = l.scalars_off + 256;
-  l.stage_bytes = round256((size_t)stage_elems * sizeof(float));
-  l.total = l.stage_off + l.stage_bytes;
+  l.total = l.scalars_off + 256;
   return l;
 }
 
@@ -108,11 +110,13 @@ using zs::plan_workspace;
 namespace {
 
 // Resident-wave cap of the step kernels per CU (0: no cap), by M and shard size.
-// Measured on MI355X: caps 7..14 swept for each M on 164M- and 1G-element
-// shards, two rounds on the same buffers (repeatable to 0.3%).  Fewer
-// contributions leave each wave less in flight, so more waves pay off; larger
-// shards favour slightly fewer.  M without a measurement takes its neighbour's
-// cap.  ZS_WAVES_PER_CU overrides the table.
+// Measured on MI355X: caps 7..14 swept for every M on flat 164M-, 1G- and
+// 4.3G-element shards, two rounds on the same buffers (repeatable to 0.3%), and
+// checked on the GPT, Llama and stress layouts.  Fewer contributions leave each
+// wave less in flight, so more waves pay off.  Shards near 1G elements favour
+// slightly fewer waves than both smaller and larger ones; fresh allocations move
+// any of these figures by up to 3%, so only differences seen on the same buffers
+// count.  ZS_WAVES_PER_CU overrides the table.
 int32_t default_waves_per_cu(int32_t M, int64_t shard_len) {
   const char* env = getenv("ZS_WAVES_PER_CU");
   if (env && *env) {
@@ -122,8 +126,10 @@ int32_t default_waves_per_cu(int32_t M, int64_t shard_len) {
   //                                   M: 0   1   2   3   4   5   6   7   8   9  10  11  12  13  14  15  16
   static const int8_t kSmall[ZS_MAX_M + 1] = {0, 12, 12, 11, 11, 11, 11, 10, 10, 10, 10, 9, 9, 9, 8, 8, 8};
   static const int8_t kLarge[ZS_MAX_M + 1] = {0, 11, 11, 11, 10, 10, 10, 9, 9, 9, 9, 9, 9, 8, 8, 7, 7};
+  static const int8_t kHuge[ZS_MAX_M + 1] = {0, 12, 12, 11, 11, 12, 11, 11, 11, 11, 11, 10, 9, 9, 9, 9, 8};
   if (M < 1 || M > ZS_MAX_M) return 0;
-  return shard_len <= (int64_t(1) << 28) ? kSmall[M] : kLarge[M];
+  if (shard_len <= (int64_t(1) << 28)) return kSmall[M];
+  return shard_len <= (int64_t(1) << 31) ? kLarge[M] : kHuge[M];
 }
 
 
@@ -196,6 +202,33 @@ extern "C" size_t zs_workspace_bytes(const zs_plan* plan, int32_t M, uint32_t fl
   (void)M;
   if (!plan) return 0;
   return plan_workspace(plan, flags).total;
+}
+
+extern "C" int zs_slab_layout(const zs_plan* plan, int32_t M, uint32_t flags, int32_t n_grads,
+                              size_t* offsets, size_t* slab_bytes) {
+  if (!plan || !offsets || !slab_bytes) return einval("zs_slab_layout: NULL argument");
+  if (M < 1 || M > ZS_MAX_M) return einval("zs_slab_layout: M must lie in [1, 16]");
+  if (n_grads < 0 || n_grads > M) return einval("zs_slab_layout: n_grads must lie in [0, M]");
+  if (flags & ~(ZS_SKIP_NONFINITE | ZS_FP16 | ZS_STAGE_AVERAGE))
+    return einval("zs_slab_layout: unknown flag");
+  const uint64_t S = (uint64_t)plan->shard_len;
+  if (S > (uint64_t(1) << 56)) return einval("zs_slab_layout: shard too large");
+  constexpr uint64_t kPeriod = uint64_t(1) << 21;  // 2 MiB
+  constexpr uint64_t kStagger = uint64_t(1) << 12;  // 4 KiB
+  const int32_t count = 5 + n_grads;
+  uint64_t pos = 0;
+  for (int32_t i = 0; i < count; i++) {
+    uint64_t bytes;
+    if (i == 0) bytes = 2 * S;                       // param (16-bit)
+    else if (i <= 3) bytes = 4 * S;                  // master, exp_avg, exp_avg_sq
+    else if (i < 4 + n_grads) bytes = 2 * S;         // gradient contributions
+    else bytes = plan_workspace(plan, flags).total;  // workspace (staged averages first)
+    pos = (pos + kPeriod - 1) / kPeriod * kPeriod + (uint64_t)i * kStagger;
+    offsets[i] = (size_t)pos;
+    pos += bytes;
+  }
+  *slab_bytes = (size_t)pos;
+  return ZS_OK;
 }
 
 extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, void* param_bf16,

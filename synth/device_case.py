@@ -37,9 +37,11 @@ class DeviceCase:
 
     special: (offset, length, kind) ranges whose gradient contributions are
     overridden in every contribution ("zero": +0.0; "subnormal": bf16
-    subnormals from their own hash stream)."""
+    subnormals from their own hash stream).  grads: M preallocated bf16 device
+    tensors of at least shard_len elements to fill (default: allocate them)."""
 
-    def __init__(self, w: Workload, shard_len: int, padding_ranges, device, special=()):
+    def __init__(self, w: Workload, shard_len: int, padding_ranges, device, special=(),
+                 grads=None):
         import torch
         self.w = w
         self.S = shard_len
@@ -49,8 +51,14 @@ class DeviceCase:
         self.sub_idx = (np.concatenate([np.arange(o, o + n) for o, n in sub]).astype(np.int64)
                         if sub else np.zeros(0, np.int64))
         self.device = device
-        n = max(shard_len, 8)
-        self.grads = [torch.empty(n, dtype=torch.bfloat16, device=device) for _ in range(w.M)]
+        if grads is not None:
+            if len(grads) != w.M or any(g.numel() < shard_len or g.dtype != torch.bfloat16
+                                        for g in grads):
+                raise ValueError("grads: expected M bf16 tensors of at least shard_len elements")
+            self.grads = list(grads)
+        else:
+            n = max(shard_len, 8)
+            self.grads = [torch.empty(n, dtype=torch.bfloat16, device=device) for _ in range(w.M)]
         self._grads_step = None
 
     # -------------------------------------------------------- device fills

@@ -73,12 +73,16 @@ class Shard:
     def __init__(self, w: Workload, flags=0, device="cuda"):
         self.w = w
         self.lay = L.plan(w.numel, w.decay, w.world_size, w.rank, w.bucket_cap, w.align)
+        # the slab placement bench.py times: state, contributions and workspace in one
+        # allocation, staggered
         self.zs = ZeroShard(w.numel, w.decay, w.world_size, w.rank, w.M, device=device,
-                            bucket_cap=w.bucket_cap, align=w.align, flags=flags)
+                            bucket_cap=w.bucket_cap, align=w.align, flags=flags,
+                            grad_buffers=True)
         assert self.zs.shard_len == self.lay.shard_len
         self.S = self.lay.shard_len
         special = special_ranges(w, [(x.shard_off, x.length, x.tensor) for x in self.lay.segments])
-        self.case = DeviceCase(w, self.S, self.lay.padding_ranges(), self.zs.device, special)
+        self.case = DeviceCase(w, self.S, self.lay.padding_ranges(), self.zs.device, special,
+                               grads=self.zs.grads)
         self.case.fill_master(self.zs.master)
         torch.cuda.synchronize()
 

@@ -1,7 +1,7 @@
 /*
  * abi_check.c -- the C ABI used from plain C with the HIP runtime alone (no
- * Python, no torch): device buffers from hipMalloc, a plan, a context, three
- * steps (the second clipped), checked bit for bit against the CPU oracle
+ * Python, no torch): one hipMalloc'ed slab placed by zs_slab_layout, a plan, a
+ * context, three steps (the second clipped), checked bit for bit against the CPU oracle
  * (oracle/libzo.so, test infrastructure) on the same inputs.  Exit status 0 on
  * agreement.
  */
@@ -85,19 +85,25 @@ int main(void)
         }
     }
 
-    /* device buffers, all owned here */
+    /* device buffers: one slab, owned here, started on a 2 MiB boundary */
     void *d_param, *d_ws, *d_grads[M];
     float *d_master, *d_m, *d_v;
     const size_t ws_bytes = zs_workspace_bytes(plan, M, 0);
-    CHECK_HIP(hipMalloc(&d_param, S * 2));
-    CHECK_HIP(hipMalloc((void **)&d_master, S * 4));
-    CHECK_HIP(hipMalloc((void **)&d_m, S * 4));
-    CHECK_HIP(hipMalloc((void **)&d_v, S * 4));
-    CHECK_HIP(hipMalloc(&d_ws, ws_bytes));
+    size_t offs[5 + M], slab_bytes = 0;
+    CHECK_ZS(zs_slab_layout(plan, M, 0, M, offs, &slab_bytes));
+    const size_t period = (size_t)1 << 21;
+    char *slab = NULL;
+    CHECK_HIP(hipMalloc((void **)&slab, slab_bytes + period));
+    char *base = slab + ((period - (uintptr_t)slab % period) % period);
+    d_param = base + offs[0];
+    d_master = (float *)(base + offs[1]);
+    d_m = (float *)(base + offs[2]);
+    d_v = (float *)(base + offs[3]);
     for (int j = 0; j < M; j++) {
-        CHECK_HIP(hipMalloc(&d_grads[j], S * 2));
+        d_grads[j] = base + offs[4 + j];
         CHECK_HIP(hipMemcpy(d_grads[j], grads[j], S * 2, hipMemcpyHostToDevice));
     }
+    d_ws = base + offs[4 + M];
     CHECK_HIP(hipMemcpy(d_master, master, S * 4, hipMemcpyHostToDevice));
     CHECK_HIP(hipMemset(d_m, 0, S * 4));
     CHECK_HIP(hipMemset(d_v, 0, S * 4));
@@ -152,15 +158,8 @@ int main(void)
     zero_shard_destroy(ctx);
     zs_plan_destroy(plan);
     CHECK_HIP(hipStreamDestroy(stream));
-    for (int j = 0; j < M; j++) {
-        CHECK_HIP(hipFree(d_grads[j]));
-        free(grads[j]);
-    }
-    CHECK_HIP(hipFree(d_param));
-    CHECK_HIP(hipFree(d_master));
-    CHECK_HIP(hipFree(d_m));
-    CHECK_HIP(hipFree(d_v));
-    CHECK_HIP(hipFree(d_ws));
+    for (int j = 0; j < M; j++) free(grads[j]);
+    CHECK_HIP(hipFree(slab));
     free(master), free(m), free(v), free(got_master), free(got_m), free(got_v);
     free(param), free(got_param), free(mask);
     printf("c-abi check ok: S=%lld, M=%d, 3 steps (one clipped), bit-identical to the oracle\n",

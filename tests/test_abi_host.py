@@ -19,7 +19,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 28
+    assert len(names) == 29
     lib = ctypes.CDLL(zs.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -101,3 +101,44 @@ def test_workspace_grows_by_the_staging_area():
         assert zs.zs_workspace_bytes(p, 4, zs.ZS_FP16 | zs.ZS_SKIP_NONFINITE) == base
     finally:
         zs.zs_plan_destroy(p)
+
+
+@pytest.mark.parametrize("numel,N,M,flags,n_grads", [
+    ([1000, 77, 4097], 3, 4, 0, 4), ([1000, 77, 4097], 3, 4, zs.ZS_STAGE_AVERAGE, 0),
+    ([0, 0], 2, 1, 0, 1), ([(1 << 22) + 64], 1, 16, zs.ZS_FP16, 16), ([5000] * 9, 8, 7, 0, 3)])
+def test_slab_layout(numel, N, M, flags, n_grads):
+    """Arrays in order, disjoint, sized for the shard, each starting 4 KiB * i past a
+    2 MiB boundary; the workspace sized as zs_workspace_bytes says."""
+    p = zs.zs_plan_create(numel, [1] * len(numel), N, N - 1)
+    try:
+        S = zs.zs_plan_query(p)["shard_len"]
+        offs, total = zs.zs_slab_layout(p, M, flags, n_grads)
+        sizes = [2 * S] + [4 * S] * 3 + [2 * S] * n_grads + [zs.zs_workspace_bytes(p, M, flags)]
+        assert len(offs) == len(sizes) == 5 + n_grads
+        end = 0
+        for i, (o, n) in enumerate(zip(offs, sizes)):
+            assert o >= end and o % (1 << 21) == i * 4096, (i, o)
+            end = o + n
+        assert total == end
+        if flags & zs.ZS_STAGE_AVERAGE:  # the staged averages open the workspace
+            assert sizes[-1] >= 4 * S
+    finally:
+        zs.zs_plan_destroy(p)
+
+
+def test_slab_layout_argument_errors():
+    p = zs.zs_plan_create([1000], [1], 1, 0)
+    try:
+        for bad in (dict(M=0), dict(M=17), dict(n_grads=5), dict(n_grads=-1), dict(flags=0x80)):
+            a = dict(M=4, flags=0, n_grads=0)
+            a.update(bad)
+            with pytest.raises(zs.ZeroShardError) as e:
+                zs.zs_slab_layout(p, a["M"], a["flags"], a["n_grads"])
+            assert e.value.code == zs.ZS_EINVAL
+    finally:
+        zs.zs_plan_destroy(p)
+    lib = ctypes.CDLL(zs.LIB_PATH)
+    out = (ctypes.c_size_t * 8)()
+    total = ctypes.c_size_t(7)
+    assert lib.zs_slab_layout(None, 4, 0, 0, out, ctypes.byref(total)) == zs.ZS_EINVAL
+    assert total.value == 7
