@@ -438,22 +438,35 @@ def main():
         zs.step(grads, step=s + 1, max_grad_norm=w.max_grad_norm, **hp)
     torch.cuda.synchronize()
 
-    # one event between consecutive steps: the total and the per-step spread
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # the timed steps, bracketed by two events (an event per step would add its own
+    # host cost to every step, which a 1M-parameter step cannot hide)
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    evs[0].record(stream)
+    e_start.record(stream)
     for s in range(args.steps):
         zs.step(grads, step=args.warmup + s + 1, max_grad_norm=w.max_grad_norm, **hp)
-        evs[s + 1].record(stream)
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = evs[0].elapsed_time(evs[-1])
+    gpu_ms = e_start.elapsed_time(e_end)
     ms_per_step = gpu_ms / args.steps
-    per_step = percentiles([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+
+    # the per-step spread, from a second run of up to 50 steps with an event between
+    # consecutive steps
+    n_spread = min(args.steps, 50)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread + 1)]
+    evs[0].record(stream)
+    for s in range(n_spread):
+        zs.step(grads, step=args.warmup + args.steps + s + 1, max_grad_norm=w.max_grad_norm,
+                **hp)
+        evs[s + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = percentiles([evs[i].elapsed_time(evs[i + 1]) for i in range(n_spread)])
 
     cold = None
     if args.cold or w.name.startswith("tiny"):
-        cold = time_cold(zs, grads, w, hp, stream, args.warmup + args.steps + 1,
+        cold = time_cold(zs, grads, w, hp, stream, args.warmup + args.steps + n_spread + 1,
                          max(args.steps // 4, 5))
 
     # the step kernel alone (per-launch average): when clipping, the norm pass is
@@ -519,7 +532,8 @@ def main():
         "cpu_baseline": None,
     }
     if args.graph or w.name.startswith("tiny") or (not args.no_extras and args.workload == 2):
-        out["graph"] = time_graph(zs, grads, w, hp, args.steps, args.warmup + args.steps + 1)
+        out["graph"] = time_graph(zs, grads, w, hp, args.steps,
+                                  args.warmup + args.steps + n_spread + 1)
     # the default run on the GPT shard adds the follow-on paths' legs
     extras = not args.no_extras and args.workload == 2
     if args.checkpoint or extras:
