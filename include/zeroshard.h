@@ -161,7 +161,7 @@ size_t zs_workspace_bytes(const zs_plan *plan, int32_t M, uint32_t flags);
  *
  * A step streams every one of these arrays at the same element index.  When
  * all of them start on 2 MiB boundaries, as separate large allocations do, the
- * step on MI355X measured 0.2% to 7% slower (shard sizes 164M to 6.7G
+ * step on MI355X measured 0.2% to 6% slower (shard sizes 164M to 6.7G
  * elements) than with starts staggered by distinct multiples of 4 KiB.  This
  * helper computes such a staggered placement; using it is optional.
  *
