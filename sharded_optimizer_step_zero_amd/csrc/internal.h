@@ -85,14 +85,15 @@ struct GradPtrs {
   const uint16_t* p[kMaxM];
 };
 
-// Device workspace layout (offsets in bytes from the workspace base).
+// Device workspace layout (offsets in bytes from the workspace base, in this
+// order, each part 256-byte aligned).
 struct WorkspaceLayout {
+  size_t stage_off, stage_bytes;  // shard_len floats with ZS_STAGE_AVERAGE, else empty
   size_t runs_off, runs_bytes;  // n_runs + 1 Run entries (the last is a sentinel)
   size_t tflags_off, tflags_bytes;  // tile_flag_words(shard_len, n_runs) words
   size_t pieces_off, pieces_bytes;  // n_pieces Piece entries
   size_t partials_off;          // sumsq_partials(shard_len) doubles
   size_t scalars_off;           // 256-byte block: ClipScalars, then StepConsts at +64
-  size_t stage_off, stage_bytes;  // shard_len floats with ZS_STAGE_AVERAGE, else empty
   size_t total;
 };
 
