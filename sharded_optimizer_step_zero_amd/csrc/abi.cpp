@@ -117,7 +117,7 @@ namespace {
 // slightly fewer waves than both smaller and larger ones; fresh allocations move
 // any of these figures by up to 3%, so only differences seen on the same buffers
 // count.  ZS_WAVES_PER_CU overrides the table.
-int32_t default_waves_per_cu(int32_t M, int64_t shard_len) {
+int32_t default_waves_per_cu(int32_t M, int64_t shard_len, int32_t n_cu) {
   const char* env = getenv("ZS_WAVES_PER_CU");
   if (env && *env) {
     const long v = strtol(env, nullptr, 10);
@@ -128,8 +128,26 @@ int32_t default_waves_per_cu(int32_t M, int64_t shard_len) {
   static const int8_t kLarge[ZS_MAX_M + 1] = {0, 11, 11, 11, 10, 10, 10, 9, 9, 9, 9, 9, 9, 8, 8, 7, 7};
   static const int8_t kHuge[ZS_MAX_M + 1] = {0, 12, 12, 11, 11, 12, 11, 11, 11, 11, 11, 10, 9, 9, 9, 9, 8};
   if (M < 1 || M > ZS_MAX_M) return 0;
-  if (shard_len <= (int64_t(1) << 28)) return kSmall[M];
-  return shard_len <= (int64_t(1) << 31) ? kLarge[M] : kHuge[M];
+  int32_t cap;
+  if (shard_len <= (int64_t(1) << 28)) cap = kSmall[M];
+  else cap = shard_len <= (int64_t(1) << 31) ? kLarge[M] : kHuge[M];
+  // A grid that up to 16 waves per CU cover in one round runs as one round: at
+  // 1M elements (4,096 tiles) the table's cap leaves a partial second round,
+  // and cap 16 measured 0-14% faster there (M = 1..16); smaller grids keep the
+  // table's cap, which spreads their few waves over more CUs.
+  const int64_t tiles = (shard_len + zs::kStepTileElems - 1) / zs::kStepTileElems;
+  const int64_t one_round = (tiles + n_cu - 1) / n_cu;
+  if (one_round > cap && one_round <= 16) cap = (int32_t)one_round;
+  return cap;
+}
+
+// Compute units of the current device (256 on MI355X if the query fails).
+int32_t device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
 }
 
 
@@ -276,9 +294,10 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   c->n_runs = (int32_t)(table.size() - 1);
   c->n_pieces = (int64_t)plan->pieces.size();
   c->canon_len = plan->total_params;
-  c->waves_per_cu = default_waves_per_cu(M, plan->shard_len);
+  const int32_t n_cu = device_cu_count();
+  c->waves_per_cu = default_waves_per_cu(M, plan->shard_len, n_cu);
   // the staged step reads 16 B of gradient per lane, as many bytes as M = 2
-  c->waves_per_cu_staged = default_waves_per_cu(2, plan->shard_len);
+  c->waves_per_cu_staged = default_waves_per_cu(2, plan->shard_len, n_cu);
   c->param = static_cast<uint16_t*>(param_bf16);
   c->master = master;
   c->m = exp_avg;
