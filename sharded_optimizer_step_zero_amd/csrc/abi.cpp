@@ -111,7 +111,8 @@ namespace {
 
 // Resident-wave cap of the step kernels per CU (0: no cap), by M and shard size.
 // Measured on MI355X: caps 7..14 swept for every M on flat 164M-, 1G- and
-// 4.3G-element shards, two rounds on the same buffers (repeatable to 0.3%), and
+// 4.3G-element shards (the last column in the staggered slab placement of
+// zs_slab_layout), two rounds on the same buffers (repeatable to 0.3%), and
 // checked on the GPT, Llama and stress layouts.  Fewer contributions leave each
 // wave less in flight, so more waves pay off.  Shards near 1G elements favour
 // slightly fewer waves than both smaller and larger ones; fresh allocations move
@@ -126,7 +127,7 @@ int32_t default_waves_per_cu(int32_t M, int64_t shard_len, int32_t n_cu) {
   //                                   M: 0   1   2   3   4   5   6   7   8   9  10  11  12  13  14  15  16
   static const int8_t kSmall[ZS_MAX_M + 1] = {0, 12, 12, 11, 11, 11, 11, 10, 10, 10, 10, 9, 9, 9, 8, 8, 8};
   static const int8_t kLarge[ZS_MAX_M + 1] = {0, 11, 11, 11, 10, 10, 10, 9, 9, 9, 9, 9, 9, 8, 8, 7, 7};
-  static const int8_t kHuge[ZS_MAX_M + 1] = {0, 12, 12, 11, 11, 12, 11, 11, 11, 11, 11, 10, 9, 9, 9, 9, 8};
+  static const int8_t kHuge[ZS_MAX_M + 1] = {0, 12, 11, 12, 10, 10, 9, 9, 9, 9, 9, 9, 9, 7, 7, 7, 7};
   if (M < 1 || M > ZS_MAX_M) return 0;
   int32_t cap;
   if (shard_len <= (int64_t(1) << 28)) cap = kSmall[M];
