@@ -281,6 +281,31 @@ int zero_shard_step_amp(zs_ctx *ctx, const void *const *grads, float lr, float b
                         zs_amp_state *state_dev, float growth_factor, float backoff_factor,
                         int32_t growth_interval, double *grad_norm_out);
 
+/*
+ * Multi-rank loss-scaled step.  With N > 1 every rank must take the same
+ * skip decision, clip coefficient and scaler update, so they come from the sum
+ * of g^2 over all shards: the norm over the whole model that clipping uses
+ * (CS324 notes §7.4) and the overflow check of the scaler (CS324 notes §13).
+ *
+ * Part 1 enqueues sum_i g_i^2 (fp64, g unscaled with the scale in *state_dev;
+ * NaN or Inf when some g is) of this shard into *sumsq_dev (an 8-byte-aligned
+ * device double); with ZS_STAGE_AVERAGE it also stages the averages for part 2.
+ * The caller sums these values over the ranks (a scalar all-reduce) and passes
+ * the global sum to part 2, which runs zero_shard_step_amp's decision, scaler
+ * update and step from it.  Each rank keeps its own copy of the scaler state;
+ * the copies stay equal because every rank applies the same global value.  An
+ * empty shard still takes part in both parts (part 1 writes 0).  Part 2 uses
+ * the same grads as part 1 (or, with ZS_STAGE_AVERAGE, what part 1 staged).
+ * Never waits.  Errors: ZS_EINVAL, ZS_ESTATE (context without ZS_FP16), ZS_EHIP.
+ */
+int zero_shard_grad_sumsq_amp(zs_ctx *ctx, const void *const *grads,
+                              const zs_amp_state *state_dev, double *sumsq_dev);
+int zero_shard_step_amp_global_norm(zs_ctx *ctx, const void *const *grads, float lr,
+                                    float beta1, float beta2, float eps, float weight_decay,
+                                    float max_grad_norm, zs_amp_state *state_dev,
+                                    float growth_factor, float backoff_factor,
+                                    int32_t growth_interval, const double *global_sumsq_dev);
+
 /* ------------------------------------------- the step on host cores (offload) */
 
 /*

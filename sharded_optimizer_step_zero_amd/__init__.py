@@ -77,6 +77,9 @@ _sig("zero_shard_step_global_norm", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f
 _sig("zero_shard_amp_state_init", ctypes.c_int, _vp, _vp, _f32)
 _sig("zero_shard_step_amp", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _f32, _vp, _f32,
      _f32, _i32, _P(_f64))
+_sig("zero_shard_grad_sumsq_amp", ctypes.c_int, _vp, _vp, _vp, _vp)
+_sig("zero_shard_step_amp_global_norm", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _f32,
+     _vp, _f32, _f32, _i32, _vp)
 _sig("zero_shard_export_state", ctypes.c_int, _vp, _vp, _vp, _vp)
 _sig("zero_shard_import_state", ctypes.c_int, _vp, _vp, _vp, _vp)
 _sig("zero_shard_params", ctypes.c_int, _vp, _P(_vp), _P(_i64))
@@ -99,6 +102,7 @@ EXPORTED = ["zs_plan_create", "zs_plan_query", "zs_plan_tensor_slice", "zs_plan_
             "zs_plan_bucket", "zs_plan_run", "zs_plan_state_bytes", "zs_plan_destroy",
             "zs_workspace_bytes", "zs_slab_layout", "zero_shard_init", "zero_shard_step", "zero_shard_grad_sumsq",
             "zero_shard_step_global_norm", "zero_shard_amp_state_init", "zero_shard_step_amp",
+            "zero_shard_grad_sumsq_amp", "zero_shard_step_amp_global_norm",
             "zero_shard_export_state", "zero_shard_import_state",
             "zero_shard_params", "zero_shard_set_stream",
             "zero_shard_destroy", "zero_shard_last_error", "zs_host_adamw",
@@ -261,6 +265,26 @@ def zero_shard_step_amp(ctx: int, grads: Sequence[int], lr: float, beta1: float,
                                          ctypes.byref(nrm) if want_norm else None))
     norm = nrm.value if want_norm else None
     return (rc, norm) if return_code else norm
+
+
+def zero_shard_grad_sumsq_amp(ctx: int, grads: Sequence[int], state_dev: int,
+                              sumsq_dev: int) -> None:
+    """Multi-rank loss-scaled step, part 1: this shard's sum of squares of the
+    unscaled average into the device double at sumsq_dev."""
+    _check(_lib.zero_shard_grad_sumsq_amp(ctx, _ptr_array(grads), state_dev, sumsq_dev))
+
+
+def zero_shard_step_amp_global_norm(ctx: int, grads: Sequence[int], lr: float, beta1: float,
+                                    beta2: float, eps: float, weight_decay: float,
+                                    max_grad_norm: float, state_dev: int,
+                                    growth_factor: float = 2.0, backoff_factor: float = 0.5,
+                                    growth_interval: int = 2000,
+                                    global_sumsq_dev: int = 0) -> None:
+    """Part 2: the loss-scaled step decided by the global sum of squares."""
+    _check(_lib.zero_shard_step_amp_global_norm(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
+                                                weight_decay, max_grad_norm, state_dev,
+                                                growth_factor, backoff_factor, growth_interval,
+                                                global_sumsq_dev))
 
 
 def zero_shard_export_state(ctx: int, canon_master: int, canon_exp_avg: int,

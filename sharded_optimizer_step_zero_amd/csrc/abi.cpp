@@ -470,67 +470,137 @@ extern "C" int zero_shard_amp_state_init(zs_ctx* ctx, zs_amp_state* state_dev, f
   return e == hipSuccess ? ZS_OK : ehip("zero_shard_amp_state_init", e);
 }
 
-extern "C" int zero_shard_step_amp(zs_ctx* ctx, const void* const* grads, float lr, float beta1,
-                                   float beta2, float eps, float weight_decay,
-                                   float max_grad_norm, zs_amp_state* state_dev,
-                                   float growth_factor, float backoff_factor,
-                                   int32_t growth_interval, double* grad_norm_out) {
-  if (!ctx) return einval("zero_shard_step_amp: ctx is NULL");
-  if (!ctx->fp16) return estate("zero_shard_step_amp: needs a context created with ZS_FP16");
+namespace {
+
+// Argument checks of the loss-scaled steps; fills the finalize parameters.
+int amp_args(const zs_ctx* ctx, const char* who, float lr, float beta1, float beta2, float eps,
+             float weight_decay, float max_grad_norm, const zs_amp_state* state_dev,
+             float growth_factor, float backoff_factor, int32_t growth_interval,
+             zs::AmpParams* p) {
+  const std::string w(who);
+  if (!ctx) return einval((w + ": ctx is NULL").c_str());
+  if (!ctx->fp16) return estate((w + ": needs a context created with ZS_FP16").c_str());
   int rc = check_hparams(lr, beta1, beta2, eps, weight_decay, 1);
   if (rc) return rc;
   if (isnan(max_grad_norm) || isinf(max_grad_norm))
-    return einval("zero_shard_step_amp: max_grad_norm must be finite");
+    return einval((w + ": max_grad_norm must be finite").c_str());
   if (!state_dev || ((uintptr_t)state_dev & 15u))
-    return einval("zero_shard_step_amp: state_dev must be a 16-byte-aligned device pointer");
+    return einval((w + ": state_dev must be a 16-byte-aligned device pointer").c_str());
   if (!(growth_factor >= 1.0f) || isinf(growth_factor) || !(backoff_factor > 0.0f) ||
       !(backoff_factor <= 1.0f) || growth_interval < 1)
-    return einval("zero_shard_step_amp: need growth >= 1, 0 < backoff <= 1, interval >= 1");
-  zs::GradPtrs g;
-  if ((rc = gather_grads(ctx, grads, &g))) return rc;
-  if (ctx->shard_len == 0) {
-    if (grad_norm_out) *grad_norm_out = 0.0;
-    return ZS_OK;
+    return einval((w + ": need growth >= 1, 0 < backoff <= 1, interval >= 1").c_str());
+  p->lr = lr;
+  p->beta1 = beta1;
+  p->beta2 = beta2;
+  p->eps = eps;
+  p->weight_decay = weight_decay;
+  p->max_norm = max_grad_norm;
+  p->growth = growth_factor;
+  p->backoff = backoff_factor;
+  p->interval = growth_interval;
+  p->clip = max_grad_norm > 0.0f ? 1 : 0;
+  return ZS_OK;
+}
+
+// The rest of a loss-scaled step once the norm pass has run (or, with
+// external, once the global sum of squares is known): the finalize (skip,
+// clip coefficient, scaler update, step constants) and the step kernel.  An
+// empty shard still runs the finalize, so its scaler advances like the others.
+int amp_finish(zs_ctx* ctx, const zs::GradPtrs& g, zs::AmpState* st, const zs::AmpParams& p,
+               const double* external, double* grad_norm_out, const char* who) {
+  const std::string w(who);
+  const int32_t n_final = ctx->shard_len ? zs::final_partials(ctx->shard_len) : 0;
+  hipError_t e = zs::launch_amp_finalize(final_partials(ctx), n_final, external, st, p,
+                                         scalars(ctx), device_consts(ctx), ctx->stream);
+  if (e != hipSuccess) return ehip((w + ": finalize").c_str(), e);
+  if (ctx->shard_len > 0) {
+    if (ctx->stage)
+      e = zs::launch_step_staged(true, stage_area(ctx), ctx->master, ctx->m, ctx->v, ctx->param,
+                                 ctx->shard_len, run_table(ctx), scalars(ctx),
+                                 zs::StepConsts{}, device_consts(ctx),
+                                 ctx->waves_per_cu_staged, ctx->stream);
+    else
+      e = zs::launch_step_f16(ctx->M, g, ctx->master, ctx->m, ctx->v, ctx->param,
+                              ctx->shard_len, run_table(ctx), scalars(ctx), device_consts(ctx),
+                              ctx->waves_per_cu, ctx->stream);
+    if (e != hipSuccess) return ehip((w + ": step kernel").c_str(), e);
   }
-  zs::AmpState* st = reinterpret_cast<zs::AmpState*>(state_dev);
-  zs::AmpParams p;
-  p.lr = lr;
-  p.beta1 = beta1;
-  p.beta2 = beta2;
-  p.eps = eps;
-  p.weight_decay = weight_decay;
-  p.max_norm = max_grad_norm;
-  p.growth = growth_factor;
-  p.backoff = backoff_factor;
-  p.interval = growth_interval;
-  p.clip = max_grad_norm > 0.0f ? 1 : 0;
-  float* stage = stage_area(ctx);
-  hipError_t e =
-      zs::launch_sumsq_f16(ctx->M, g, ctx->shard_len, partials(ctx), st, stage, ctx->stream);
-  if (e != hipSuccess) return ehip("zero_shard_step_amp: norm pass", e);
-  e = zs::launch_amp_finalize(final_partials(ctx), zs::final_partials(ctx->shard_len), st, p,
-                              scalars(ctx), device_consts(ctx), ctx->stream);
-  if (e != hipSuccess) return ehip("zero_shard_step_amp: finalize", e);
-  if (stage)
-    e = zs::launch_step_staged(true, stage, ctx->master, ctx->m, ctx->v, ctx->param,
-                               ctx->shard_len, run_table(ctx), scalars(ctx),
-                               zs::StepConsts{}, device_consts(ctx), ctx->waves_per_cu_staged,
-                               ctx->stream);
-  else
-    e = zs::launch_step_f16(ctx->M, g, ctx->master, ctx->m, ctx->v, ctx->param, ctx->shard_len,
-                            run_table(ctx), scalars(ctx), device_consts(ctx),
-                            ctx->waves_per_cu, ctx->stream);
-  if (e != hipSuccess) return ehip("zero_shard_step_amp: step kernel", e);
   if (grad_norm_out) {
     double norm = 0.0;
     e = hipMemcpyAsync(&norm, &scalars(ctx)->norm, sizeof(double), hipMemcpyDeviceToHost,
                        ctx->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
-    if (e != hipSuccess) return ehip("zero_shard_step_amp: reading the norm", e);
+    if (e != hipSuccess) return ehip((w + ": reading the norm").c_str(), e);
     *grad_norm_out = norm;
     if (!isfinite(norm)) return ZS_NONFINITE;
   }
   return ZS_OK;
+}
+
+}  // namespace
+
+extern "C" int zero_shard_step_amp(zs_ctx* ctx, const void* const* grads, float lr, float beta1,
+                                   float beta2, float eps, float weight_decay,
+                                   float max_grad_norm, zs_amp_state* state_dev,
+                                   float growth_factor, float backoff_factor,
+                                   int32_t growth_interval, double* grad_norm_out) {
+  const char* who = "zero_shard_step_amp";
+  zs::AmpParams p;
+  int rc = amp_args(ctx, who, lr, beta1, beta2, eps, weight_decay, max_grad_norm, state_dev,
+                    growth_factor, backoff_factor, growth_interval, &p);
+  if (rc) return rc;
+  zs::GradPtrs g;
+  if ((rc = gather_grads(ctx, grads, &g))) return rc;
+  zs::AmpState* st = reinterpret_cast<zs::AmpState*>(state_dev);
+  if (ctx->shard_len > 0) {
+    const hipError_t e = zs::launch_sumsq_f16(ctx->M, g, ctx->shard_len, partials(ctx), st,
+                                              stage_area(ctx), ctx->stream);
+    if (e != hipSuccess) return ehip("zero_shard_step_amp: norm pass", e);
+  }
+  return amp_finish(ctx, g, st, p, nullptr, grad_norm_out, who);
+}
+
+extern "C" int zero_shard_grad_sumsq_amp(zs_ctx* ctx, const void* const* grads,
+                                         const zs_amp_state* state_dev, double* sumsq_dev) {
+  if (!ctx) return einval("zero_shard_grad_sumsq_amp: ctx is NULL");
+  if (!ctx->fp16)
+    return estate("zero_shard_grad_sumsq_amp: needs a context created with ZS_FP16");
+  if (!state_dev || ((uintptr_t)state_dev & 15u))
+    return einval("zero_shard_grad_sumsq_amp: state_dev must be a 16-byte-aligned device pointer");
+  if (!sumsq_dev || ((uintptr_t)sumsq_dev & 7u))
+    return einval("zero_shard_grad_sumsq_amp: sumsq_dev must be an 8-byte-aligned device pointer");
+  zs::GradPtrs g;
+  int rc = gather_grads(ctx, grads, &g);
+  if (rc) return rc;
+  const int32_t n_final = ctx->shard_len ? zs::final_partials(ctx->shard_len) : 0;
+  hipError_t e = hipSuccess;
+  if (n_final)
+    e = zs::launch_sumsq_f16(ctx->M, g, ctx->shard_len, partials(ctx),
+                             reinterpret_cast<const zs::AmpState*>(state_dev), stage_area(ctx),
+                             ctx->stream);
+  if (e == hipSuccess)
+    e = zs::launch_sumsq_total(final_partials(ctx), n_final, sumsq_dev, ctx->stream);
+  return e == hipSuccess ? ZS_OK : ehip("zero_shard_grad_sumsq_amp", e);
+}
+
+extern "C" int zero_shard_step_amp_global_norm(zs_ctx* ctx, const void* const* grads, float lr,
+                                               float beta1, float beta2, float eps,
+                                               float weight_decay, float max_grad_norm,
+                                               zs_amp_state* state_dev, float growth_factor,
+                                               float backoff_factor, int32_t growth_interval,
+                                               const double* global_sumsq_dev) {
+  const char* who = "zero_shard_step_amp_global_norm";
+  zs::AmpParams p;
+  int rc = amp_args(ctx, who, lr, beta1, beta2, eps, weight_decay, max_grad_norm, state_dev,
+                    growth_factor, backoff_factor, growth_interval, &p);
+  if (rc) return rc;
+  if (!global_sumsq_dev || ((uintptr_t)global_sumsq_dev & 7u))
+    return einval(
+        "zero_shard_step_amp_global_norm: global_sumsq_dev must be an aligned device pointer");
+  zs::GradPtrs g;
+  if ((rc = gather_grads(ctx, grads, &g))) return rc;
+  return amp_finish(ctx, g, reinterpret_cast<zs::AmpState*>(state_dev), p, global_sumsq_dev,
+                    nullptr, who);
 }
 
 extern "C" int zero_shard_params(zs_ctx* ctx, const void** param_bf16, int64_t* shard_len) {

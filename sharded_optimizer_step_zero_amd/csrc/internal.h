@@ -164,9 +164,10 @@ hipError_t launch_sumsq_total(const double* partials, int32_t n_partials, double
 // scaler, the step kernel, and the scaler initialisation.
 hipError_t launch_sumsq_f16(int M, const GradPtrs& g, int64_t shard_len, double* partials,
                             const AmpState* st, float* stage, hipStream_t stream);
-hipError_t launch_amp_finalize(const double* partials, int32_t n_partials, AmpState* st,
-                               const AmpParams& p, ClipScalars* out, StepConsts* kout,
-                               hipStream_t stream);
+// external (nullable): a global sum of squares used instead of the partials.
+hipError_t launch_amp_finalize(const double* partials, int32_t n_partials,
+                               const double* external, AmpState* st, const AmpParams& p,
+                               ClipScalars* out, StepConsts* kout, hipStream_t stream);
 hipError_t launch_step_f16(int M, const GradPtrs& g, float* master, float* m, float* v,
                            uint16_t* param, int64_t shard_len, const RunTable& rt,
                            const ClipScalars* clip, const StepConsts* k, int32_t waves_per_cu,

@@ -443,11 +443,15 @@ __global__ __launch_bounds__(kThreads) void sumsq_f16_kernel(GradPtrs g, int64_t
   if (threadIdx.x == 0) partials[blockIdx.x] = t;
 }
 
+// external (nullable): the global sum of squares over every rank's shard, which
+// then replaces this shard's partials (the multi-rank split of the step).
 __global__ __launch_bounds__(kThreads) void amp_finalize_kernel(
-    const double* __restrict__ partials, int32_t n, AmpState* __restrict__ st, AmpParams p,
-    ClipScalars* __restrict__ out, StepConsts* __restrict__ kout) {
-  const double total = sum_partials(partials, n);
+    const double* __restrict__ partials, int32_t n, const double* __restrict__ external,
+    AmpState* __restrict__ st, AmpParams p, ClipScalars* __restrict__ out,
+    StepConsts* __restrict__ kout) {
+  const double part = external ? 0.0 : sum_partials(partials, n);
   if (threadIdx.x != 0) return;
+  const double total = external ? *external : part;
   AmpState s = *st;
   const bool found_inf = !__builtin_isfinite(total);
   const double norm = __builtin_sqrt(total);
@@ -747,11 +751,11 @@ hipError_t launch_sumsq_f16(int M, const GradPtrs& g, int64_t shard_len, double*
 #undef ZS_CALL_SUMSQ16
 }
 
-hipError_t launch_amp_finalize(const double* partials, int32_t n_partials, AmpState* st,
-                               const AmpParams& p, ClipScalars* out, StepConsts* kout,
-                               hipStream_t stream) {
+hipError_t launch_amp_finalize(const double* partials, int32_t n_partials,
+                               const double* external, AmpState* st, const AmpParams& p,
+                               ClipScalars* out, StepConsts* kout, hipStream_t stream) {
   hipLaunchKernelGGL(amp_finalize_kernel, dim3(1), dim3(kThreads), 0, stream, partials,
-                     n_partials, st, p, out, kout);
+                     n_partials, external, st, p, out, kout);
   return hipGetLastError();
 }
 

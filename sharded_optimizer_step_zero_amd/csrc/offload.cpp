@@ -393,8 +393,8 @@ extern "C" int zero_offload_step_amp(zs_offload* c, const void* const* grads, fl
   // step constants at t = applied + 1, all on the device
   hipError_t e = zs::launch_sumsq_f16(c->M, g, S, partials, st, stage, c->stream);
   if (e == hipSuccess)
-    e = zs::launch_amp_finalize(partials + zs::level1_partials(S), zs::final_partials(S), st, p,
-                                reinterpret_cast<zs::ClipScalars*>(block),
+    e = zs::launch_amp_finalize(partials + zs::level1_partials(S), zs::final_partials(S),
+                                nullptr, st, p, reinterpret_cast<zs::ClipScalars*>(block),
                                 reinterpret_cast<zs::StepConsts*>(block + 64), c->stream);
   if (e != hipSuccess) return zs::ehip("zero_offload_step_amp: norm pass", e);
   return pipeline(c, nullptr, true, grad_norm_out, "zero_offload_step_amp");

@@ -19,7 +19,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 29
+    assert len(names) == 31
     lib = ctypes.CDLL(zs.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -77,6 +77,13 @@ def test_init_and_step_argument_errors_before_any_device_call():
         assert e.value.code == zs.ZS_EINVAL and "workspace" in str(e.value)
         with pytest.raises(zs.ZeroShardError):
             zs.zero_shard_step(0, [16] * 4, 1e-3, 0.9, 0.95, 1e-8, 0.1, 1)
+        for call in (lambda: zs.zero_shard_grad_sumsq_amp(0, [16] * 4, 16, 16),
+                     lambda: zs.zero_shard_step_amp_global_norm(0, [16] * 4, 1e-3, 0.9, 0.95,
+                                                                1e-8, 0.1, 1.0, 16,
+                                                                global_sumsq_dev=16)):
+            with pytest.raises(zs.ZeroShardError) as e:
+                call()
+            assert e.value.code == zs.ZS_EINVAL and "ctx is NULL" in str(e.value)
     finally:
         zs.zs_plan_destroy(p)
     assert zs.zero_shard_last_error()

@@ -132,11 +132,34 @@ def test_amp_rejects_wrong_context():
     with pytest.raises(zsm.ZeroShardError) as e:
         z.step_amp([torch.zeros(1000, dtype=torch.int16, device="cuda")], **HP)
     assert e.value.code == zsm.ZS_ESTATE
+    gt = torch.zeros(1024, dtype=torch.int16, device="cuda")
+    g = [gt.data_ptr()]
+    d = torch.zeros(2, dtype=torch.float64, device="cuda")
+    for call in (lambda: zsm.zero_shard_grad_sumsq_amp(z.ctx, g, z.amp_state.data_ptr(),
+                                                       d.data_ptr()),
+                 lambda: zsm.zero_shard_step_amp_global_norm(
+                     z.ctx, g, max_grad_norm=1.0, state_dev=z.amp_state.data_ptr(),
+                     global_sumsq_dev=d.data_ptr(), **HP)):
+        with pytest.raises(zsm.ZeroShardError) as e:
+            call()
+        assert e.value.code == zsm.ZS_ESTATE
     z.close()
     y = ZeroShard([1000], [1], 1, 0, 1, fp16=True)
     with pytest.raises(zsm.ZeroShardError) as e:
         y.step([torch.zeros(1000, dtype=torch.int16, device="cuda")], step=1, **HP)
     assert e.value.code == zsm.ZS_ESTATE
+    y.amp_init(1024.0)
+    st = y.amp_state.data_ptr()
+    for bad in (dict(state_dev=st + 8, global_sumsq_dev=d.data_ptr()),      # state alignment
+                dict(state_dev=st, global_sumsq_dev=d.data_ptr() + 4),      # sumsq alignment
+                dict(state_dev=st, global_sumsq_dev=0)):                    # NULL
+        with pytest.raises(zsm.ZeroShardError) as e:
+            zsm.zero_shard_step_amp_global_norm(y.ctx, g, max_grad_norm=1.0, **bad, **HP)
+        assert e.value.code == zsm.ZS_EINVAL
+    with pytest.raises(zsm.ZeroShardError) as e:
+        zsm.zero_shard_grad_sumsq_amp(y.ctx, g, st, d.data_ptr() + 4)
+    assert e.value.code == zsm.ZS_EINVAL
+    assert y.amp_read() == (1024.0, 0, 0)       # rejected calls changed nothing
     y.close()
 
 
@@ -176,4 +199,28 @@ def test_gpt13b_shard_amp_full(stage):
         assert z.amp_read() == (float(sc.scale[0]), int(sc.tracker[0]), sc.applied)
         del dev
         log(f"  step {s + 1}: {'skipped' if fi else 'applied'}, bit-exact over {S:,} elements")
+    z.close()
+
+
+def test_amp_empty_shard_keeps_the_scaler_in_step():
+    """A rank whose shard is empty still advances its scaler like every other
+    rank: the norm of nothing is 0 (finite), and a global value decides the
+    multi-rank split."""
+    log("test_amp_empty_shard_keeps_the_scaler_in_step")
+    z = ZeroShard([0, 0], [1, 1], 2, 1, 2, fp16=True)
+    assert z.shard_len == 0
+    z.amp_init(1024.0)
+    g = torch.zeros(8, dtype=torch.int16, device="cuda")
+    for _ in range(2):
+        assert z.step_amp([g, g], growth_interval=2, want_norm=True, **HP) == 0.0
+    assert z.amp_read() == (2048.0, 0, 2)
+    d = torch.full((1,), 7.0, dtype=torch.float64, device="cuda")
+    zsm.zero_shard_grad_sumsq_amp(z.ctx, [g.data_ptr()] * 2, z.amp_state.data_ptr(), d.data_ptr())
+    assert d.item() == 0.0
+    for total, want in ((4.0, (2048.0, 1, 3)), (float("inf"), (1024.0, 0, 3))):
+        d.fill_(total)
+        zsm.zero_shard_step_amp_global_norm(z.ctx, [g.data_ptr()] * 2, max_grad_norm=1.0,
+                                            state_dev=z.amp_state.data_ptr(), growth_interval=2,
+                                            global_sumsq_dev=d.data_ptr(), **HP)
+        assert z.amp_read() == want
     z.close()
