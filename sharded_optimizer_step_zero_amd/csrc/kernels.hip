@@ -52,7 +52,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;  // 4 wave64s per workgroup (norm pass)
-constexpr int kVec = 8;        // elements per lane in the norm pass (one dwordx4 of bf16)
+constexpr int kVec = 8;        // elements per lane in the norm pass (two groups of 4)
 constexpr int64_t kNormTile = (int64_t)kThreads * kVec;
 constexpr int64_t kLevel2 = 8192;  // level-1 partials summed by one level-2 workgroup
 
@@ -79,31 +79,6 @@ __device__ __forceinline__ float h2f(uint32_t bits) {
 }
 __device__ __forceinline__ uint32_t f2h(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
-}
-
-__device__ __forceinline__ void unpack(const u32x4 w, float s[kVec]) {
-  s[0] = bf16_lo(w.x); s[1] = bf16_hi(w.x);
-  s[2] = bf16_lo(w.y); s[3] = bf16_hi(w.y);
-  s[4] = bf16_lo(w.z); s[5] = bf16_hi(w.z);
-  s[6] = bf16_lo(w.w); s[7] = bf16_hi(w.w);
-}
-
-// The M-way reduce of 8 consecutive elements starting at e, divided by M.
-template <int M>
-__device__ __forceinline__ void reduce8(const GradPtrs& g, int64_t e, float s[kVec]) {
-  u32x4 w[M];
-#pragma unroll
-  for (int j = 0; j < M; j++) w[j] = ld_stream(reinterpret_cast<const u32x4*>(g.p[j] + e));
-  unpack(w[0], s);
-#pragma unroll
-  for (int j = 1; j < M; j++) {
-    float t[kVec];
-    unpack(w[j], t);
-#pragma unroll
-    for (int q = 0; q < kVec; q++) s[q] = s[q] + t[q];
-  }
-#pragma unroll
-  for (int q = 0; q < kVec; q++) s[q] = s[q] / (float)M;
 }
 
 __device__ __forceinline__ void adamw(float g, float& p, float& m, float& v, const StepConsts& k,
@@ -134,16 +109,6 @@ __device__ __forceinline__ int32_t find_run(const Run* __restrict__ runs, int32_
     if (runs[mid].start <= e) lo = mid; else hi = mid - 1;
   }
   return lo;
-}
-
-// Eight consecutive fp32 values as two 16-byte non-temporal stores (p is
-// 32-byte aligned: a multiple-of-8 element offset into a 256-byte-aligned array).
-__device__ __forceinline__ void store8(float* p, const float (&s)[8]) {
-  f32x4 a, b;
-  a[0] = s[0]; a[1] = s[1]; a[2] = s[2]; a[3] = s[3];
-  b[0] = s[4]; b[1] = s[5]; b[2] = s[6]; b[3] = s[7];
-  __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p));
-  __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p + 4));
 }
 
 // Decay flag (0 or 1) of element e of the tile starting at tile0 (tile index
@@ -244,24 +209,54 @@ __device__ __forceinline__ double block_sum(double x) {
 }
 
 // Norm pass, level 1: one 2048-element tile per workgroup (in-order, short-lived
-// workgroups stream best); each lane squares its 8 averaged values in fp64 (the
-// square of an fp32 value is exact in fp64), the workgroup sums in a fixed order.
-// With STAGE it also stores the 8 averages to stage[e..e+8) for the staged step.
+// workgroups stream best).  Lane t takes elements [4t, 4t+4) and [1024+4t,
+// 1024+4t+4) of the tile, so each load and store instruction of the wave covers
+// one contiguous stretch (8-byte loads of 16-bit values, 16-byte stores of fp32;
+// measured 3.5-4% faster than 8 consecutive elements per lane).  It squares its
+// 8 averaged values in fp64 (the square of an fp32 value is exact in fp64), in
+// that order, and the workgroup sums in a fixed order.  With STAGE it also
+// stores the averages for the staged step.
 template <int M, bool STAGE>
 __global__ __launch_bounds__(kThreads) void sumsq_kernel(GradPtrs g, int64_t n,
                                                          double* __restrict__ partials,
                                                          float* __restrict__ stage) {
-  const int64_t e = (int64_t)blockIdx.x * kNormTile + (int64_t)threadIdx.x * kVec;
-  double acc = 0.0;
-  if (e < n) {  // n is a multiple of 8
-    float s[kVec];
-    reduce8<M>(g, e, s);
+  const int64_t base = (int64_t)blockIdx.x * kNormTile + (int64_t)threadIdx.x * 4;
+  // every load of both halves first: a staged store must not hold the second
+  // half's loads back (the compiler cannot tell stage from the contributions)
+  bool in[2];
+  u32x2 w[2][M];
 #pragma unroll
-    for (int q = 0; q < kVec; q++) {
+  for (int h = 0; h < 2; h++) {
+    const int64_t e = base + h * (kNormTile / 2);
+    in[h] = e < n;  // n is a multiple of 8: 4-element groups are all in or all out
+    if (in[h]) {
+#pragma unroll
+      for (int j = 0; j < M; j++) w[h][j] = ld_stream(reinterpret_cast<const u32x2*>(g.p[j] + e));
+    }
+  }
+  double acc = 0.0;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    if (!in[h]) continue;
+    float s[4];
+    s[0] = bf16_lo(w[h][0].x); s[1] = bf16_hi(w[h][0].x);
+    s[2] = bf16_lo(w[h][0].y); s[3] = bf16_hi(w[h][0].y);
+#pragma unroll
+    for (int j = 1; j < M; j++) {
+      s[0] = s[0] + bf16_lo(w[h][j].x); s[1] = s[1] + bf16_hi(w[h][j].x);
+      s[2] = s[2] + bf16_lo(w[h][j].y); s[3] = s[3] + bf16_hi(w[h][j].y);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      s[q] = s[q] / (float)M;
       const double x = (double)s[q];
       acc = acc + x * x;
     }
-    if (STAGE) store8(stage + e, s);
+    if (STAGE) {
+      f32x4 a;
+      a[0] = s[0]; a[1] = s[1]; a[2] = s[2]; a[3] = s[3];
+      __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(stage + base + h * (kNormTile / 2)));
+    }
   }
   const double t = block_sum(acc);
   if (threadIdx.x == 0) partials[blockIdx.x] = t;
@@ -411,33 +406,41 @@ __global__ __launch_bounds__(kThreads) void sumsq_f16_kernel(GradPtrs g, int64_t
                                                              const AmpState* __restrict__ st,
                                                              float* __restrict__ stage) {
   const float inv = (float)(1.0 / (double)st->scale);
-  const int64_t e = (int64_t)blockIdx.x * kNormTile + (int64_t)threadIdx.x * kVec;
-  double acc = 0.0;
-  if (e < n) {
-    u32x4 w[M];
+  const int64_t base = (int64_t)blockIdx.x * kNormTile + (int64_t)threadIdx.x * 4;
+  bool in[2];
+  u32x2 w[2][M];
 #pragma unroll
-    for (int j = 0; j < M; j++) w[j] = ld_stream(reinterpret_cast<const u32x4*>(g.p[j] + e));
-    float s[kVec];
+  for (int h = 0; h < 2; h++) {
+    const int64_t e = base + h * (kNormTile / 2);
+    in[h] = e < n;
+    if (in[h]) {
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-      s[2 * q] = h2f(w[0][q]);
-      s[2 * q + 1] = h2f(w[0][q] >> 16);
+      for (int j = 0; j < M; j++) w[h][j] = ld_stream(reinterpret_cast<const u32x2*>(g.p[j] + e));
     }
+  }
+  double acc = 0.0;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    if (!in[h]) continue;
+    float s[4];
+    s[0] = h2f(w[h][0].x); s[1] = h2f(w[h][0].x >> 16);
+    s[2] = h2f(w[h][0].y); s[3] = h2f(w[h][0].y >> 16);
 #pragma unroll
     for (int j = 1; j < M; j++) {
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        s[2 * q] = s[2 * q] + h2f(w[j][q]);
-        s[2 * q + 1] = s[2 * q + 1] + h2f(w[j][q] >> 16);
-      }
+      s[0] = s[0] + h2f(w[h][j].x); s[1] = s[1] + h2f(w[h][j].x >> 16);
+      s[2] = s[2] + h2f(w[h][j].y); s[3] = s[3] + h2f(w[h][j].y >> 16);
     }
 #pragma unroll
-    for (int q = 0; q < kVec; q++) {
+    for (int q = 0; q < 4; q++) {
       s[q] = (s[q] / (float)M) * inv;
       const double x = (double)s[q];
       acc = acc + x * x;
     }
-    if (STAGE) store8(stage + e, s);
+    if (STAGE) {
+      f32x4 a;
+      a[0] = s[0]; a[1] = s[1]; a[2] = s[2]; a[3] = s[3];
+      __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(stage + base + h * (kNormTile / 2)));
+    }
   }
   const double t = block_sum(acc);
   if (threadIdx.x == 0) partials[blockIdx.x] = t;
