@@ -383,6 +383,31 @@ int zero_offload_step_amp(zs_offload *ctx, const void *const *grads, float lr, f
                           zs_amp_state *state_dev, float growth_factor, float backoff_factor,
                           int32_t growth_interval, double *grad_norm_out);
 
+/*
+ * The multi-rank split of the offloaded steps, as for the device steps
+ * (zero_shard_grad_sumsq / zero_shard_step_global_norm and their _amp twins):
+ * part 1 runs the device norm pass, which also stages the averages part 2
+ * sends to the host, and enqueues this shard's sum of squares into *sumsq_dev;
+ * the caller sums it over the ranks; part 2 takes the clip coefficient (bf16:
+ * max_grad_norm must be > 0), or the loss-scaled step's skip decision, clip and
+ * scaler update, from the global value and runs the host update.  Part 1
+ * enqueues only; part 2 returns when the host state is updated and the params
+ * are queued back.  Part 2 uses what the same context's part 1 staged.
+ * Errors: ZS_EINVAL, ZS_ESTATE (the wrong kind of context), ZS_EHIP.
+ */
+int zero_offload_grad_sumsq(zs_offload *ctx, const void *const *grads, double *sumsq_dev);
+int zero_offload_step_global_norm(zs_offload *ctx, const void *const *grads, float lr,
+                                  float beta1, float beta2, float eps, float weight_decay,
+                                  int64_t step, float max_grad_norm,
+                                  const double *global_sumsq_dev);
+int zero_offload_grad_sumsq_amp(zs_offload *ctx, const void *const *grads,
+                                const zs_amp_state *state_dev, double *sumsq_dev);
+int zero_offload_step_amp_global_norm(zs_offload *ctx, const void *const *grads, float lr,
+                                      float beta1, float beta2, float eps, float weight_decay,
+                                      float max_grad_norm, zs_amp_state *state_dev,
+                                      float growth_factor, float backoff_factor,
+                                      int32_t growth_interval, const double *global_sumsq_dev);
+
 /* Later offload steps enqueue their device work on `stream`. */
 int zero_offload_set_stream(zs_offload *ctx, void *stream);
 

@@ -95,6 +95,12 @@ _sig("zero_offload_step", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, 
      _P(_f64))
 _sig("zero_offload_step_amp", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _f32, _vp,
      _f32, _f32, _i32, _P(_f64))
+_sig("zero_offload_grad_sumsq", ctypes.c_int, _vp, _vp, _vp)
+_sig("zero_offload_step_global_norm", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _i64,
+     _f32, _vp)
+_sig("zero_offload_grad_sumsq_amp", ctypes.c_int, _vp, _vp, _vp, _vp)
+_sig("zero_offload_step_amp_global_norm", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32,
+     _f32, _vp, _f32, _f32, _i32, _vp)
 _sig("zero_offload_set_stream", ctypes.c_int, _vp, _vp)
 _sig("zero_offload_destroy", None, _vp)
 
@@ -107,7 +113,9 @@ EXPORTED = ["zs_plan_create", "zs_plan_query", "zs_plan_tensor_slice", "zs_plan_
             "zero_shard_params", "zero_shard_set_stream",
             "zero_shard_destroy", "zero_shard_last_error", "zs_host_adamw",
             "zs_offload_staging_bytes", "zero_offload_init", "zero_offload_step",
-            "zero_offload_step_amp", "zero_offload_set_stream", "zero_offload_destroy"]
+            "zero_offload_step_amp", "zero_offload_grad_sumsq", "zero_offload_step_global_norm",
+            "zero_offload_grad_sumsq_amp", "zero_offload_step_amp_global_norm",
+            "zero_offload_set_stream", "zero_offload_destroy"]
 
 
 class ZeroShardError(RuntimeError):
@@ -368,6 +376,35 @@ def zero_offload_step_amp(ctx: int, grads: Sequence[int], lr: float, beta1: floa
                                            ctypes.byref(nrm) if want_norm else None))
     norm = nrm.value if want_norm else None
     return (rc, norm) if return_code else norm
+
+
+def zero_offload_grad_sumsq(ctx: int, grads: Sequence[int], sumsq_dev: int) -> None:
+    _check(_lib.zero_offload_grad_sumsq(ctx, _ptr_array(grads), sumsq_dev))
+
+
+def zero_offload_step_global_norm(ctx: int, grads: Sequence[int], lr: float, beta1: float,
+                                  beta2: float, eps: float, weight_decay: float, step: int,
+                                  max_grad_norm: float, global_sumsq_dev: int) -> None:
+    _check(_lib.zero_offload_step_global_norm(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
+                                              weight_decay, step, max_grad_norm,
+                                              global_sumsq_dev))
+
+
+def zero_offload_grad_sumsq_amp(ctx: int, grads: Sequence[int], state_dev: int,
+                                sumsq_dev: int) -> None:
+    _check(_lib.zero_offload_grad_sumsq_amp(ctx, _ptr_array(grads), state_dev, sumsq_dev))
+
+
+def zero_offload_step_amp_global_norm(ctx: int, grads: Sequence[int], lr: float, beta1: float,
+                                      beta2: float, eps: float, weight_decay: float,
+                                      max_grad_norm: float, state_dev: int,
+                                      growth_factor: float = 2.0, backoff_factor: float = 0.5,
+                                      growth_interval: int = 2000,
+                                      global_sumsq_dev: int = 0) -> None:
+    _check(_lib.zero_offload_step_amp_global_norm(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
+                                                  weight_decay, max_grad_norm, state_dev,
+                                                  growth_factor, backoff_factor,
+                                                  growth_interval, global_sumsq_dev))
 
 
 def zero_offload_set_stream(ctx: int, stream: int) -> None:

@@ -100,6 +100,33 @@ int check_hparams(float lr, float beta1, float beta2, float eps, float wd, int64
   return ZS_OK;
 }
 
+int check_amp_args(const char* who, float lr, float beta1, float beta2, float eps,
+                   float weight_decay, float max_grad_norm, const zs_amp_state* state_dev,
+                   float growth_factor, float backoff_factor, int32_t growth_interval,
+                   AmpParams* p) {
+  const std::string w(who);
+  int rc = check_hparams(lr, beta1, beta2, eps, weight_decay, 1);
+  if (rc) return rc;
+  if (isnan(max_grad_norm) || isinf(max_grad_norm))
+    return einval((w + ": max_grad_norm must be finite").c_str());
+  if (!state_dev || ((uintptr_t)state_dev & 15u))
+    return einval((w + ": state_dev must be a 16-byte-aligned device pointer").c_str());
+  if (!(growth_factor >= 1.0f) || isinf(growth_factor) || !(backoff_factor > 0.0f) ||
+      !(backoff_factor <= 1.0f) || growth_interval < 1)
+    return einval((w + ": need growth >= 1, 0 < backoff <= 1, interval >= 1").c_str());
+  p->lr = lr;
+  p->beta1 = beta1;
+  p->beta2 = beta2;
+  p->eps = eps;
+  p->weight_decay = weight_decay;
+  p->max_norm = max_grad_norm;
+  p->growth = growth_factor;
+  p->backoff = backoff_factor;
+  p->interval = growth_interval;
+  p->clip = max_grad_norm > 0.0f ? 1 : 0;
+  return ZS_OK;
+}
+
 }  // namespace zs
 
 using zs::check_hparams;
@@ -480,26 +507,8 @@ int amp_args(const zs_ctx* ctx, const char* who, float lr, float beta1, float be
   const std::string w(who);
   if (!ctx) return einval((w + ": ctx is NULL").c_str());
   if (!ctx->fp16) return estate((w + ": needs a context created with ZS_FP16").c_str());
-  int rc = check_hparams(lr, beta1, beta2, eps, weight_decay, 1);
-  if (rc) return rc;
-  if (isnan(max_grad_norm) || isinf(max_grad_norm))
-    return einval((w + ": max_grad_norm must be finite").c_str());
-  if (!state_dev || ((uintptr_t)state_dev & 15u))
-    return einval((w + ": state_dev must be a 16-byte-aligned device pointer").c_str());
-  if (!(growth_factor >= 1.0f) || isinf(growth_factor) || !(backoff_factor > 0.0f) ||
-      !(backoff_factor <= 1.0f) || growth_interval < 1)
-    return einval((w + ": need growth >= 1, 0 < backoff <= 1, interval >= 1").c_str());
-  p->lr = lr;
-  p->beta1 = beta1;
-  p->beta2 = beta2;
-  p->eps = eps;
-  p->weight_decay = weight_decay;
-  p->max_norm = max_grad_norm;
-  p->growth = growth_factor;
-  p->backoff = backoff_factor;
-  p->interval = growth_interval;
-  p->clip = max_grad_norm > 0.0f ? 1 : 0;
-  return ZS_OK;
+  return zs::check_amp_args(who, lr, beta1, beta2, eps, weight_decay, max_grad_norm, state_dev,
+                            growth_factor, backoff_factor, growth_interval, p);
 }
 
 // The rest of a loss-scaled step once the norm pass has run (or, with

@@ -7,6 +7,7 @@
 
 #include <string>
 
+#include "../../include/zeroshard.h"
 #include "internal.h"
 
 namespace zs {
@@ -20,5 +21,11 @@ int einval(const char* msg);
 int ehip(const char* where, hipError_t e);
 // ZS_OK or ZS_EINVAL for the AdamW hyper-parameters and the 1-based step.
 int check_hparams(float lr, float beta1, float beta2, float eps, float wd, int64_t step);
+// The arguments of a loss-scaled step (hyper-parameters, clip threshold, scaler
+// state pointer and rules); fills the finalize parameters.  ZS_OK or ZS_EINVAL.
+int check_amp_args(const char* who, float lr, float beta1, float beta2, float eps,
+                   float weight_decay, float max_grad_norm, const zs_amp_state* state_dev,
+                   float growth_factor, float backoff_factor, int32_t growth_interval,
+                   AmpParams* p);
 
 }  // namespace zs

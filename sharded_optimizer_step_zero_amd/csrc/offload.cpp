@@ -355,49 +355,136 @@ extern "C" int zero_offload_step_amp(zs_offload* c, const void* const* grads, fl
                                      float max_grad_norm, zs_amp_state* state_dev,
                                      float growth_factor, float backoff_factor,
                                      int32_t growth_interval, double* grad_norm_out) {
-  using zs::einval;
-  if (!c) return einval("zero_offload_step_amp: ctx is NULL");
+  const char* who = "zero_offload_step_amp";
+  if (!c) return zs::einval("zero_offload_step_amp: ctx is NULL");
   if (!c->fp16) return estate("zero_offload_step_amp: needs a context created with ZS_FP16");
-  int rc = zs::check_hparams(lr, beta1, beta2, eps, weight_decay, 1);
+  zs::AmpParams p;
+  int rc = zs::check_amp_args(who, lr, beta1, beta2, eps, weight_decay, max_grad_norm, state_dev,
+                              growth_factor, backoff_factor, growth_interval, &p);
   if (rc) return rc;
-  if (isnan(max_grad_norm) || isinf(max_grad_norm))
-    return einval("zero_offload_step_amp: max_grad_norm must be finite");
-  if (!state_dev || !aligned(state_dev, 16))
-    return einval("zero_offload_step_amp: state_dev must be a 16-byte-aligned device pointer");
-  if (!(growth_factor >= 1.0f) || isinf(growth_factor) || !(backoff_factor > 0.0f) ||
-      !(backoff_factor <= 1.0f) || growth_interval < 1)
-    return einval("zero_offload_step_amp: need growth >= 1, 0 < backoff <= 1, interval >= 1");
   zs::GradPtrs g;
-  if ((rc = gather(c, grads, &g, "zero_offload_step_amp"))) return rc;
-  if (c->shard_len == 0) {
-    if (grad_norm_out) *grad_norm_out = 0.0;
-    return ZS_OK;
-  }
+  if ((rc = gather(c, grads, &g, who))) return rc;
   const int64_t S = c->shard_len;
   zs::AmpState* st = reinterpret_cast<zs::AmpState*>(state_dev);
-  zs::AmpParams p;
-  p.lr = lr;
-  p.beta1 = beta1;
-  p.beta2 = beta2;
-  p.eps = eps;
-  p.weight_decay = weight_decay;
-  p.max_norm = max_grad_norm;
-  p.growth = growth_factor;
-  p.backoff = backoff_factor;
-  p.interval = growth_interval;
-  p.clip = max_grad_norm > 0.0f ? 1 : 0;
   float* stage = reinterpret_cast<float*>(c->ws + c->lay.stage_off);
   double* partials = reinterpret_cast<double*>(c->ws + c->lay.partials_off);
   char* block = c->ws + c->lay.scalars_off;
   // the device part: unscaled averages staged, found-inf, scaler update and the
-  // step constants at t = applied + 1, all on the device
-  hipError_t e = zs::launch_sumsq_f16(c->M, g, S, partials, st, stage, c->stream);
+  // step constants at t = applied + 1, all on the device; an empty shard still
+  // runs the finalize, so its scaler advances like every other rank's
+  hipError_t e = hipSuccess;
+  if (S > 0) e = zs::launch_sumsq_f16(c->M, g, S, partials, st, stage, c->stream);
   if (e == hipSuccess)
-    e = zs::launch_amp_finalize(partials + zs::level1_partials(S), zs::final_partials(S),
-                                nullptr, st, p, reinterpret_cast<zs::ClipScalars*>(block),
+    e = zs::launch_amp_finalize(partials + zs::level1_partials(S),
+                                S ? zs::final_partials(S) : 0, nullptr, st, p,
+                                reinterpret_cast<zs::ClipScalars*>(block),
                                 reinterpret_cast<zs::StepConsts*>(block + 64), c->stream);
   if (e != hipSuccess) return zs::ehip("zero_offload_step_amp: norm pass", e);
-  return pipeline(c, nullptr, true, grad_norm_out, "zero_offload_step_amp");
+  return pipeline(c, nullptr, true, grad_norm_out, who);
+}
+
+namespace {
+
+// Part 1 of the multi-rank split on an offload context: the device norm pass
+// (which stages the averages part 2 sends to the host) and this shard's sum of
+// squares into *sumsq_dev.
+int offload_sumsq(zs_offload* c, const void* const* grads, const zs_amp_state* state_dev,
+                  double* sumsq_dev, const char* who) {
+  const std::string w(who);
+  if (!sumsq_dev || !aligned(sumsq_dev, 8))
+    return zs::einval((w + ": sumsq_dev must be an 8-byte-aligned device pointer").c_str());
+  zs::GradPtrs g;
+  int rc = gather(c, grads, &g, who);
+  if (rc) return rc;
+  const int64_t S = c->shard_len;
+  float* stage = reinterpret_cast<float*>(c->ws + c->lay.stage_off);
+  double* partials = reinterpret_cast<double*>(c->ws + c->lay.partials_off);
+  const int32_t n_final = S ? zs::final_partials(S) : 0;
+  hipError_t e = hipSuccess;
+  if (n_final)
+    e = state_dev ? zs::launch_sumsq_f16(c->M, g, S, partials,
+                                         reinterpret_cast<const zs::AmpState*>(state_dev),
+                                         stage, c->stream)
+                  : zs::launch_sumsq(c->M, g, S, partials, stage, c->stream);
+  if (e == hipSuccess)
+    e = zs::launch_sumsq_total(partials + zs::level1_partials(S), n_final, sumsq_dev, c->stream);
+  return e == hipSuccess ? ZS_OK : zs::ehip(who, e);
+}
+
+}  // namespace
+
+extern "C" int zero_offload_grad_sumsq(zs_offload* c, const void* const* grads,
+                                       double* sumsq_dev) {
+  if (!c) return zs::einval("zero_offload_grad_sumsq: ctx is NULL");
+  if (c->fp16) return estate("zero_offload_grad_sumsq: fp16 context: use zero_offload_grad_sumsq_amp");
+  return offload_sumsq(c, grads, nullptr, sumsq_dev, "zero_offload_grad_sumsq");
+}
+
+extern "C" int zero_offload_step_global_norm(zs_offload* c, const void* const* grads, float lr,
+                                             float beta1, float beta2, float eps,
+                                             float weight_decay, int64_t step,
+                                             float max_grad_norm,
+                                             const double* global_sumsq_dev) {
+  using zs::einval;
+  const char* who = "zero_offload_step_global_norm";
+  if (!c) return einval("zero_offload_step_global_norm: ctx is NULL");
+  if (c->fp16) return estate("zero_offload_step_global_norm: fp16 context: use the _amp calls");
+  int rc = zs::check_hparams(lr, beta1, beta2, eps, weight_decay, step);
+  if (rc) return rc;
+  if (!(max_grad_norm > 0.0f) || isinf(max_grad_norm))
+    return einval("zero_offload_step_global_norm: max_grad_norm must be finite and > 0");
+  if (!global_sumsq_dev || !aligned(global_sumsq_dev, 8))
+    return einval("zero_offload_step_global_norm: global_sumsq_dev must be an aligned device pointer");
+  zs::GradPtrs g;
+  if ((rc = gather(c, grads, &g, who))) return rc;
+  if (c->shard_len == 0) return ZS_OK;
+  const zs::HostConsts k =
+      host_consts(zs::step_consts(lr, beta1, beta2, eps, weight_decay, step));
+  zs::ClipScalars* sc_dev = reinterpret_cast<zs::ClipScalars*>(c->ws + c->lay.scalars_off);
+  const hipError_t e = zs::launch_finalize(nullptr, 0, global_sumsq_dev, max_grad_norm, 1,
+                                           (c->flags & ZS_SKIP_NONFINITE) ? 1 : 0, sc_dev,
+                                           c->stream);
+  if (e != hipSuccess) return zs::ehip("zero_offload_step_global_norm: finalize", e);
+  return pipeline(c, &k, false, nullptr, who);
+}
+
+extern "C" int zero_offload_grad_sumsq_amp(zs_offload* c, const void* const* grads,
+                                           const zs_amp_state* state_dev, double* sumsq_dev) {
+  if (!c) return zs::einval("zero_offload_grad_sumsq_amp: ctx is NULL");
+  if (!c->fp16)
+    return estate("zero_offload_grad_sumsq_amp: needs a context created with ZS_FP16");
+  if (!state_dev || !aligned(state_dev, 16))
+    return zs::einval(
+        "zero_offload_grad_sumsq_amp: state_dev must be a 16-byte-aligned device pointer");
+  return offload_sumsq(c, grads, state_dev, sumsq_dev, "zero_offload_grad_sumsq_amp");
+}
+
+extern "C" int zero_offload_step_amp_global_norm(zs_offload* c, const void* const* grads,
+                                                 float lr, float beta1, float beta2, float eps,
+                                                 float weight_decay, float max_grad_norm,
+                                                 zs_amp_state* state_dev, float growth_factor,
+                                                 float backoff_factor, int32_t growth_interval,
+                                                 const double* global_sumsq_dev) {
+  const char* who = "zero_offload_step_amp_global_norm";
+  if (!c) return zs::einval("zero_offload_step_amp_global_norm: ctx is NULL");
+  if (!c->fp16)
+    return estate("zero_offload_step_amp_global_norm: needs a context created with ZS_FP16");
+  zs::AmpParams p;
+  int rc = zs::check_amp_args(who, lr, beta1, beta2, eps, weight_decay, max_grad_norm, state_dev,
+                              growth_factor, backoff_factor, growth_interval, &p);
+  if (rc) return rc;
+  if (!global_sumsq_dev || !aligned(global_sumsq_dev, 8))
+    return zs::einval(
+        "zero_offload_step_amp_global_norm: global_sumsq_dev must be an aligned device pointer");
+  zs::GradPtrs g;
+  if ((rc = gather(c, grads, &g, who))) return rc;
+  char* block = c->ws + c->lay.scalars_off;
+  const hipError_t e = zs::launch_amp_finalize(
+      nullptr, 0, global_sumsq_dev, reinterpret_cast<zs::AmpState*>(state_dev), p,
+      reinterpret_cast<zs::ClipScalars*>(block), reinterpret_cast<zs::StepConsts*>(block + 64),
+      c->stream);
+  if (e != hipSuccess) return zs::ehip("zero_offload_step_amp_global_norm: finalize", e);
+  return pipeline(c, nullptr, true, nullptr, who);
 }
 
 extern "C" int zero_offload_set_stream(zs_offload* c, void* stream) {

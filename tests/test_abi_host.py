@@ -19,7 +19,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 31
+    assert len(names) == 35
     lib = ctypes.CDLL(zs.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -78,6 +78,13 @@ def test_init_and_step_argument_errors_before_any_device_call():
         with pytest.raises(zs.ZeroShardError):
             zs.zero_shard_step(0, [16] * 4, 1e-3, 0.9, 0.95, 1e-8, 0.1, 1)
         for call in (lambda: zs.zero_shard_grad_sumsq_amp(0, [16] * 4, 16, 16),
+                     lambda: zs.zero_offload_grad_sumsq(0, [16] * 4, 16),
+                     lambda: zs.zero_offload_step_global_norm(0, [16] * 4, 1e-3, 0.9, 0.95, 1e-8,
+                                                              0.1, 1, 1.0, 16),
+                     lambda: zs.zero_offload_grad_sumsq_amp(0, [16] * 4, 16, 16),
+                     lambda: zs.zero_offload_step_amp_global_norm(0, [16] * 4, 1e-3, 0.9, 0.95,
+                                                                  1e-8, 0.1, 1.0, 16,
+                                                                  global_sumsq_dev=16),
                      lambda: zs.zero_shard_step_amp_global_norm(0, [16] * 4, 1e-3, 0.9, 0.95,
                                                                 1e-8, 0.1, 1.0, 16,
                                                                 global_sumsq_dev=16)):

@@ -1,12 +1,14 @@
 """The multi-rank split of the clipped and of the loss-scaled step, on one GPU.
 
 N ranks are simulated as N contexts, each over its own shard of one model (its
-own plan for rank r of N).  Per step every rank enqueues part 1 (its shard's
-sum of squares); the scalar all-reduce that a real job would run over the
-ranks is a fixed-order sum of the N device doubles; every rank then runs part 2
-with that global value.  The shards, mapped back tensor by tensor, must equal
-the unsharded oracle run over the whole model bit for bit: the same clip
-coefficient, the same skip decision and the same scaler state on every rank.
+own plan for rank r of N): device contexts (fused and with the staged average)
+and offload contexts (the update on host cores).  Per step every rank enqueues
+part 1 (its shard's sum of squares); the scalar all-reduce that a real job
+would run over the ranks is a fixed-order sum of the N device doubles; every
+rank then runs part 2 with that global value.  The shards, mapped back tensor
+by tensor, must equal the unsharded oracle run over the whole model bit for
+bit: the same clip coefficient, the same skip decision and the same scaler
+state on every rank.
 """
 import numpy as np
 import pytest
@@ -16,7 +18,7 @@ import oracle
 import synth
 import sharded_optimizer_step_zero_amd as zsm
 from oracle import layout as L
-from sharded_optimizer_step_zero_amd import ZeroShard
+from sharded_optimizer_step_zero_amd import ZeroOffload, ZeroShard
 
 from _gpu import log, to_host
 
@@ -57,12 +59,30 @@ def _u16(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
 
 
-def _setup(fp16, stage):
+VARIANTS = ["device", "device_staged", "offload"]
+
+# part 1 and part 2 of the split, by context kind
+SUMSQ = {"device": zsm.zero_shard_grad_sumsq, "offload": zsm.zero_offload_grad_sumsq}
+STEP = {"device": zsm.zero_shard_step_global_norm, "offload": zsm.zero_offload_step_global_norm}
+SUMSQ_AMP = {"device": zsm.zero_shard_grad_sumsq_amp, "offload": zsm.zero_offload_grad_sumsq_amp}
+STEP_AMP = {"device": zsm.zero_shard_step_amp_global_norm,
+            "offload": zsm.zero_offload_step_amp_global_norm}
+
+
+def _kind(variant):
+    return "offload" if variant == "offload" else "device"
+
+
+def _setup(fp16, variant):
     lays = [L.plan(NUMEL, DECAY, N, r, CAP, 64) for r in range(N)]
     one = L.plan(NUMEL, DECAY, 1, 0, CAP, 64)
-    flags = zsm.ZS_STAGE_AVERAGE if stage else 0
-    zs = [ZeroShard(NUMEL, DECAY, N, r, M, bucket_cap=CAP, fp16=fp16, flags=flags)
-          for r in range(N)]
+    if variant == "offload":   # small chunks: the host pipeline runs many of them
+        zs = [ZeroOffload(NUMEL, DECAY, N, r, M, bucket_cap=CAP, fp16=fp16, chunk_elems=8192)
+              for r in range(N)]
+    else:
+        flags = zsm.ZS_STAGE_AVERAGE if variant == "device_staged" else 0
+        zs = [ZeroShard(NUMEL, DECAY, N, r, M, bucket_cap=CAP, fp16=fp16, flags=flags)
+              for r in range(N)]
     master_t = [synth.host_normal_f32(n, synth.key(31, t), 0.02) for t, n in enumerate(NUMEL)]
     for lay, z in zip(lays, zs):
         assert z.shard_len == lay.shard_len
@@ -84,10 +104,11 @@ def _check(lays, one, zs, ref, step):
             assert np.array_equal(_bits(got[t]), _bits(want[t])), (step, key, t)
 
 
-@pytest.mark.parametrize("stage", [False, True])
-def test_bf16_clip_split_over_ranks_equals_unsharded(stage):
-    log(f"test_bf16_clip_split_over_ranks_equals_unsharded stage={stage}")
-    lays, one, zs, ref = _setup(False, stage)
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_bf16_clip_split_over_ranks_equals_unsharded(variant):
+    log(f"test_bf16_clip_split_over_ranks_equals_unsharded {variant}")
+    lays, one, zs, ref = _setup(False, variant)
+    kind = _kind(variant)
     part = torch.zeros(N, dtype=torch.float64, device="cuda")
     glob = torch.zeros(1, dtype=torch.float64, device="cuda")
     mask = one.decay_mask()
@@ -97,14 +118,12 @@ def test_bf16_clip_split_over_ranks_equals_unsharded(stage):
                     for t, n in enumerate(NUMEL)] for j in range(M)]
         dev = [[_u16(_scatter(lay, grads_t[j], np.uint16)) for j in range(M)] for lay in lays]
         for r, z in enumerate(zs):
-            zsm.zero_shard_grad_sumsq(z.ctx, [g.data_ptr() for g in dev[r]],
-                                      part[r:r + 1].data_ptr())
+            SUMSQ[kind](z.ctx, [g.data_ptr() for g in dev[r]], part[r:r + 1].data_ptr())
         glob.copy_(part[0:1] + part[1:2] + part[2:3])        # the scalar all-reduce
         max_norm = 0.02 if s % 2 else 1e3                    # binding, then not
         for r, z in enumerate(zs):
-            zsm.zero_shard_step_global_norm(z.ctx, [g.data_ptr() for g in dev[r]], step=s + 1,
-                                            max_grad_norm=max_norm,
-                                            global_sumsq_dev=glob.data_ptr(), **HP)
+            STEP[kind](z.ctx, [g.data_ptr() for g in dev[r]], step=s + 1,
+                       max_grad_norm=max_norm, global_sumsq_dev=glob.data_ptr(), **HP)
         torch.cuda.synchronize()
         g_one = [_scatter(one, grads_t[j], np.uint16) for j in range(M)]
         want = float(np.sqrt(oracle.grad_sumsq(g_one)))
@@ -119,10 +138,11 @@ def test_bf16_clip_split_over_ranks_equals_unsharded(stage):
         z.close()
 
 
-@pytest.mark.parametrize("stage", [False, True])
-def test_amp_split_over_ranks_equals_unsharded(stage):
-    log(f"test_amp_split_over_ranks_equals_unsharded stage={stage}")
-    lays, one, zs, ref = _setup(True, stage)
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_amp_split_over_ranks_equals_unsharded(variant):
+    log(f"test_amp_split_over_ranks_equals_unsharded {variant}")
+    lays, one, zs, ref = _setup(True, variant)
+    kind = _kind(variant)
     for z in zs:
         z.amp_init(2.0 ** 12)
     sc = oracle.Scaler(scale=2.0 ** 12, growth_interval=2)
@@ -138,15 +158,14 @@ def test_amp_split_over_ranks_equals_unsharded(stage):
             grads_t[1][3][123] = 0x7C00 if s == 2 else 0xFE00
         dev = [[_u16(_scatter(lay, grads_t[j], np.uint16)) for j in range(M)] for lay in lays]
         for r, z in enumerate(zs):
-            zsm.zero_shard_grad_sumsq_amp(z.ctx, [g.data_ptr() for g in dev[r]],
-                                          z.amp_state.data_ptr(), part[r:r + 1].data_ptr())
+            SUMSQ_AMP[kind](z.ctx, [g.data_ptr() for g in dev[r]], z.amp_state.data_ptr(),
+                            part[r:r + 1].data_ptr())
         glob.copy_(part[0:1] + part[1:2] + part[2:3])
         clip = 0.01 if s % 2 else 0.0
         for r, z in enumerate(zs):
-            zsm.zero_shard_step_amp_global_norm(z.ctx, [g.data_ptr() for g in dev[r]],
-                                                max_grad_norm=clip, state_dev=z.amp_state.data_ptr(),
-                                                growth_interval=2,
-                                                global_sumsq_dev=glob.data_ptr(), **HP)
+            STEP_AMP[kind](z.ctx, [g.data_ptr() for g in dev[r]], max_grad_norm=clip,
+                           state_dev=z.amp_state.data_ptr(), growth_interval=2,
+                           global_sumsq_dev=glob.data_ptr(), **HP)
         torch.cuda.synchronize()
         g_one = [_scatter(one, grads_t[j], np.uint16) for j in range(M)]
         fi, onorm = oracle.amp_step(g_one, ref["p"], ref["m"], ref["v"], ref["b"], mask, sc,

@@ -246,3 +246,29 @@ def test_offload_amp_equals_device_amp():
         assert zo.amp_read() == zd.amp_read()
     zo.close()
     zd.close()
+
+
+def test_offload_amp_empty_shard_keeps_the_scaler_in_step():
+    """An offload rank with an empty shard advances its scaler like the others,
+    alone and through the multi-rank split."""
+    log("test_offload_amp_empty_shard_keeps_the_scaler_in_step")
+    HPA = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    z = ZeroOffload([0, 0], [1, 1], 2, 1, 2, fp16=True)
+    assert z.shard_len == 0
+    z.amp_init(1024.0)
+    g = torch.zeros(8, dtype=torch.int16, device="cuda")
+    for _ in range(2):
+        assert z.step_amp([g, g], growth_interval=2, want_norm=True, **HPA) == 0.0
+    assert z.amp_read() == (2048.0, 0, 2)
+    d = torch.full((1,), 7.0, dtype=torch.float64, device="cuda")
+    zsm.zero_offload_grad_sumsq_amp(z.ctx, [g.data_ptr()] * 2, z.amp_state.data_ptr(),
+                                    d.data_ptr())
+    assert d.item() == 0.0
+    for total, want in ((4.0, (2048.0, 1, 3)), (float("inf"), (1024.0, 0, 3))):
+        d.fill_(total)
+        zsm.zero_offload_step_amp_global_norm(z.ctx, [g.data_ptr()] * 2, max_grad_norm=1.0,
+                                              state_dev=z.amp_state.data_ptr(),
+                                              growth_interval=2, global_sumsq_dev=d.data_ptr(),
+                                              **HPA)
+        assert z.amp_read() == want
+    z.close()
