@@ -126,6 +126,7 @@ struct zs_offload {
   hipStream_t stream = nullptr, d2h = nullptr, h2d = nullptr;
   hipEvent_t ready = nullptr, scalars = nullptr, done = nullptr;
   hipEvent_t g_ready[2] = {nullptr, nullptr}, p_sent[2] = {nullptr, nullptr};
+  std::vector<hipEvent_t> chunk_done;  // per chunk: its averages are staged on the device
   std::unique_ptr<zs::HostPool> pool;
 
   ~zs_offload() {
@@ -133,6 +134,8 @@ struct zs_offload {
     if (d2h) (void)hipStreamSynchronize(d2h);
     if (h2d) (void)hipStreamSynchronize(h2d);
     for (hipEvent_t e : {ready, scalars, done, g_ready[0], g_ready[1], p_sent[0], p_sent[1]})
+      if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : chunk_done)
       if (e) (void)hipEventDestroy(e);
     if (d2h) (void)hipStreamDestroy(d2h);
     if (h2d) (void)hipStreamDestroy(h2d);
@@ -195,6 +198,7 @@ extern "C" int zero_offload_init(zs_offload** out, const zs_plan* plan, int32_t 
   try {
     c->runs = host_runs(plan);
     c->chunks = chunk_schedule(plan->shard_len, chunk_elems);
+    c->chunk_done.assign(c->chunks.size(), nullptr);
     c->pool.reset(new zs::HostPool(n_threads > 0 ? n_threads : zs::default_host_threads()));
   } catch (const std::bad_alloc&) {
     return enomem("zero_offload_init: out of host memory");
@@ -208,6 +212,8 @@ extern "C" int zero_offload_init(zs_offload** out, const zs_plan* plan, int32_t 
   for (hipEvent_t* ev : {&c->ready, &c->scalars, &c->done, &c->g_ready[0], &c->g_ready[1],
                          &c->p_sent[0], &c->p_sent[1]})
     if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+  for (hipEvent_t& ev : c->chunk_done)
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
   // both param buffers start out free: their events complete on an empty stream
   for (int b = 0; b < 2 && e == hipSuccess; b++) e = hipEventRecord(c->p_sent[b], c->h2d);
   if (e == hipSuccess) e = hipStreamSynchronize(c->h2d);
@@ -248,8 +254,12 @@ int gather(const zs_offload* c, const void* const* grads, zs::GradPtrs* g, const
 // staged averages): the scalars and the averages come to the host, the host
 // updates chunk by chunk, the params go back.  k_host: the step constants, or
 // null to take the ones the device computed (the loss-scaled step).
+// per_chunk (non-null: a bf16 step that needs no norm): the device part has not
+// run; it is queued here chunk by chunk, each chunk's copy to the host waiting
+// only for its own averages, so the host starts on the first chunk while the
+// device still reduces the rest.  The coefficient is then 1 and nothing skips.
 int pipeline(zs_offload* c, const zs::HostConsts* k_host, bool out_f16, double* grad_norm_out,
-             const char* who) {
+             const char* who, const zs::GradPtrs* per_chunk = nullptr) {
   float* stage = reinterpret_cast<float*>(c->ws + c->lay.stage_off);
   const char* block_dev = c->ws + c->lay.scalars_off;
   volatile char* block_host = c->staging;  // the first 256 staging bytes
@@ -257,9 +267,20 @@ int pipeline(zs_offload* c, const zs::HostConsts* k_host, bool out_f16, double* 
   hipError_t e = hipEventRecord(c->ready, c->stream);
   if (e == hipSuccess) e = hipStreamWaitEvent(c->d2h, c->ready, 0);
   if (e == hipSuccess) e = hipStreamWaitEvent(c->h2d, c->ready, 0);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync((void*)block_host, block_dev, 256, hipMemcpyDeviceToHost, c->d2h);
-  if (e == hipSuccess) e = hipEventRecord(c->scalars, c->d2h);
+  if (per_chunk) {
+    double* partials = reinterpret_cast<double*>(c->ws + c->lay.partials_off);
+    for (size_t ci = 0; ci < c->chunks.size() && e == hipSuccess; ci++) {
+      const int64_t off = c->chunks[ci].first, len = c->chunks[ci].second;
+      zs::GradPtrs g = *per_chunk;
+      for (int j = 0; j < c->M; j++) g.p[j] += off;
+      e = zs::launch_sumsq(c->M, g, len, partials, stage + off, c->stream);
+      if (e == hipSuccess) e = hipEventRecord(c->chunk_done[ci], c->stream);
+    }
+  } else {
+    if (e == hipSuccess)
+      e = hipMemcpyAsync((void*)block_host, block_dev, 256, hipMemcpyDeviceToHost, c->d2h);
+    if (e == hipSuccess) e = hipEventRecord(c->scalars, c->d2h);
+  }
   if (e != hipSuccess) return fail(c, who, e);
 
   const int64_t n_chunks = (int64_t)c->chunks.size();
@@ -268,18 +289,24 @@ int pipeline(zs_offload* c, const zs::HostConsts* k_host, bool out_f16, double* 
   auto fetch = [&](int64_t ci) {  // queue chunk ci's averages into gradient buffer ci % 2
     const int64_t off = c->chunks[ci].first, len = c->chunks[ci].second;
     const int b = (int)(ci & 1);
-    hipError_t r = hipMemcpyAsync(gbuf(b), stage + off, (size_t)len * sizeof(float),
-                                  hipMemcpyDeviceToHost, c->d2h);
+    hipError_t r = per_chunk ? hipStreamWaitEvent(c->d2h, c->chunk_done[ci], 0) : hipSuccess;
+    if (r == hipSuccess)
+      r = hipMemcpyAsync(gbuf(b), stage + off, (size_t)len * sizeof(float),
+                         hipMemcpyDeviceToHost, c->d2h);
     if (r == hipSuccess) r = hipEventRecord(c->g_ready[b], c->d2h);
     return r;
   };
   for (int64_t ci = 0; ci < std::min<int64_t>(2, n_chunks) && e == hipSuccess; ci++) e = fetch(ci);
-  if (e == hipSuccess) e = hipEventSynchronize(c->scalars);
+  if (e == hipSuccess && !per_chunk) e = hipEventSynchronize(c->scalars);
   if (e != hipSuccess) return fail(c, who, e);
-  zs::ClipScalars sc;
-  zs::StepConsts kd;
-  memcpy(&sc, (const void*)block_host, sizeof sc);
-  memcpy(&kd, (const void*)(block_host + 64), sizeof kd);
+  zs::ClipScalars sc{};
+  zs::StepConsts kd{};
+  if (per_chunk) {
+    sc.coef = 1.0f;
+  } else {
+    memcpy(&sc, (const void*)block_host, sizeof sc);
+    memcpy(&kd, (const void*)(block_host + 64), sizeof kd);
+  }
   if (grad_norm_out) *grad_norm_out = sc.norm;
   const int done_rc = (grad_norm_out && !isfinite(sc.norm)) ? ZS_NONFINITE : ZS_OK;
   if (sc.skip) {  // the step is skipped: the state stays as it is
@@ -337,6 +364,9 @@ extern "C" int zero_offload_step(zs_offload* c, const void* const* grads, float 
   const int64_t S = c->shard_len;
   const zs::HostConsts k =
       host_consts(zs::step_consts(lr, beta1, beta2, eps, weight_decay, step));
+  // nothing needs the norm: the device reduce runs chunk by chunk inside the pipeline
+  if (!(max_grad_norm > 0.0f) && !(c->flags & ZS_SKIP_NONFINITE) && !grad_norm_out)
+    return pipeline(c, &k, false, nullptr, "zero_offload_step", &g);
   float* stage = reinterpret_cast<float*>(c->ws + c->lay.stage_off);
   double* partials = reinterpret_cast<double*>(c->ws + c->lay.partials_off);
   zs::ClipScalars* sc_dev = reinterpret_cast<zs::ClipScalars*>(c->ws + c->lay.scalars_off);
