@@ -136,6 +136,39 @@ static_assert(kTile == kStepTileElems, "tile-flag table and step tiles agree");
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Streamed outputs are written with buffer stores whose cache policy is
+// non-temporal at device scope (LLVM's cache-policy bits NT = 2 | SC1 = 16).
+// Measured on MI355X against plain non-temporal stores, same buffers: +1.5% on
+// the GPT-1.3B shard, +1.8% on the stress workload, +0.6% on Llama-6.7B; the
+// same policy on loads changed nothing.  The resource covers `bytes` from
+// `base` (a whole tile; lanes past the shard's end return before storing).
+constexpr int kStorePolicy = 2 | 16;
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
+
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(T* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ void st_out(__amdgpu_buffer_rsrc_t r, int byte_off, f32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, byte_off, 0,
+                                         kStorePolicy);
+}
+__device__ __forceinline__ void st_out(__amdgpu_buffer_rsrc_t r, int byte_off, u32x2 x) {
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, byte_off, 0, kStorePolicy);
+}
+
+// The four outputs of one lane of a step tile: master, m, v (fp32) and the
+// 16-bit param copy, elements [tile0 + 4*lane, tile0 + 4*lane + 4).
+__device__ __forceinline__ void store_step(float* master, float* mom1, float* mom2,
+                                           uint16_t* param, int64_t tile0, f32x4 p4, f32x4 m4,
+                                           f32x4 v4, u32x2 pk) {
+  const int lane = threadIdx.x;
+  st_out(out_rsrc(master + tile0, kTile * 4), lane * 16, p4);
+  st_out(out_rsrc(mom1 + tile0, kTile * 4), lane * 16, m4);
+  st_out(out_rsrc(mom2 + tile0, kTile * 4), lane * 16, v4);
+  st_out(out_rsrc(param + tile0, kTile * 2), lane * 8, pk);
+}
+
 template <int M, bool CLIP>
 __global__ __launch_bounds__(kStepLanes) void step_kernel(
     GradPtrs g, float* __restrict__ master, float* __restrict__ mom1, float* __restrict__ mom2,
@@ -182,13 +215,10 @@ __global__ __launch_bounds__(kStepLanes) void step_kernel(
     v4[q] = v;
     b[q] = to_bf16(p);
   }
-  __builtin_nontemporal_store(p4, reinterpret_cast<f32x4*>(master + e));
-  __builtin_nontemporal_store(m4, reinterpret_cast<f32x4*>(mom1 + e));
-  __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(mom2 + e));
   u32x2 pb;
   pb.x = b[0] | (b[1] << 16);
   pb.y = b[2] | (b[3] << 16);
-  __builtin_nontemporal_store(pb, reinterpret_cast<u32x2*>(param + e));
+  store_step(master, mom1, mom2, param, tile0, p4, m4, v4, pb);
 }
 
 // Sum over the workgroup in a fixed order: butterfly inside each wave64, then
@@ -255,7 +285,9 @@ __global__ __launch_bounds__(kThreads) void sumsq_kernel(GradPtrs g, int64_t n,
     if (STAGE) {
       f32x4 a;
       a[0] = s[0]; a[1] = s[1]; a[2] = s[2]; a[3] = s[3];
-      __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(stage + base + h * (kNormTile / 2)));
+      st_out(out_rsrc(stage + (int64_t)blockIdx.x * kNormTile + h * (kNormTile / 2),
+                      (int)(kNormTile / 2) * 4),
+             threadIdx.x * 16, a);
     }
   }
   const double t = block_sum(acc);
@@ -439,7 +471,9 @@ __global__ __launch_bounds__(kThreads) void sumsq_f16_kernel(GradPtrs g, int64_t
     if (STAGE) {
       f32x4 a;
       a[0] = s[0]; a[1] = s[1]; a[2] = s[2]; a[3] = s[3];
-      __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(stage + base + h * (kNormTile / 2)));
+      st_out(out_rsrc(stage + (int64_t)blockIdx.x * kNormTile + h * (kNormTile / 2),
+                      (int)(kNormTile / 2) * 4),
+             threadIdx.x * 16, a);
     }
   }
   const double t = block_sum(acc);
@@ -528,13 +562,10 @@ __global__ __launch_bounds__(kStepLanes) void step_f16_kernel(
     v4[q] = v;
     b[q] = f2h(p);
   }
-  __builtin_nontemporal_store(p4, reinterpret_cast<f32x4*>(master + e));
-  __builtin_nontemporal_store(m4, reinterpret_cast<f32x4*>(mom1 + e));
-  __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(mom2 + e));
   u32x2 ph;
   ph.x = b[0] | (b[1] << 16);
   ph.y = b[2] | (b[3] << 16);
-  __builtin_nontemporal_store(ph, reinterpret_cast<u32x2*>(param + e));
+  store_step(master, mom1, mom2, param, tile0, p4, m4, v4, ph);
 }
 
 __global__ void amp_state_init_kernel(AmpState* st, float scale) {
@@ -581,13 +612,10 @@ __global__ __launch_bounds__(kStepLanes) void step_staged_kernel(
     v4[q] = v;
     b[q] = AMP ? f2h(p) : to_bf16(p);
   }
-  __builtin_nontemporal_store(p4, reinterpret_cast<f32x4*>(master + e));
-  __builtin_nontemporal_store(m4, reinterpret_cast<f32x4*>(mom1 + e));
-  __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(mom2 + e));
   u32x2 pk;
   pk.x = b[0] | (b[1] << 16);
   pk.y = b[2] | (b[3] << 16);
-  __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(param + e));
+  store_step(master, mom1, mom2, param, tile0, p4, m4, v4, pk);
 }
 
 // The LDS reservation that caps a single-wave step kernel at waves_per_cu
