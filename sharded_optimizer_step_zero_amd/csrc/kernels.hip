@@ -390,29 +390,35 @@ __global__ __launch_bounds__(kThreads) void state_copy_kernel(
   int32_t done = 0;
   if (vec) {
     const int32_t quads = pc.len >> 2;
+    // the part's outputs as buffer resources (uniform over the workgroup), written
+    // with the streamed-output store policy
+    const int bytes32 = pc.len * 4;
+    const __amdgpu_buffer_rsrc_t o1 = out_rsrc(EXPORT ? c_master + c0 : master + s0, bytes32);
+    const __amdgpu_buffer_rsrc_t o2 = out_rsrc(EXPORT ? c_m + c0 : mom1 + s0, bytes32);
+    const __amdgpu_buffer_rsrc_t o3 = out_rsrc(EXPORT ? c_v + c0 : mom2 + s0, bytes32);
     for (int32_t q = threadIdx.x; q < quads; q += kThreads) {
       const int64_t s = s0 + 4 * (int64_t)q, c = c0 + 4 * (int64_t)q;
       if (EXPORT) {
         const f32x4 a = ld_stream(reinterpret_cast<const f32x4*>(master + s));
         const f32x4 b = ld_stream(reinterpret_cast<const f32x4*>(mom1 + s));
         const f32x4 d = ld_stream(reinterpret_cast<const f32x4*>(mom2 + s));
-        __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(c_master + c));
-        __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(c_m + c));
-        __builtin_nontemporal_store(d, reinterpret_cast<f32x4*>(c_v + c));
+        st_out(o1, q * 16, a);
+        st_out(o2, q * 16, b);
+        st_out(o3, q * 16, d);
       } else {
         const f32x4 p = ld_stream(reinterpret_cast<const f32x4*>(c_master + c));
         const f32x4 a = ld_stream(reinterpret_cast<const f32x4*>(c_m + c));
         const f32x4 d = ld_stream(reinterpret_cast<const f32x4*>(c_v + c));
-        __builtin_nontemporal_store(p, reinterpret_cast<f32x4*>(master + s));
-        __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(mom1 + s));
-        __builtin_nontemporal_store(d, reinterpret_cast<f32x4*>(mom2 + s));
+        st_out(o1, q * 16, p);
+        st_out(o2, q * 16, a);
+        st_out(o3, q * 16, d);
         uint32_t b[4];
 #pragma unroll
         for (int k = 0; k < 4; k++) b[k] = F16 ? f2h(p[k]) : to_bf16(p[k]);
         u32x2 pk;
         pk.x = b[0] | (b[1] << 16);
         pk.y = b[2] | (b[3] << 16);
-        __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(param + s));
+        st_out(out_rsrc(param + s0, pc.len * 2), q * 8, pk);
       }
     }
     done = quads << 2;
