@@ -137,14 +137,14 @@ using zs::plan_workspace;
 namespace {
 
 // Resident-wave cap of the step kernels per CU (0: no cap), by M and shard size.
-// Measured on MI355X: caps 7..14 swept for every M on flat 164M-, 1G- and
-// 4.3G-element shards (the last column in the staggered slab placement of
-// zs_slab_layout), two rounds on the same buffers (repeatable to 0.3%), and
-// checked on the GPT, Llama and stress layouts.  Fewer contributions leave each
-// wave less in flight, so more waves pay off.  Shards near 1G elements favour
-// slightly fewer waves than both smaller and larger ones; fresh allocations move
-// any of these figures by up to 3%, so only differences seen on the same buffers
-// count.  ZS_WAVES_PER_CU overrides the table.
+// Measured on MI355X with the device-scope non-temporal stores and the
+// staggered slab placement of zs_slab_layout: caps 5..12 swept for every M on
+// flat 164M-, 1G- and 4.3G-element shards, two rounds on the same buffers
+// (repeatable to 0.3%), and checked on the GPT, Llama and stress layouts.  Fewer
+// contributions leave each wave less in flight, so more waves pay off; from
+// M = 10 on, 7 waves are best everywhere (6 and 5 lose 3-20%).  Fresh
+// allocations move any of these figures by up to 3%, so only differences seen
+// on the same buffers count.  ZS_WAVES_PER_CU overrides the table.
 int32_t default_waves_per_cu(int32_t M, int64_t shard_len, int32_t n_cu) {
   const char* env = getenv("ZS_WAVES_PER_CU");
   if (env && *env) {
@@ -152,9 +152,9 @@ int32_t default_waves_per_cu(int32_t M, int64_t shard_len, int32_t n_cu) {
     if (v == 0 || (v >= 3 && v <= 64)) return (int32_t)v;
   }
   //                                   M: 0   1   2   3   4   5   6   7   8   9  10  11  12  13  14  15  16
-  static const int8_t kSmall[ZS_MAX_M + 1] = {0, 12, 12, 11, 11, 11, 11, 10, 10, 10, 10, 9, 9, 9, 8, 8, 8};
-  static const int8_t kLarge[ZS_MAX_M + 1] = {0, 11, 11, 11, 10, 10, 10, 9, 9, 9, 9, 9, 9, 8, 8, 7, 7};
-  static const int8_t kHuge[ZS_MAX_M + 1] = {0, 12, 11, 12, 10, 10, 9, 9, 9, 9, 9, 9, 9, 7, 7, 7, 7};
+  static const int8_t kSmall[ZS_MAX_M + 1] = {0, 12, 11, 11, 10, 10, 9, 9, 9, 9, 7, 7, 7, 7, 7, 7, 7};
+  static const int8_t kLarge[ZS_MAX_M + 1] = {0, 11, 11, 10, 9, 9, 8, 8, 8, 8, 7, 7, 7, 7, 7, 7, 7};
+  static const int8_t kHuge[ZS_MAX_M + 1] = {0, 12, 10, 10, 8, 8, 9, 9, 7, 7, 7, 7, 7, 7, 7, 7, 7};
   if (M < 1 || M > ZS_MAX_M) return 0;
   int32_t cap;
   if (shard_len <= (int64_t(1) << 28)) cap = kSmall[M];
