@@ -193,6 +193,17 @@ int zs_slab_layout(const zs_plan *plan, int32_t M, uint32_t flags, int32_t n_gra
  * ZS_FP16, ZS_STAGE_AVERAGE (0 for none).
  * Uploads the run table on `stream` and waits for that copy.  The plan may
  * be destroyed afterwards.  Errors: ZS_EINVAL, ZS_ENOMEM, ZS_EHIP.
+ *
+ * Read from the environment at this call (zero_offload_init reads the second):
+ *   ZS_WAVES_PER_CU           resident waves per CU of the step kernels, 3..64,
+ *                             or 0 for no cap; unset: a measured table by M and
+ *                             shard size.
+ *   ZS_MAX_GROUPS_PER_LAUNCH  work-groups per kernel launch, > 0.  A grid larger
+ *                             than one dispatch carries (2^32 - 1 work-items,
+ *                             reached by shards beyond 2^34 elements) is always
+ *                             issued as consecutive launches; this lowers the
+ *                             slice size, which lets tests split small shards.
+ *                             Results do not depend on it.
  */
 int zero_shard_init(zs_ctx **out, const zs_plan *plan, int32_t M, void *param_bf16,
                     float *master, float *exp_avg, float *exp_avg_sq, void *workspace,

@@ -21,6 +21,13 @@ thread_local std::string g_last_error;
 
 void set_error(const std::string& msg) { g_last_error = msg; }
 
+int64_t max_groups_from_env() {
+  const char* env = getenv("ZS_MAX_GROUPS_PER_LAUNCH");
+  if (!env || !*env) return 0;
+  const long long v = strtoll(env, nullptr, 10);
+  return v > 0 ? (int64_t)v : 0;
+}
+
 }  // namespace zs
 
 struct zs_ctx {
@@ -31,6 +38,7 @@ struct zs_ctx {
   int64_t shard_len = 0, n_pieces = 0, canon_len = 0;
   int32_t n_runs = 0;
   int32_t waves_per_cu = 0, waves_per_cu_staged = 0;
+  int64_t max_groups = 0;  // work-groups per launch slice (0: the dispatch limit)
   uint16_t* param = nullptr;
   float* master = nullptr;
   float* m = nullptr;
@@ -326,6 +334,7 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   c->waves_per_cu = default_waves_per_cu(M, plan->shard_len, n_cu);
   // the staged step reads 16 B of gradient per lane, as many bytes as M = 2
   c->waves_per_cu_staged = default_waves_per_cu(2, plan->shard_len, n_cu);
+  c->max_groups = zs::max_groups_from_env();
   c->param = static_cast<uint16_t*>(param_bf16);
   c->master = master;
   c->m = exp_avg;
@@ -364,7 +373,8 @@ int enqueue_step(zs_ctx* ctx, const zs::GradPtrs& g, const zs::StepConsts& k, bo
   float* stage = (need_norm && !external_sumsq) ? stage_area(ctx) : nullptr;
   if (need_norm) {
     if (!external_sumsq) {
-      e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), stage, ctx->stream);
+      e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), stage, ctx->max_groups,
+                           ctx->stream);
       if (e != hipSuccess) return ehip("zero_shard_step: norm pass", e);
     }
     e = zs::launch_finalize(final_partials(ctx), zs::final_partials(ctx->shard_len),
@@ -375,11 +385,11 @@ int enqueue_step(zs_ctx* ctx, const zs::GradPtrs& g, const zs::StepConsts& k, bo
   if (stage)
     e = zs::launch_step_staged(false, stage, ctx->master, ctx->m, ctx->v, ctx->param,
                                ctx->shard_len, run_table(ctx), sc, k, nullptr,
-                               ctx->waves_per_cu_staged, ctx->stream);
+                               ctx->waves_per_cu_staged, ctx->max_groups, ctx->stream);
   else
     e = zs::launch_step(ctx->M, need_norm, g, ctx->master, ctx->m, ctx->v, ctx->param,
                         ctx->shard_len, run_table(ctx), sc, k, ctx->waves_per_cu,
-                        ctx->stream);
+                        ctx->max_groups, ctx->stream);
   if (e != hipSuccess) return ehip("zero_shard_step: step kernel", e);
   return ZS_OK;
 }
@@ -434,7 +444,8 @@ extern "C" int zero_shard_grad_sumsq(zs_ctx* ctx, const void* const* grads, doub
   const int32_t n_final = ctx->shard_len ? zs::final_partials(ctx->shard_len) : 0;
   hipError_t e = hipSuccess;
   if (n_final)
-    e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), nullptr, ctx->stream);
+    e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), nullptr, ctx->max_groups,
+                         ctx->stream);
   if (e == hipSuccess) e = zs::launch_sumsq_total(final_partials(ctx), n_final, sumsq_dev,
                                                   ctx->stream);
   return e == hipSuccess ? ZS_OK : ehip("zero_shard_grad_sumsq", e);
@@ -467,7 +478,8 @@ int state_copy(zs_ctx* ctx, bool do_export, float* cm, float* cmm, float* cv, co
     return einval((std::string(who) + ": canonical buffers must be non-NULL").c_str());
   const hipError_t e = zs::launch_state_copy(
       do_export, ctx->fp16, reinterpret_cast<const zs::Piece*>(ctx->ws + ctx->lay.pieces_off),
-      ctx->n_pieces, ctx->master, ctx->m, ctx->v, ctx->param, cm, cmm, cv, ctx->stream);
+      ctx->n_pieces, ctx->master, ctx->m, ctx->v, ctx->param, cm, cmm, cv, ctx->max_groups,
+      ctx->stream);
   return e == hipSuccess ? ZS_OK : ehip(who, e);
 }
 
@@ -527,11 +539,11 @@ int amp_finish(zs_ctx* ctx, const zs::GradPtrs& g, zs::AmpState* st, const zs::A
       e = zs::launch_step_staged(true, stage_area(ctx), ctx->master, ctx->m, ctx->v, ctx->param,
                                  ctx->shard_len, run_table(ctx), scalars(ctx),
                                  zs::StepConsts{}, device_consts(ctx),
-                                 ctx->waves_per_cu_staged, ctx->stream);
+                                 ctx->waves_per_cu_staged, ctx->max_groups, ctx->stream);
     else
       e = zs::launch_step_f16(ctx->M, g, ctx->master, ctx->m, ctx->v, ctx->param,
                               ctx->shard_len, run_table(ctx), scalars(ctx), device_consts(ctx),
-                              ctx->waves_per_cu, ctx->stream);
+                              ctx->waves_per_cu, ctx->max_groups, ctx->stream);
     if (e != hipSuccess) return ehip((w + ": step kernel").c_str(), e);
   }
   if (grad_norm_out) {
@@ -563,7 +575,7 @@ extern "C" int zero_shard_step_amp(zs_ctx* ctx, const void* const* grads, float 
   zs::AmpState* st = reinterpret_cast<zs::AmpState*>(state_dev);
   if (ctx->shard_len > 0) {
     const hipError_t e = zs::launch_sumsq_f16(ctx->M, g, ctx->shard_len, partials(ctx), st,
-                                              stage_area(ctx), ctx->stream);
+                                              stage_area(ctx), ctx->max_groups, ctx->stream);
     if (e != hipSuccess) return ehip("zero_shard_step_amp: norm pass", e);
   }
   return amp_finish(ctx, g, st, p, nullptr, grad_norm_out, who);
@@ -586,7 +598,7 @@ extern "C" int zero_shard_grad_sumsq_amp(zs_ctx* ctx, const void* const* grads,
   if (n_final)
     e = zs::launch_sumsq_f16(ctx->M, g, ctx->shard_len, partials(ctx),
                              reinterpret_cast<const zs::AmpState*>(state_dev), stage_area(ctx),
-                             ctx->stream);
+                             ctx->max_groups, ctx->stream);
   if (e == hipSuccess)
     e = zs::launch_sumsq_total(final_partials(ctx), n_final, sumsq_dev, ctx->stream);
   return e == hipSuccess ? ZS_OK : ehip("zero_shard_grad_sumsq_amp", e);

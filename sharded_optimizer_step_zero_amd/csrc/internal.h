@@ -147,12 +147,18 @@ int64_t level1_partials(int64_t shard_len);
 int64_t sumsq_partials(int64_t shard_len);
 int32_t final_partials(int64_t shard_len);
 
-// Kernel launchers (kernels.hip).  All enqueue on `stream`.
+// ZS_MAX_GROUPS_PER_LAUNCH from the environment (0 when unset or invalid).
+int64_t max_groups_from_env();
+
+// Kernel launchers (kernels.hip).  All enqueue on `stream`.  A grid beyond what
+// one dispatch carries (2^32 - 1 work-items) goes out as consecutive slices;
+// max_groups > 0 caps the work-groups of each slice below that (a context takes
+// it from ZS_MAX_GROUPS_PER_LAUNCH at init; 0 leaves only the dispatch limit).
 // The norm pass over a non-empty shard: both partial levels into `partials`.
 // stage (nullable): also store the fp32 averages, shard_len floats, for
 // launch_step_staged.
 hipError_t launch_sumsq(int M, const GradPtrs& g, int64_t shard_len, double* partials,
-                        float* stage, hipStream_t stream);
+                        float* stage, int64_t max_groups, hipStream_t stream);
 // Reduces the partials (or takes *external_sumsq when non-null) into *out.
 hipError_t launch_finalize(const double* partials, int32_t n_partials,
                            const double* external_sumsq, float max_norm, int clip,
@@ -163,7 +169,8 @@ hipError_t launch_sumsq_total(const double* partials, int32_t n_partials, double
 // step that also computes the step constants on the device and updates the
 // scaler, the step kernel, and the scaler initialisation.
 hipError_t launch_sumsq_f16(int M, const GradPtrs& g, int64_t shard_len, double* partials,
-                            const AmpState* st, float* stage, hipStream_t stream);
+                            const AmpState* st, float* stage, int64_t max_groups,
+                            hipStream_t stream);
 // external (nullable): a global sum of squares used instead of the partials.
 hipError_t launch_amp_finalize(const double* partials, int32_t n_partials,
                                const double* external, AmpState* st, const AmpParams& p,
@@ -171,14 +178,14 @@ hipError_t launch_amp_finalize(const double* partials, int32_t n_partials,
 hipError_t launch_step_f16(int M, const GradPtrs& g, float* master, float* m, float* v,
                            uint16_t* param, int64_t shard_len, const RunTable& rt,
                            const ClipScalars* clip, const StepConsts* k, int32_t waves_per_cu,
-                           hipStream_t stream);
+                           int64_t max_groups, hipStream_t stream);
 hipError_t launch_amp_state_init(AmpState* st, float scale, hipStream_t stream);
 // The step on the averages a norm pass staged (amp: constants *kd and an fp16
 // param; otherwise kh and a bf16 param).
 hipError_t launch_step_staged(bool amp, const float* stage, float* master, float* m, float* v,
                               uint16_t* param, int64_t shard_len, const RunTable& rt,
                               const ClipScalars* clip, const StepConsts& kh, const StepConsts* kd,
-                              int32_t waves_per_cu, hipStream_t stream);
+                              int32_t waves_per_cu, int64_t max_groups, hipStream_t stream);
 
 // waves_per_cu > 0 caps the resident waves per CU of the step kernel (0: no cap).
 // Copies fp32 master/m/v between the shard and the canonical order over the
@@ -187,11 +194,12 @@ hipError_t launch_step_staged(bool amp, const float* stage, float* master, float
 // imported elements).
 hipError_t launch_state_copy(bool do_export, bool param_f16, const Piece* pieces,
                              int64_t n_pieces, float* master, float* m, float* v, uint16_t* param,
-                             float* c_master, float* c_m, float* c_v, hipStream_t stream);
+                             float* c_master, float* c_m, float* c_v, int64_t max_groups,
+                             hipStream_t stream);
 hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, float* m,
                        float* v, uint16_t* param, int64_t shard_len, const RunTable& rt,
                        const ClipScalars* clip, const StepConsts& k, int32_t waves_per_cu,
-                       hipStream_t stream);
+                       int64_t max_groups, hipStream_t stream);
 
 }  // namespace zs
 

@@ -111,14 +111,14 @@ __device__ __forceinline__ int32_t find_run(const Run* __restrict__ runs, int32_
   return lo;
 }
 
-// Decay flag (0 or 1) of element e of the tile starting at tile0 (tile index
-// blockIdx.x).  One uniform load of the tile's 2 bits; only a tile that
-// straddles a run boundary looks the run up per lane, from a uniform binary
-// search for the tile's first run (runs[n_runs] is a sentinel past the shard).
-__device__ __forceinline__ uint32_t decay_flag(const RunTable& rt, int64_t tile0, int64_t e) {
+// Decay flag (0 or 1) of element e of tile `tile`, which starts at element
+// tile0.  One uniform load of the tile's 2 bits; only a tile that straddles a
+// run boundary looks the run up per lane, from a uniform binary search for the
+// tile's first run (runs[n_runs] is a sentinel past the shard).
+__device__ __forceinline__ uint32_t decay_flag(const RunTable& rt, int64_t tile, int64_t tile0,
+                                               int64_t e) {
   if (rt.n_runs == 1) return (uint32_t)rt.runs[0].flags & 1u;
-  const uint32_t t = blockIdx.x;
-  const uint32_t f = (rt.tile_flags[t >> 4] >> ((t & 15u) * 2u)) & 3u;
+  const uint32_t f = (rt.tile_flags[tile >> 4] >> ((uint32_t)(tile & 15) * 2u)) & 3u;
   if (!(f & 2u)) return f;
   int32_t r = find_run(rt.runs, rt.n_runs, tile0);
   while (rt.runs[r + 1].start <= e) r++;
@@ -173,8 +173,9 @@ template <int M, bool CLIP>
 __global__ __launch_bounds__(kStepLanes) void step_kernel(
     GradPtrs g, float* __restrict__ master, float* __restrict__ mom1, float* __restrict__ mom2,
     uint16_t* __restrict__ param, int64_t n, RunTable rt, const ClipScalars* __restrict__ clip,
-    StepConsts k) {
-  const int64_t tile0 = (int64_t)blockIdx.x * kTile;
+    StepConsts k, int64_t group0) {
+  const int64_t tile = group0 + blockIdx.x;
+  const int64_t tile0 = tile * kTile;
   const int64_t e = tile0 + (int64_t)threadIdx.x * kStepVec;
   if (e >= n) return;  // n is a multiple of 8: a lane's 4 elements are all in or all out
 
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kStepLanes) void step_kernel(
   f32x4 v4 = ld_stream(reinterpret_cast<const f32x4*>(mom2 + e));
 
   // the tile's decay flag, issued after the vector loads
-  const float d = decay_flag(rt, tile0, e) ? k.decay_mul : 1.0f;
+  const float d = decay_flag(rt, tile, tile0, e) ? k.decay_mul : 1.0f;
   float coef = 1.0f;
   if (CLIP) {
     if (clip->skip) return;  // uniform: the whole grid leaves the state untouched
@@ -249,8 +250,10 @@ __device__ __forceinline__ double block_sum(double x) {
 template <int M, bool STAGE>
 __global__ __launch_bounds__(kThreads) void sumsq_kernel(GradPtrs g, int64_t n,
                                                          double* __restrict__ partials,
-                                                         float* __restrict__ stage) {
-  const int64_t base = (int64_t)blockIdx.x * kNormTile + (int64_t)threadIdx.x * 4;
+                                                         float* __restrict__ stage,
+                                                         int64_t group0) {
+  const int64_t blk = group0 + blockIdx.x;
+  const int64_t base = blk * kNormTile + (int64_t)threadIdx.x * 4;
   // every load of both halves first: a staged store must not hold the second
   // half's loads back (the compiler cannot tell stage from the contributions)
   bool in[2];
@@ -285,13 +288,13 @@ __global__ __launch_bounds__(kThreads) void sumsq_kernel(GradPtrs g, int64_t n,
     if (STAGE) {
       f32x4 a;
       a[0] = s[0]; a[1] = s[1]; a[2] = s[2]; a[3] = s[3];
-      st_out(out_rsrc(stage + (int64_t)blockIdx.x * kNormTile + h * (kNormTile / 2),
+      st_out(out_rsrc(stage + blk * kNormTile + h * (kNormTile / 2),
                       (int)(kNormTile / 2) * 4),
              threadIdx.x * 16, a);
     }
   }
   const double t = block_sum(acc);
-  if (threadIdx.x == 0) partials[blockIdx.x] = t;
+  if (threadIdx.x == 0) partials[blk] = t;
 }
 
 // Norm pass, level 2: workgroup b sums partials [b*kLevel2, (b+1)*kLevel2) in a
@@ -375,9 +378,10 @@ template <bool EXPORT, bool F16>
 __global__ __launch_bounds__(kThreads) void state_copy_kernel(
     const Piece* __restrict__ pieces, float* __restrict__ master, float* __restrict__ mom1,
     float* __restrict__ mom2, uint16_t* __restrict__ param, float* __restrict__ c_master,
-    float* __restrict__ c_m, float* __restrict__ c_v) {
-  const Piece whole = pieces[blockIdx.x / kCopySplit];
-  const int32_t part = (int32_t)(blockIdx.x % kCopySplit) * kCopyPart;
+    float* __restrict__ c_m, float* __restrict__ c_v, int64_t group0) {
+  const int64_t grp = group0 + blockIdx.x;
+  const Piece whole = pieces[grp / kCopySplit];
+  const int32_t part = (int32_t)(grp % kCopySplit) * kCopyPart;
   if (part >= whole.len) return;
   Piece pc = whole;
   pc.shard_off += part;
@@ -442,9 +446,11 @@ template <int M, bool STAGE>
 __global__ __launch_bounds__(kThreads) void sumsq_f16_kernel(GradPtrs g, int64_t n,
                                                              double* __restrict__ partials,
                                                              const AmpState* __restrict__ st,
-                                                             float* __restrict__ stage) {
+                                                             float* __restrict__ stage,
+                                                             int64_t group0) {
   const float inv = (float)(1.0 / (double)st->scale);
-  const int64_t base = (int64_t)blockIdx.x * kNormTile + (int64_t)threadIdx.x * 4;
+  const int64_t blk = group0 + blockIdx.x;
+  const int64_t base = blk * kNormTile + (int64_t)threadIdx.x * 4;
   bool in[2];
   u32x2 w[2][M];
 #pragma unroll
@@ -477,13 +483,13 @@ __global__ __launch_bounds__(kThreads) void sumsq_f16_kernel(GradPtrs g, int64_t
     if (STAGE) {
       f32x4 a;
       a[0] = s[0]; a[1] = s[1]; a[2] = s[2]; a[3] = s[3];
-      st_out(out_rsrc(stage + (int64_t)blockIdx.x * kNormTile + h * (kNormTile / 2),
+      st_out(out_rsrc(stage + blk * kNormTile + h * (kNormTile / 2),
                       (int)(kNormTile / 2) * 4),
              threadIdx.x * 16, a);
     }
   }
   const double t = block_sum(acc);
-  if (threadIdx.x == 0) partials[blockIdx.x] = t;
+  if (threadIdx.x == 0) partials[blk] = t;
 }
 
 // external (nullable): the global sum of squares over every rank's shard, which
@@ -533,8 +539,9 @@ template <int M>
 __global__ __launch_bounds__(kStepLanes) void step_f16_kernel(
     GradPtrs g, float* __restrict__ master, float* __restrict__ mom1, float* __restrict__ mom2,
     uint16_t* __restrict__ param, int64_t n, RunTable rt, const ClipScalars* __restrict__ clip,
-    const StepConsts* __restrict__ kp) {
-  const int64_t tile0 = (int64_t)blockIdx.x * kTile;
+    const StepConsts* __restrict__ kp, int64_t group0) {
+  const int64_t tile = group0 + blockIdx.x;
+  const int64_t tile0 = tile * kTile;
   const int64_t e = tile0 + (int64_t)threadIdx.x * kStepVec;
   if (e >= n) return;
   u32x2 w[M];
@@ -543,7 +550,7 @@ __global__ __launch_bounds__(kStepLanes) void step_f16_kernel(
   f32x4 p4 = ld_stream(reinterpret_cast<const f32x4*>(master + e));
   f32x4 m4 = ld_stream(reinterpret_cast<const f32x4*>(mom1 + e));
   f32x4 v4 = ld_stream(reinterpret_cast<const f32x4*>(mom2 + e));
-  const uint32_t dflag = decay_flag(rt, tile0, e);
+  const uint32_t dflag = decay_flag(rt, tile, tile0, e);
   if (clip->skip) return;  // found-inf: uniform over the grid
   const StepConsts k = *kp;
   const float inv = clip->inv_scale, coef = clip->coef;
@@ -594,15 +601,17 @@ template <bool AMP>
 __global__ __launch_bounds__(kStepLanes) void step_staged_kernel(
     const float* __restrict__ stage, float* __restrict__ master, float* __restrict__ mom1,
     float* __restrict__ mom2, uint16_t* __restrict__ param, int64_t n, RunTable rt,
-    const ClipScalars* __restrict__ clip, StepConsts kh, const StepConsts* __restrict__ kd) {
-  const int64_t tile0 = (int64_t)blockIdx.x * kTile;
+    const ClipScalars* __restrict__ clip, StepConsts kh, const StepConsts* __restrict__ kd,
+    int64_t group0) {
+  const int64_t tile = group0 + blockIdx.x;
+  const int64_t tile0 = tile * kTile;
   const int64_t e = tile0 + (int64_t)threadIdx.x * kStepVec;
   if (e >= n) return;
   f32x4 g4 = ld_stream(reinterpret_cast<const f32x4*>(stage + e));
   f32x4 p4 = ld_stream(reinterpret_cast<const f32x4*>(master + e));
   f32x4 m4 = ld_stream(reinterpret_cast<const f32x4*>(mom1 + e));
   f32x4 v4 = ld_stream(reinterpret_cast<const f32x4*>(mom2 + e));
-  const uint32_t dflag = decay_flag(rt, tile0, e);
+  const uint32_t dflag = decay_flag(rt, tile, tile0, e);
   if (clip->skip) return;  // uniform over the grid
   const StepConsts k = AMP ? *kd : kh;
   const float coef = clip->coef;  // 1 when the call does not clip
@@ -646,17 +655,36 @@ size_t step_lds(int32_t waves_per_cu) {
   return (kLdsPerCu / (size_t)waves_per_cu) & ~(size_t)255;
 }
 
+// A dispatch carries at most 2^32 - 1 work-items (its grid size is a 32-bit
+// count of work-items), which a step grid passes beyond 2^34 elements.  Larger
+// grids go out as consecutive slices of whole work-groups on the same stream;
+// launch(group0, groups) issues one slice and its kernel adds group0 to
+// blockIdx.x.  max_groups > 0 lowers the slice size.
+template <typename F>
+hipError_t for_slices(int64_t groups, int block, int64_t max_groups, F&& launch) {
+  const int64_t lim = (int64_t)0xffffffff / block;
+  const int64_t per = (max_groups > 0 && max_groups < lim) ? max_groups : lim;
+  for (int64_t g0 = 0; g0 < groups; g0 += per) {
+    launch(g0, (unsigned)(groups - g0 < per ? groups - g0 : per));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <int M>
 hipError_t launch_sumsq_f16_m(const GradPtrs& g, int64_t shard_len, double* partials,
-                              const AmpState* st, float* stage, hipStream_t stream) {
+                              const AmpState* st, float* stage, int64_t max_groups,
+                              hipStream_t stream) {
   const int64_t p1 = (shard_len + kNormTile - 1) / kNormTile;
-  if (stage)
-    hipLaunchKernelGGL((sumsq_f16_kernel<M, true>), dim3((unsigned)p1), dim3(kThreads),
-                       stage_lds(M), stream, g, shard_len, partials, st, stage);
-  else
-    hipLaunchKernelGGL((sumsq_f16_kernel<M, false>), dim3((unsigned)p1), dim3(kThreads), 0,
-                       stream, g, shard_len, partials, st, stage);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = for_slices(p1, kThreads, max_groups, [&](int64_t g0, unsigned n) {
+    if (stage)
+      hipLaunchKernelGGL((sumsq_f16_kernel<M, true>), dim3(n), dim3(kThreads), stage_lds(M),
+                         stream, g, shard_len, partials, st, stage, g0);
+    else
+      hipLaunchKernelGGL((sumsq_f16_kernel<M, false>), dim3(n), dim3(kThreads), 0, stream, g,
+                         shard_len, partials, st, stage, g0);
+  });
   if (e != hipSuccess) return e;
   const int64_t p2 = (p1 + kLevel2 - 1) / kLevel2;
   hipLaunchKernelGGL(sum_blocks_kernel, dim3((unsigned)p2), dim3(kThreads), 0, stream,
@@ -668,40 +696,42 @@ template <int M>
 hipError_t launch_step_f16_m(const GradPtrs& g, float* master, float* m, float* v,
                              uint16_t* param, int64_t n, const RunTable& rt,
                              const ClipScalars* clip, const StepConsts* k, size_t lds,
-                             hipStream_t stream) {
+                             int64_t max_groups, hipStream_t stream) {
   const int64_t tiles = (n + kTile - 1) / kTile;
-  hipLaunchKernelGGL((step_f16_kernel<M>), dim3((unsigned)tiles), dim3(kStepLanes), lds, stream,
-                     g, master, m, v, param, n, rt, clip, k);
-  return hipGetLastError();
+  return for_slices(tiles, kStepLanes, max_groups, [&](int64_t g0, unsigned nt) {
+    hipLaunchKernelGGL((step_f16_kernel<M>), dim3(nt), dim3(kStepLanes), lds, stream, g, master,
+                       m, v, param, n, rt, clip, k, g0);
+  });
 }
 
 template <int M>
 hipError_t launch_step_m(bool use_clip, const GradPtrs& g, float* master, float* m, float* v,
                          uint16_t* param, int64_t n, const RunTable& rt,
                          const ClipScalars* clip, const StepConsts& k, size_t lds,
-                         hipStream_t stream) {
+                         int64_t max_groups, hipStream_t stream) {
   const int64_t tiles = (n + kTile - 1) / kTile;
-  const dim3 grid((unsigned)tiles), block(kStepLanes);
-  if (use_clip)
-    hipLaunchKernelGGL((step_kernel<M, true>), grid, block, lds, stream, g, master, m, v, param,
-                       n, rt, clip, k);
-  else
-    hipLaunchKernelGGL((step_kernel<M, false>), grid, block, lds, stream, g, master, m, v, param,
-                       n, rt, clip, k);
-  return hipGetLastError();
+  return for_slices(tiles, kStepLanes, max_groups, [&](int64_t g0, unsigned nt) {
+    if (use_clip)
+      hipLaunchKernelGGL((step_kernel<M, true>), dim3(nt), dim3(kStepLanes), lds, stream, g,
+                         master, m, v, param, n, rt, clip, k, g0);
+    else
+      hipLaunchKernelGGL((step_kernel<M, false>), dim3(nt), dim3(kStepLanes), lds, stream, g,
+                         master, m, v, param, n, rt, clip, k, g0);
+  });
 }
 
 template <int M>
 hipError_t launch_sumsq_m(const GradPtrs& g, int64_t shard_len, double* partials, float* stage,
-                          hipStream_t stream) {
+                          int64_t max_groups, hipStream_t stream) {
   const int64_t p1 = (shard_len + kNormTile - 1) / kNormTile;
-  if (stage)
-    hipLaunchKernelGGL((sumsq_kernel<M, true>), dim3((unsigned)p1), dim3(kThreads),
-                       stage_lds(M), stream, g, shard_len, partials, stage);
-  else
-    hipLaunchKernelGGL((sumsq_kernel<M, false>), dim3((unsigned)p1), dim3(kThreads), 0, stream,
-                       g, shard_len, partials, stage);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = for_slices(p1, kThreads, max_groups, [&](int64_t g0, unsigned n) {
+    if (stage)
+      hipLaunchKernelGGL((sumsq_kernel<M, true>), dim3(n), dim3(kThreads), stage_lds(M), stream,
+                         g, shard_len, partials, stage, g0);
+    else
+      hipLaunchKernelGGL((sumsq_kernel<M, false>), dim3(n), dim3(kThreads), 0, stream, g,
+                         shard_len, partials, stage, g0);
+  });
   if (e != hipSuccess) return e;
   const int64_t p2 = (p1 + kLevel2 - 1) / kLevel2;
   hipLaunchKernelGGL(sum_blocks_kernel, dim3((unsigned)p2), dim3(kThreads), 0, stream,
@@ -748,56 +778,59 @@ int32_t final_partials(int64_t shard_len) {
     default: return hipErrorInvalidValue; \
   }
 
-// A step launch must fit the grid limit and have its run data: a run table,
-// and the tile flags when there is more than one run.
-static bool step_args_ok(int64_t shard_len, const RunTable& rt) {
-  return (shard_len + kTile - 1) / kTile <= 0x7fffffff && rt.n_runs >= 1 && rt.runs &&
-         (rt.n_runs == 1 || rt.tile_flags);
+// A step launch needs its run data: a run table, and the tile flags when there
+// is more than one run.
+static bool step_args_ok(const RunTable& rt) {
+  return rt.n_runs >= 1 && rt.runs && (rt.n_runs == 1 || rt.tile_flags);
 }
 
 hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, float* m,
                        float* v, uint16_t* param, int64_t shard_len, const RunTable& rt,
                        const ClipScalars* clip, const StepConsts& k, int32_t waves_per_cu,
-                       hipStream_t stream) {
+                       int64_t max_groups, hipStream_t stream) {
   if (shard_len <= 0) return hipSuccess;
-  if (!step_args_ok(shard_len, rt)) return hipErrorInvalidValue;
+  if (!step_args_ok(rt)) return hipErrorInvalidValue;
   const size_t lds = step_lds(waves_per_cu);
 #define ZS_CALL_STEP(X) \
-  launch_step_m<X>(use_clip, g, master, m, v, param, shard_len, rt, clip, k, lds, stream)
+  launch_step_m<X>(use_clip, g, master, m, v, param, shard_len, rt, clip, k, lds, max_groups, \
+                   stream)
   ZS_DISPATCH_M(M, ZS_CALL_STEP)
 #undef ZS_CALL_STEP
 }
 
 hipError_t launch_sumsq(int M, const GradPtrs& g, int64_t shard_len, double* partials,
-                        float* stage, hipStream_t stream) {
+                        float* stage, int64_t max_groups, hipStream_t stream) {
   if (shard_len <= 0 || level1_partials(shard_len) > 0x7fffffff) return hipErrorInvalidValue;
-#define ZS_CALL_SUMSQ(X) launch_sumsq_m<X>(g, shard_len, partials, stage, stream)
+#define ZS_CALL_SUMSQ(X) launch_sumsq_m<X>(g, shard_len, partials, stage, max_groups, stream)
   ZS_DISPATCH_M(M, ZS_CALL_SUMSQ)
 #undef ZS_CALL_SUMSQ
 }
 
 hipError_t launch_state_copy(bool do_export, bool param_f16, const Piece* pieces,
                              int64_t n_pieces, float* master, float* m, float* v, uint16_t* param,
-                             float* c_master, float* c_m, float* c_v, hipStream_t stream) {
+                             float* c_master, float* c_m, float* c_v, int64_t max_groups,
+                             hipStream_t stream) {
   if (n_pieces <= 0) return hipSuccess;
-  if (n_pieces > 0x7fffffff / kCopySplit) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(n_pieces * kCopySplit)), block(kThreads);
-  if (do_export)
-    hipLaunchKernelGGL((state_copy_kernel<true, false>), grid, block, 0, stream, pieces, master, m,
-                       v, param, c_master, c_m, c_v);
-  else if (param_f16)
-    hipLaunchKernelGGL((state_copy_kernel<false, true>), grid, block, 0, stream, pieces, master,
-                       m, v, param, c_master, c_m, c_v);
-  else
-    hipLaunchKernelGGL((state_copy_kernel<false, false>), grid, block, 0, stream, pieces, master,
-                       m, v, param, c_master, c_m, c_v);
-  return hipGetLastError();
+  const dim3 block(kThreads);
+  return for_slices(n_pieces * kCopySplit, kThreads, max_groups, [&](int64_t g0, unsigned n) {
+    if (do_export)
+      hipLaunchKernelGGL((state_copy_kernel<true, false>), dim3(n), block, 0, stream, pieces,
+                         master, m, v, param, c_master, c_m, c_v, g0);
+    else if (param_f16)
+      hipLaunchKernelGGL((state_copy_kernel<false, true>), dim3(n), block, 0, stream, pieces,
+                         master, m, v, param, c_master, c_m, c_v, g0);
+    else
+      hipLaunchKernelGGL((state_copy_kernel<false, false>), dim3(n), block, 0, stream, pieces,
+                         master, m, v, param, c_master, c_m, c_v, g0);
+  });
 }
 
 hipError_t launch_sumsq_f16(int M, const GradPtrs& g, int64_t shard_len, double* partials,
-                            const AmpState* st, float* stage, hipStream_t stream) {
+                            const AmpState* st, float* stage, int64_t max_groups,
+                            hipStream_t stream) {
   if (shard_len <= 0 || level1_partials(shard_len) > 0x7fffffff) return hipErrorInvalidValue;
-#define ZS_CALL_SUMSQ16(X) launch_sumsq_f16_m<X>(g, shard_len, partials, st, stage, stream)
+#define ZS_CALL_SUMSQ16(X) \
+  launch_sumsq_f16_m<X>(g, shard_len, partials, st, stage, max_groups, stream)
   ZS_DISPATCH_M(M, ZS_CALL_SUMSQ16)
 #undef ZS_CALL_SUMSQ16
 }
@@ -813,12 +846,12 @@ hipError_t launch_amp_finalize(const double* partials, int32_t n_partials,
 hipError_t launch_step_f16(int M, const GradPtrs& g, float* master, float* m, float* v,
                            uint16_t* param, int64_t shard_len, const RunTable& rt,
                            const ClipScalars* clip, const StepConsts* k, int32_t waves_per_cu,
-                           hipStream_t stream) {
+                           int64_t max_groups, hipStream_t stream) {
   if (shard_len <= 0) return hipSuccess;
-  if (!step_args_ok(shard_len, rt)) return hipErrorInvalidValue;
+  if (!step_args_ok(rt)) return hipErrorInvalidValue;
   const size_t lds = step_lds(waves_per_cu);
 #define ZS_CALL_STEP16(X) \
-  launch_step_f16_m<X>(g, master, m, v, param, shard_len, rt, clip, k, lds, stream)
+  launch_step_f16_m<X>(g, master, m, v, param, shard_len, rt, clip, k, lds, max_groups, stream)
   ZS_DISPATCH_M(M, ZS_CALL_STEP16)
 #undef ZS_CALL_STEP16
 }
@@ -826,18 +859,19 @@ hipError_t launch_step_f16(int M, const GradPtrs& g, float* master, float* m, fl
 hipError_t launch_step_staged(bool amp, const float* stage, float* master, float* m, float* v,
                               uint16_t* param, int64_t shard_len, const RunTable& rt,
                               const ClipScalars* clip, const StepConsts& kh, const StepConsts* kd,
-                              int32_t waves_per_cu, hipStream_t stream) {
+                              int32_t waves_per_cu, int64_t max_groups, hipStream_t stream) {
   if (shard_len <= 0) return hipSuccess;
-  if (!step_args_ok(shard_len, rt)) return hipErrorInvalidValue;
+  if (!step_args_ok(rt)) return hipErrorInvalidValue;
   const size_t lds = step_lds(waves_per_cu);
-  const dim3 grid((unsigned)((shard_len + kTile - 1) / kTile)), block(kStepLanes);
-  if (amp)
-    hipLaunchKernelGGL((step_staged_kernel<true>), grid, block, lds, stream, stage, master, m, v,
-                       param, shard_len, rt, clip, kh, kd);
-  else
-    hipLaunchKernelGGL((step_staged_kernel<false>), grid, block, lds, stream, stage, master, m, v,
-                       param, shard_len, rt, clip, kh, kd);
-  return hipGetLastError();
+  const int64_t tiles = (shard_len + kTile - 1) / kTile;
+  return for_slices(tiles, kStepLanes, max_groups, [&](int64_t g0, unsigned nt) {
+    if (amp)
+      hipLaunchKernelGGL((step_staged_kernel<true>), dim3(nt), dim3(kStepLanes), lds, stream,
+                         stage, master, m, v, param, shard_len, rt, clip, kh, kd, g0);
+    else
+      hipLaunchKernelGGL((step_staged_kernel<false>), dim3(nt), dim3(kStepLanes), lds, stream,
+                         stage, master, m, v, param, shard_len, rt, clip, kh, kd, g0);
+  });
 }
 
 hipError_t launch_amp_state_init(AmpState* st, float scale, hipStream_t stream) {

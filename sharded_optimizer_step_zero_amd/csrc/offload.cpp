@@ -113,6 +113,7 @@ struct zs_offload {
   uint32_t flags = 0;
   bool fp16 = false;  // ZS_FP16: fp16 gradients and param, zero_offload_step_amp
   int64_t shard_len = 0, chunk = 0;
+  int64_t max_groups = 0;  // work-groups per launch slice (0: the dispatch limit)
   std::vector<zs::HostRun> runs;
   std::vector<std::pair<int64_t, int64_t>> chunks;
   uint16_t* param = nullptr;
@@ -182,6 +183,7 @@ extern "C" int zero_offload_init(zs_offload** out, const zs_plan* plan, int32_t 
   std::unique_ptr<zs_offload> c(new (std::nothrow) zs_offload);
   if (!c) return enomem("zero_offload_init: out of host memory");
   c->M = M;
+  c->max_groups = zs::max_groups_from_env();
   c->flags = flags;
   c->fp16 = (flags & ZS_FP16) != 0;
   c->shard_len = plan->shard_len;
@@ -273,7 +275,7 @@ int pipeline(zs_offload* c, const zs::HostConsts* k_host, bool out_f16, double* 
       const int64_t off = c->chunks[ci].first, len = c->chunks[ci].second;
       zs::GradPtrs g = *per_chunk;
       for (int j = 0; j < c->M; j++) g.p[j] += off;
-      e = zs::launch_sumsq(c->M, g, len, partials, stage + off, c->stream);
+      e = zs::launch_sumsq(c->M, g, len, partials, stage + off, c->max_groups, c->stream);
       if (e == hipSuccess) e = hipEventRecord(c->chunk_done[ci], c->stream);
     }
   } else {
@@ -371,7 +373,7 @@ extern "C" int zero_offload_step(zs_offload* c, const void* const* grads, float 
   double* partials = reinterpret_cast<double*>(c->ws + c->lay.partials_off);
   zs::ClipScalars* sc_dev = reinterpret_cast<zs::ClipScalars*>(c->ws + c->lay.scalars_off);
   // the device part: reduce, stage the averages, norm and clip scalars
-  hipError_t e = zs::launch_sumsq(c->M, g, S, partials, stage, c->stream);
+  hipError_t e = zs::launch_sumsq(c->M, g, S, partials, stage, c->max_groups, c->stream);
   if (e == hipSuccess)
     e = zs::launch_finalize(partials + zs::level1_partials(S), zs::final_partials(S), nullptr,
                             max_grad_norm, max_grad_norm > 0.0f ? 1 : 0,
@@ -403,7 +405,8 @@ extern "C" int zero_offload_step_amp(zs_offload* c, const void* const* grads, fl
   // step constants at t = applied + 1, all on the device; an empty shard still
   // runs the finalize, so its scaler advances like every other rank's
   hipError_t e = hipSuccess;
-  if (S > 0) e = zs::launch_sumsq_f16(c->M, g, S, partials, st, stage, c->stream);
+  if (S > 0)
+    e = zs::launch_sumsq_f16(c->M, g, S, partials, st, stage, c->max_groups, c->stream);
   if (e == hipSuccess)
     e = zs::launch_amp_finalize(partials + zs::level1_partials(S),
                                 S ? zs::final_partials(S) : 0, nullptr, st, p,
@@ -434,8 +437,8 @@ int offload_sumsq(zs_offload* c, const void* const* grads, const zs_amp_state* s
   if (n_final)
     e = state_dev ? zs::launch_sumsq_f16(c->M, g, S, partials,
                                          reinterpret_cast<const zs::AmpState*>(state_dev),
-                                         stage, c->stream)
-                  : zs::launch_sumsq(c->M, g, S, partials, stage, c->stream);
+                                         stage, c->max_groups, c->stream)
+                  : zs::launch_sumsq(c->M, g, S, partials, stage, c->max_groups, c->stream);
   if (e == hipSuccess)
     e = zs::launch_sumsq_total(partials + zs::level1_partials(S), n_final, sumsq_dev, c->stream);
   return e == hipSuccess ? ZS_OK : zs::ehip(who, e);
