@@ -154,6 +154,8 @@ int64_t max_groups_from_env();
 // one dispatch carries (2^32 - 1 work-items) goes out as consecutive slices;
 // max_groups > 0 caps the work-groups of each slice below that (a context takes
 // it from ZS_MAX_GROUPS_PER_LAUNCH at init; 0 leaves only the dispatch limit).
+// waves_per_cu > 0 caps the resident waves per CU of a step kernel (0: no cap).
+//
 // The norm pass over a non-empty shard: both partial levels into `partials`.
 // stage (nullable): also store the fp32 averages, shard_len floats, for
 // launch_step_staged.
@@ -187,7 +189,6 @@ hipError_t launch_step_staged(bool amp, const float* stage, float* master, float
                               const ClipScalars* clip, const StepConsts& kh, const StepConsts* kd,
                               int32_t waves_per_cu, int64_t max_groups, hipStream_t stream);
 
-// waves_per_cu > 0 caps the resident waves per CU of the step kernel (0: no cap).
 // Copies fp32 master/m/v between the shard and the canonical order over the
 // piece table (export: shard -> canonical; import: canonical -> shard, which
 // also writes param = bf16_rne(master), or fp16 when param_f16, for the
@@ -196,6 +197,7 @@ hipError_t launch_state_copy(bool do_export, bool param_f16, const Piece* pieces
                              int64_t n_pieces, float* master, float* m, float* v, uint16_t* param,
                              float* c_master, float* c_m, float* c_v, int64_t max_groups,
                              hipStream_t stream);
+// The fused bf16 step (use_clip: scale by the coefficient in *clip, or skip).
 hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, float* m,
                        float* v, uint16_t* param, int64_t shard_len, const RunTable& rt,
                        const ClipScalars* clip, const StepConsts& k, int32_t waves_per_cu,
