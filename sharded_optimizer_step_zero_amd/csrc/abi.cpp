@@ -35,7 +35,7 @@ struct zs_ctx {
   uint32_t flags = 0;
   bool fp16 = false;
   bool stage = false;  // ZS_STAGE_AVERAGE
-  int64_t shard_len = 0, n_pieces = 0, canon_len = 0;
+  int64_t shard_len = 0, n_pieces = 0, n_whole_pieces = 0, canon_len = 0;
   int32_t n_runs = 0;
   int32_t waves_per_cu = 0, waves_per_cu_staged = 0;
   int64_t max_groups = 0;  // work-groups per launch slice (0: the dispatch limit)
@@ -329,6 +329,7 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   c->shard_len = plan->shard_len;
   c->n_runs = (int32_t)(table.size() - 1);
   c->n_pieces = (int64_t)plan->pieces.size();
+  c->n_whole_pieces = plan->n_whole_pieces;
   c->canon_len = plan->total_params;
   const int32_t n_cu = device_cu_count();
   c->waves_per_cu = default_waves_per_cu(M, plan->shard_len, n_cu);
@@ -478,8 +479,8 @@ int state_copy(zs_ctx* ctx, bool do_export, float* cm, float* cmm, float* cv, co
     return einval((std::string(who) + ": canonical buffers must be non-NULL").c_str());
   const hipError_t e = zs::launch_state_copy(
       do_export, ctx->fp16, reinterpret_cast<const zs::Piece*>(ctx->ws + ctx->lay.pieces_off),
-      ctx->n_pieces, ctx->master, ctx->m, ctx->v, ctx->param, cm, cmm, cv, ctx->max_groups,
-      ctx->stream);
+      ctx->n_pieces, ctx->n_whole_pieces, ctx->master, ctx->m, ctx->v, ctx->param, cm, cmm, cv,
+      ctx->max_groups, ctx->stream);
   return e == hipSuccess ? ZS_OK : ehip(who, e);
 }
 

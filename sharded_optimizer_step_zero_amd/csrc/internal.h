@@ -45,15 +45,18 @@ struct Segment {
   int32_t decay;
 };
 
-// A piece of a tensor segment (at most kPieceElems elements) for the state
-// export/import kernel: shard offset, offset in the canonical order (tensors
-// concatenated without padding), length.
+// A piece of a tensor segment for the state export/import kernel: shard
+// offset, offset in the canonical order (tensors concatenated without
+// padding), length.  A plan's piece table holds its whole pieces (kPieceElems
+// elements, copied as kPieceElems / kCopyPart parts) first, then the
+// remainder of every segment as parts of at most kCopyPart elements.
 struct Piece {
   int64_t shard_off, canon_off;
   int32_t len, pad;
 };
 static_assert(sizeof(Piece) == 24, "piece descriptor is 24 bytes");
 constexpr int64_t kPieceElems = 65536;
+constexpr int64_t kCopyPart = 256;  // elements per work-group of the copy kernel
 
 // Per-step constants, each computed in fp64 from the fp32 hyper-parameters
 // and rounded once to fp32.
@@ -194,7 +197,7 @@ hipError_t launch_step_staged(bool amp, const float* stage, float* master, float
 // also writes param = bf16_rne(master), or fp16 when param_f16, for the
 // imported elements).
 hipError_t launch_state_copy(bool do_export, bool param_f16, const Piece* pieces,
-                             int64_t n_pieces, float* master, float* m, float* v, uint16_t* param,
+                             int64_t n_pieces, int64_t n_whole, float* master, float* m, float* v, uint16_t* param,
                              float* c_master, float* c_m, float* c_v, int64_t max_groups,
                              hipStream_t stream);
 // The fused bf16 step (use_clip: scale by the coefficient in *clip, or skip).
@@ -215,6 +218,7 @@ struct zs_plan {
   std::vector<int64_t> bucket_off, bucket_len;
   std::vector<zs::Segment> segments;
   std::vector<zs::Run> runs;
-  std::vector<zs::Piece> pieces;
+  std::vector<zs::Piece> pieces;  // whole pieces first (n_whole_pieces), then parts
+  int64_t n_whole_pieces = 0;
   int64_t shard_len = 0, padded_total = 0, total_params = 0;
 };

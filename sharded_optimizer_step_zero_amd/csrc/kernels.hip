@@ -344,15 +344,25 @@ __global__ __launch_bounds__(kThreads) void sumsq_total_kernel(const double* __r
   if (threadIdx.x == 0) *out = t;
 }
 
-// State export/import: kCopySplit short-lived workgroups per piece (a piece
-// holds at most 65536 elements), each over its 1024-element part, the lanes
-// striding over it.  A piece whose six (seven on import) addresses are
-// all 16-byte aligned -- every piece when tensor sizes are multiples of 4 --
-// moves 4 elements per lane with 16-byte accesses; any other piece, and a
-// piece's last len % 4 elements, take the 4-byte path (still coalesced, 256 B
-// per wave).  The choice is per piece, so uniform over the workgroup.
-constexpr int32_t kCopyPart = 1024;
+// State export/import: one single-wave workgroup per part of at most 256
+// elements, the same shape as the step's tiles.  The piece table lists whole
+// pieces first (kCopySplit parts each, found by division) and then every other
+// part as its own entry, so no workgroup is empty.  A part whose six (seven on
+// import) addresses are all 16-byte aligned -- every part when tensor sizes
+// are multiples of 4 -- moves 4 elements per lane with 16-byte accesses; any
+// other part takes the 4-byte path (still coalesced, 256 B per wave), and a
+// 16-byte part's last len % 4 elements are copied one per lane.  The choice is
+// per part, so uniform over the workgroup.  Resident waves per CU are capped at kCopyWavesPerCu through an
+// LDS reservation, as for the step.  Measured on MI355X against 256-lane
+// workgroups over 1,024-element parts and no cap (GPT-1.3B shard, same
+// buffers): export 6.81 against 5.70 TB/s, import 6.74 against 5.72; caps 9-14
+// swept, 10 best.  On the stress layout (10k tensors, mostly unaligned
+// canonical offsets, so mostly the 4-byte path): export 4.72 against 4.59,
+// import 5.11 against 5.06.
+constexpr int kCopyLanes = 64;
 constexpr int32_t kCopySplit = (int32_t)(kPieceElems / kCopyPart);
+constexpr int kCopyWavesPerCu = 10;
+static_assert(kCopyPart == kCopyLanes * 4, "one 4-element group per lane");
 
 template <bool EXPORT, bool F16>
 __device__ __forceinline__ void copy_one(int64_t s, int64_t c, float* __restrict__ master,
@@ -375,18 +385,23 @@ __device__ __forceinline__ void copy_one(int64_t s, int64_t c, float* __restrict
 __device__ __forceinline__ bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 template <bool EXPORT, bool F16>
-__global__ __launch_bounds__(kThreads) void state_copy_kernel(
-    const Piece* __restrict__ pieces, float* __restrict__ master, float* __restrict__ mom1,
-    float* __restrict__ mom2, uint16_t* __restrict__ param, float* __restrict__ c_master,
-    float* __restrict__ c_m, float* __restrict__ c_v, int64_t group0) {
+__global__ __launch_bounds__(kCopyLanes) void state_copy_kernel(
+    const Piece* __restrict__ pieces, int64_t n_whole, float* __restrict__ master,
+    float* __restrict__ mom1, float* __restrict__ mom2, uint16_t* __restrict__ param,
+    float* __restrict__ c_master, float* __restrict__ c_m, float* __restrict__ c_v,
+    int64_t group0) {
   const int64_t grp = group0 + blockIdx.x;
-  const Piece whole = pieces[grp / kCopySplit];
-  const int32_t part = (int32_t)(grp % kCopySplit) * kCopyPart;
-  if (part >= whole.len) return;
-  Piece pc = whole;
-  pc.shard_off += part;
-  pc.canon_off += part;
-  pc.len = min(kCopyPart, whole.len - part);
+  const int64_t whole_groups = n_whole * kCopySplit;
+  Piece pc;
+  if (grp < whole_groups) {  // a part of a whole piece
+    pc = pieces[grp / kCopySplit];
+    const int64_t part = (grp % kCopySplit) * kCopyPart;
+    pc.shard_off += part;
+    pc.canon_off += part;
+    pc.len = (int32_t)kCopyPart;
+  } else {
+    pc = pieces[n_whole + (grp - whole_groups)];
+  }
   const int64_t s0 = pc.shard_off, c0 = pc.canon_off;
   const bool vec = al16(master + s0) && al16(mom1 + s0) && al16(mom2 + s0) &&
                    al16(c_master + c0) && al16(c_m + c0) && al16(c_v + c0) &&
@@ -400,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void state_copy_kernel(
     const __amdgpu_buffer_rsrc_t o1 = out_rsrc(EXPORT ? c_master + c0 : master + s0, bytes32);
     const __amdgpu_buffer_rsrc_t o2 = out_rsrc(EXPORT ? c_m + c0 : mom1 + s0, bytes32);
     const __amdgpu_buffer_rsrc_t o3 = out_rsrc(EXPORT ? c_v + c0 : mom2 + s0, bytes32);
-    for (int32_t q = threadIdx.x; q < quads; q += kThreads) {
+    for (int32_t q = threadIdx.x; q < quads; q += kCopyLanes) {
       const int64_t s = s0 + 4 * (int64_t)q, c = c0 + 4 * (int64_t)q;
       if (EXPORT) {
         const f32x4 a = ld_stream(reinterpret_cast<const f32x4*>(master + s));
@@ -426,9 +441,44 @@ __global__ __launch_bounds__(kThreads) void state_copy_kernel(
       }
     }
     done = quads << 2;
+    for (int32_t i = done + threadIdx.x; i < pc.len; i += kCopyLanes)
+      copy_one<EXPORT, F16>(s0 + i, c0 + i, master, mom1, mom2, param, c_master, c_m, c_v);
+    return;
   }
-  for (int32_t i = done + threadIdx.x; i < pc.len; i += kThreads)
-    copy_one<EXPORT, F16>(s0 + i, c0 + i, master, mom1, mom2, param, c_master, c_m, c_v);
+  // 4-byte path: lane t takes elements t, t + 64, t + 128, t + 192 of the part
+  // (each access instruction covers 256 contiguous bytes), and issues every
+  // load before its first store, so a wave keeps as many bytes in flight as
+  // on the 16-byte path.  The fp32 outputs use ordinary stores: an unaligned
+  // part shares its first and last cache lines with its neighbours, and
+  // measured on MI355X (stress layout, mostly unaligned canonical offsets)
+  // export ran 4.72 TB/s this way against 3.93 with non-temporal stores.
+  const float* src1 = EXPORT ? master + s0 : c_master + c0;
+  const float* src2 = EXPORT ? mom1 + s0 : c_m + c0;
+  const float* src3 = EXPORT ? mom2 + s0 : c_v + c0;
+  float* dst1 = EXPORT ? c_master + c0 : master + s0;
+  float* dst2 = EXPORT ? c_m + c0 : mom1 + s0;
+  float* dst3 = EXPORT ? c_v + c0 : mom2 + s0;
+  float x1[4], x2[4], x3[4];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int32_t i = (int32_t)threadIdx.x + k * kCopyLanes;
+    if (i < pc.len) {
+      x1[k] = ld_stream(src1 + i);
+      x2[k] = ld_stream(src2 + i);
+      x3[k] = ld_stream(src3 + i);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int32_t i = (int32_t)threadIdx.x + k * kCopyLanes;
+    if (i < pc.len) {
+      dst1[i] = x1[k];
+      dst2[i] = x2[k];
+      dst3[i] = x3[k];
+      if (!EXPORT)
+        __builtin_nontemporal_store((uint16_t)(F16 ? f2h(x1[k]) : to_bf16(x1[k])), param + s0 + i);
+    }
+  }
 }
 
 // ------------------------------------------------- loss-scaled fp16 path
@@ -807,21 +857,24 @@ hipError_t launch_sumsq(int M, const GradPtrs& g, int64_t shard_len, double* par
 }
 
 hipError_t launch_state_copy(bool do_export, bool param_f16, const Piece* pieces,
-                             int64_t n_pieces, float* master, float* m, float* v, uint16_t* param,
-                             float* c_master, float* c_m, float* c_v, int64_t max_groups,
-                             hipStream_t stream) {
+                             int64_t n_pieces, int64_t n_whole, float* master, float* m, float* v,
+                             uint16_t* param, float* c_master, float* c_m, float* c_v,
+                             int64_t max_groups, hipStream_t stream) {
   if (n_pieces <= 0) return hipSuccess;
-  const dim3 block(kThreads);
-  return for_slices(n_pieces * kCopySplit, kThreads, max_groups, [&](int64_t g0, unsigned n) {
+  if (n_whole < 0 || n_whole > n_pieces) return hipErrorInvalidValue;
+  const dim3 block(kCopyLanes);
+  const size_t lds = step_lds(kCopyWavesPerCu);
+  const int64_t groups = n_whole * kCopySplit + (n_pieces - n_whole);
+  return for_slices(groups, kCopyLanes, max_groups, [&](int64_t g0, unsigned n) {
     if (do_export)
-      hipLaunchKernelGGL((state_copy_kernel<true, false>), dim3(n), block, 0, stream, pieces,
-                         master, m, v, param, c_master, c_m, c_v, g0);
+      hipLaunchKernelGGL((state_copy_kernel<true, false>), dim3(n), block, lds, stream, pieces,
+                         n_whole, master, m, v, param, c_master, c_m, c_v, g0);
     else if (param_f16)
-      hipLaunchKernelGGL((state_copy_kernel<false, true>), dim3(n), block, 0, stream, pieces,
-                         master, m, v, param, c_master, c_m, c_v, g0);
+      hipLaunchKernelGGL((state_copy_kernel<false, true>), dim3(n), block, lds, stream, pieces,
+                         n_whole, master, m, v, param, c_master, c_m, c_v, g0);
     else
-      hipLaunchKernelGGL((state_copy_kernel<false, false>), dim3(n), block, 0, stream, pieces,
-                         master, m, v, param, c_master, c_m, c_v, g0);
+      hipLaunchKernelGGL((state_copy_kernel<false, false>), dim3(n), block, lds, stream, pieces,
+                         n_whole, master, m, v, param, c_master, c_m, c_v, g0);
   });
 }
 

@@ -26,6 +26,9 @@
 //  6. Pieces: the tensor segments again, with their offsets in the canonical
 //     order (every tensor contiguous and unpadded, in forward order) -- the
 //     format a checkpoint stores, independent of N and of the bucket layout.
+//     The table lists every whole piece (kPieceElems elements) first, then the
+//     rest of each segment cut into parts of at most kCopyPart elements, so
+//     the copy kernel runs exactly one work-group per part.
 #include <string.h>
 
 #include <algorithm>
@@ -172,14 +175,22 @@ extern "C" int zs_plan_create(const int64_t* numel, const uint8_t* decay, int64_
     // 5. weight-decay runs
     build_runs(*p);
 
-    // 6. pieces for state export/import: each tensor segment, cut into at most
-    //    kPieceElems elements, with its offset in the canonical order
+    // 6. pieces for state export/import, with their offsets in the canonical
+    //    order: the whole kPieceElems-element pieces of every tensor segment,
+    //    then each segment's remainder in parts of at most kCopyPart elements
     std::vector<int64_t> canon(n_tensors, 0);
     for (int64_t t = 1; t < n_tensors; t++) canon[t] = canon[t - 1] + numel[t - 1];
     for (const zs::Segment& s : p->segments) {
       if (s.tensor < 0) continue;
-      for (int64_t o = 0; o < s.len; o += zs::kPieceElems) {
-        const int64_t len = std::min(zs::kPieceElems, s.len - o);
+      for (int64_t o = 0; o + zs::kPieceElems <= s.len; o += zs::kPieceElems)
+        p->pieces.push_back(
+            {s.shard_off + o, canon[s.tensor] + s.tensor_off + o, (int32_t)zs::kPieceElems, 0});
+    }
+    p->n_whole_pieces = (int64_t)p->pieces.size();
+    for (const zs::Segment& s : p->segments) {
+      if (s.tensor < 0) continue;
+      for (int64_t o = s.len / zs::kPieceElems * zs::kPieceElems; o < s.len; o += zs::kCopyPart) {
+        const int64_t len = std::min(zs::kCopyPart, s.len - o);
         p->pieces.push_back({s.shard_off + o, canon[s.tensor] + s.tensor_off + o, (int32_t)len, 0});
       }
     }
