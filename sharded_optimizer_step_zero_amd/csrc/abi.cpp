@@ -186,14 +186,11 @@ int32_t device_cu_count() {
   return n;
 }
 
-
-
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 zs::StepConsts step_consts(float lr, float beta1, float beta2, float eps, float wd, int64_t t) {
   return zs::step_consts(lr, beta1, beta2, eps, wd, t);
 }
-
 
 int gather_grads(const zs_ctx* ctx, const void* const* grads, zs::GradPtrs* out) {
   if (!grads) return einval("zero_shard_step: grads is NULL");
