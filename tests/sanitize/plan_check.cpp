@@ -4,17 +4,22 @@
 // rank) through the public C functions, with the layout's invariants checked:
 // segments and runs partition [0, shard_len) in order, padding is where no
 // tensor is, every tensor element lands on exactly one rank, bucket lengths are
-// non-zero multiples of world_size * align, and the per-stage byte counts
-// follow their formulas.  Exit status 0 when every check holds.
+// non-zero multiples of world_size * align, the per-stage byte counts follow
+// their formulas, and the export/import piece table (internal to the planner)
+// covers every owned tensor element exactly once with consistent canonical
+// offsets: whole pieces of kPieceElems elements first, then parts of at most
+// kCopyPart.  Exit status 0 when every check holds.
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <memory>
 #include <string>
 #include <vector>
 
 #include "../../include/zeroshard.h"
+#include "../../sharded_optimizer_step_zero_amd/csrc/internal.h"
 
 namespace zs {
 void set_error(const std::string&) {}
@@ -35,6 +40,40 @@ static uint64_t next_u64() {  // xorshift64* (inputs only)
       return 1;                                                           \
     }                                                                     \
   } while (0)
+
+// The piece table: sizes by kind, each piece inside one tensor segment with the
+// canonical offset of its first element, and together an exact cover of the
+// shard's tensor elements.
+static int check_pieces(const zs_plan* p, const std::vector<int64_t>& numel) {
+  std::vector<int64_t> canon(numel.size(), 0);
+  for (size_t t = 1; t < numel.size(); t++) canon[t] = canon[t - 1] + numel[t - 1];
+  const int64_t nw = p->n_whole_pieces;
+  REQUIRE(nw >= 0 && nw <= (int64_t)p->pieces.size());
+  int64_t owned = 0;
+  for (const zs::Segment& sg : p->segments)
+    if (sg.tensor >= 0) owned += sg.len;
+  std::vector<std::pair<int64_t, int64_t>> spans;
+  int64_t sum = 0;
+  for (size_t i = 0; i < p->pieces.size(); i++) {
+    const zs::Piece& pc = p->pieces[i];
+    if ((int64_t)i < nw) REQUIRE(pc.len == zs::kPieceElems);
+    else REQUIRE(pc.len >= 1 && pc.len <= zs::kCopyPart);
+    // the segment holding the piece's first element
+    const zs::Segment* seg = nullptr;
+    for (const zs::Segment& sg : p->segments)
+      if (sg.shard_off <= pc.shard_off && pc.shard_off < sg.shard_off + sg.len) seg = &sg;
+    REQUIRE(seg && seg->tensor >= 0);
+    REQUIRE(pc.shard_off + pc.len <= seg->shard_off + seg->len);
+    REQUIRE(pc.canon_off == canon[seg->tensor] + seg->tensor_off + (pc.shard_off - seg->shard_off));
+    spans.push_back({pc.shard_off, pc.len});
+    sum += pc.len;
+  }
+  REQUIRE(sum == owned);
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); i++)
+    REQUIRE(spans[i - 1].first + spans[i - 1].second <= spans[i].first);
+  return 0;
+}
 
 static int check_layout(const std::vector<int64_t>& numel, const std::vector<uint8_t>& decay,
                         int32_t N, int64_t cap, int32_t align) {
@@ -97,6 +136,7 @@ static int check_layout(const std::vector<int64_t>& numel, const std::vector<uin
     REQUIRE(zs_plan_state_bytes(p, 3, &b3) == ZS_OK && b3 == 16 * S);
     int64_t x;
     REQUIRE(zs_plan_segment(p, nseg, &x, &x, &x, &x, nullptr) == ZS_EINVAL);
+    REQUIRE(check_pieces(p, numel) == 0);
   }
   for (size_t t = 0; t < numel.size(); t++) REQUIRE(covered[t] == numel[t]);
   return 0;
