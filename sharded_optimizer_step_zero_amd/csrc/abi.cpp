@@ -53,7 +53,7 @@ namespace {
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // The scalars block is 256 bytes: ClipScalars at 0, the device-computed
-// StepConsts at 64.  The staging area (ZS_STAGE_AVERAGE) comes last.
+// StepConsts at 64.  The staging area (ZS_STAGE_AVERAGE) comes first.
 zs::WorkspaceLayout workspace_layout(int64_t shard_len, int64_t n_runs, int64_t n_pieces,
                                      int64_t n_partials, int64_t stage_elems) {
   static_assert(sizeof(zs::ClipScalars) <= 64 && sizeof(zs::StepConsts) <= 192,
