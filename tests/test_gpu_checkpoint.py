@@ -155,6 +155,48 @@ def test_checkpoint_file_roundtrip(tmp_path):
     b.close()
 
 
+@pytest.mark.parametrize("numel", [NUMEL, [4096, 8192, 65_536 * 2 + 256]])
+def test_fp16_context_import_writes_fp16_param(numel):
+    """Import into a ZS_FP16 context: master, m, v of this rank's elements and the
+    fp16 param copy fp16_rne(master), padding untouched; export returns the state.
+    NUMEL's sizes put most canonical offsets off 16-byte alignment (the 4-byte
+    path); the second list keeps every part aligned (the 16-byte path)."""
+    log(f"test_fp16_context_import_writes_fp16_param numel={numel}")
+    decay = [1] * len(numel)
+    N, rank = 2, 1
+    lay = L.plan(numel, decay, N, rank, 25_000_000, 64)
+    z = ZeroShard(numel, decay, N, rank, M, fp16=True)
+    S, total = z.shard_len, sum(numel)
+    new = [synth.host_normal_f32(total, synth.key(SEED, 200 + k), 3.0) for k in range(3)]
+    z.import_state(*[torch.from_numpy(a).cuda() for a in new])
+    torch.cuda.synchronize()
+    own = np.ones(S, bool)
+    for o, n in lay.padding_ranges():
+        own[o:o + n] = False
+    for t, a in zip((z.master, z.exp_avg, z.exp_avg_sq), new):
+        want = np.zeros(S, np.float32)
+        lay.from_canonical(a, want)
+        assert _same(to_host(t)[:S], want)
+    want_p = np.zeros(S, np.float32)
+    lay.from_canonical(new[0], want_p)
+    got_p = z.param.cpu().view(torch.int16).numpy().view(np.uint16)[:S]
+    assert np.array_equal(got_p[own], oracle.f32_to_f16(want_p)[own])
+    assert not got_p[~own].any()
+    back = [torch.full((total,), -1.0, device="cuda") for _ in range(3)]
+    z.export_state(*back)
+    torch.cuda.synchronize()
+    mine = np.zeros(total, bool)         # canonical positions this rank owns
+    co = lay.canonical_offsets()
+    for sg in lay.segments:
+        if sg.tensor >= 0:
+            c0 = co[sg.tensor] + sg.tensor_off
+            mine[c0:c0 + sg.length] = True
+    for c, a in zip(back, new):
+        got = to_host(c)
+        assert _same(got[mine], a[mine]) and (got[~mine] == -1.0).all()
+    z.close()
+
+
 def test_llama67b_export_import_sampled():
     """Export and import at the Llama-6.7B size (6.74G parameters: canonical
     offsets beyond 2^32), checked on samples through device gathers: seeded
