@@ -85,6 +85,19 @@ def test_offload_matches_oracle(case):
     _run_vs_oracle(w, 4, chunk, n_threads=[0, 1, 5, 16][case])
 
 
+@pytest.mark.parametrize("groups", ["1", "5"])
+@pytest.mark.parametrize("case", [0, 3])
+def test_offload_sliced_norm_pass_matches_oracle(monkeypatch, case, groups):
+    """The device norm pass of an offload context issued as launches of 1 or 5
+    work-groups (ZS_MAX_GROUPS_PER_LAUNCH, read at init), clip and norm included."""
+    monkeypatch.setenv("ZS_MAX_GROUPS_PER_LAUNCH", groups)
+    numel, decay, N, rank, M, clip, chunk = CASES[case]
+    w = scaled(workload(1), numel, decay, world_size=N, rank=rank, M=M, name=f"offload{case}")
+    w.max_grad_norm = clip
+    log(f"test_offload_sliced_norm_pass_matches_oracle[{case}] groups={groups}")
+    _run_vs_oracle(w, 3, chunk)
+
+
 def test_gpt13b_shard_offload():
     w = workload(2)
     log(f"test_gpt13b_shard_offload: {w.description}, 3 steps, chunk 4M")
