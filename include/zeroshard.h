@@ -51,8 +51,11 @@
  *   - Device buffers must be 16-byte aligned; the workspace 256-byte aligned.
  *   - `stream` is a hipStream_t handle (NULL: the null stream).  Calls
  *     enqueue work and return without waiting, except where stated.
- *   - Return value: 0 = ZS_OK; negative = error, nothing enqueued, state
- *     unchanged, message in zero_shard_last_error(); positive = warning.
+ *   - Return value: 0 = ZS_OK; positive = warning; negative = error, with a
+ *     message in zero_shard_last_error().  ZS_EINVAL, ZS_ENOMEM and ZS_ESTATE
+ *     are found before anything is enqueued (state unchanged).  ZS_EHIP from
+ *     a later kernel launch of a call can leave that call's earlier kernels
+ *     enqueued; a HIP launch error usually means the device is unusable.
  *   - A context is used by one host thread at a time.
  */
 #ifndef ZEROSHARD_H
