@@ -45,7 +45,8 @@
  * Conventions.
  *   - Pointers named *_dev or taking buffers are device pointers; the caller
  *     allocates and owns every device buffer (grads, param, master, moments,
- *     workspace).  The library never allocates or frees device memory.
+ *     workspace).  The library allocates or frees device memory only in the
+ *     optional zs_device_alloc_contiguous / zs_device_free.
  *     zs_plan and zs_ctx are host objects owned by the library, released by
  *     their destroy calls.
  *   - Device buffers must be 16-byte aligned; the workspace 256-byte aligned.
@@ -439,6 +440,27 @@ void zero_shard_destroy(zs_ctx *ctx);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char *zero_shard_last_error(void);
+
+/* ------------------------------------------- optional device memory */
+
+/*
+ * For callers that want physically contiguous device memory for a large slab
+ * (zs_slab_layout's); these are the library's only allocating calls, and no
+ * other entry point uses them.  Contiguous memory lets the GPU map the slab
+ * with large page fragments: on MI355X the step on the Llama-70B 1/16 shard
+ * (a 129 GB slab) ran 6.44 against 6.38 TB/s on ordinary device memory, the
+ * Llama-6.7B step (108 GB) 0.3% faster; a 4.9 GB slab gained nothing.
+ *
+ * zs_device_alloc_contiguous: `bytes` of device memory on `device`, physically
+ * contiguous when the driver can provide it, else ordinary device memory (the
+ * caller cannot tell which); NULL when neither is available.  `stream` is
+ * ignored.  zs_device_free releases such a pointer (NULL is ignored).  The
+ * signatures are those of a torch pluggable allocator, so a torch memory pool
+ * can serve tensors from it.  Neither touches the current device of the
+ * calling thread.
+ */
+void *zs_device_alloc_contiguous(size_t bytes, int device, void *stream);
+void zs_device_free(void *ptr, size_t bytes, int device, void *stream);
 
 #ifdef __cplusplus
 }

@@ -103,6 +103,8 @@ _sig("zero_offload_step_amp_global_norm", ctypes.c_int, _vp, _vp, _f32, _f32, _f
      _f32, _vp, _f32, _f32, _i32, _vp)
 _sig("zero_offload_set_stream", ctypes.c_int, _vp, _vp)
 _sig("zero_offload_destroy", None, _vp)
+_sig("zs_device_alloc_contiguous", _vp, ctypes.c_size_t, _i32, _vp)
+_sig("zs_device_free", None, _vp, ctypes.c_size_t, _i32, _vp)
 
 EXPORTED = ["zs_plan_create", "zs_plan_query", "zs_plan_tensor_slice", "zs_plan_segment",
             "zs_plan_bucket", "zs_plan_run", "zs_plan_state_bytes", "zs_plan_destroy",
@@ -115,7 +117,8 @@ EXPORTED = ["zs_plan_create", "zs_plan_query", "zs_plan_tensor_slice", "zs_plan_
             "zs_offload_staging_bytes", "zero_offload_init", "zero_offload_step",
             "zero_offload_step_amp", "zero_offload_grad_sumsq", "zero_offload_step_global_norm",
             "zero_offload_grad_sumsq_amp", "zero_offload_step_amp_global_norm",
-            "zero_offload_set_stream", "zero_offload_destroy"]
+            "zero_offload_set_stream", "zero_offload_destroy", "zs_device_alloc_contiguous",
+            "zs_device_free"]
 
 
 class ZeroShardError(RuntimeError):
@@ -418,6 +421,27 @@ def zero_offload_destroy(ctx: int) -> None:
 # ----------------------------------------------------- convenience owner
 
 
+def zs_device_alloc_contiguous(nbytes: int, device: int = 0) -> int:
+    """Device memory, physically contiguous when available; 0 when none is left."""
+    return _lib.zs_device_alloc_contiguous(nbytes, device, None) or 0
+
+
+def zs_device_free(ptr: int, nbytes: int = 0, device: int = 0) -> None:
+    _lib.zs_device_free(ptr, nbytes, device, None)
+
+
+_CONTIG = None
+
+
+def _contiguous_allocator():
+    """The torch pluggable allocator over zs_device_alloc_contiguous / zs_device_free."""
+    global _CONTIG
+    if _CONTIG is None:
+        from torch.cuda.memory import CUDAPluggableAllocator
+        _CONTIG = CUDAPluggableAllocator(LIB_PATH, "zs_device_alloc_contiguous", "zs_device_free")
+    return _CONTIG
+
+
 class ZeroShard:
     """One rank's shard: plan + torch-allocated device buffers + bound context.
 
@@ -428,9 +452,12 @@ class ZeroShard:
     the caller fills them before each step)."""
 
     _PERIOD = 1 << 21
+    # slabs from this size on come from physically contiguous memory by default
+    # (measured faster on 108 GB and 129 GB slabs, no gain on a 4.9 GB one)
+    CONTIGUOUS_FROM = 64 << 30
 
     def __init__(self, numel, decay, world_size=1, rank=0, M=1, device=None, bucket_cap=25_000_000,
-                 align=64, flags=0, stream=None, fp16=False, grad_buffers=False):
+                 align=64, flags=0, stream=None, fp16=False, grad_buffers=False, contiguous=None):
         import torch
         self.device = torch.device(device if device is not None else "cuda")
         self.M = M
@@ -446,7 +473,19 @@ class ZeroShard:
         offs, total = zs_slab_layout(self.plan, M, flags, n_grads)
         self.ws_bytes = zs_workspace_bytes(self.plan, M, flags)
         # over-allocate one period so the slab can start on a 2 MiB boundary
-        self.slab = torch.zeros(total + self._PERIOD, dtype=torch.uint8, device=self.device)
+        if contiguous is None:
+            contiguous = total >= self.CONTIGUOUS_FROM
+        self.contiguous = bool(contiguous)
+        self._pool = None
+        if self.contiguous:
+            # a private torch memory pool served by zs_device_alloc_contiguous; it is
+            # dropped in close(), which returns the memory
+            self._pool = torch.cuda.MemPool(_contiguous_allocator().allocator())
+            idx = self.device.index if self.device.index is not None else torch.cuda.current_device()
+            with torch.cuda.use_mem_pool(self._pool, idx):
+                self.slab = torch.zeros(total + self._PERIOD, dtype=torch.uint8, device=self.device)
+        else:
+            self.slab = torch.zeros(total + self._PERIOD, dtype=torch.uint8, device=self.device)
         base = (-self.slab.data_ptr()) % self._PERIOD
         S = self.shard_len
 
@@ -525,6 +564,15 @@ class ZeroShard:
         if getattr(self, "plan", None):
             zs_plan_destroy(self.plan)
             self.plan = None
+        if getattr(self, "_pool", None) is not None:
+            # a contiguous slab: wait for queued work, drop this object's views and the
+            # private pool; the memory returns once no tensor uses it
+            import torch
+            torch.cuda.synchronize(self.device)
+            self.param = self.master = self.exp_avg = self.exp_avg_sq = None
+            self.grads, self.workspace, self.slab = [], None, None
+            self._pool = None
+            torch.cuda.empty_cache()
 
     def __del__(self):
         try:

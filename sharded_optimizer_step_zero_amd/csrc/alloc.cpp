@@ -1,0 +1,42 @@
+// alloc.cpp -- optional device-memory helpers for callers that place a rank's
+// arrays themselves.  No step, copy or plan call uses them.
+//
+// A physically contiguous allocation lets the GPU map a large slab with large
+// page fragments, so the twelve streams of a step at M = 8 miss the address
+// translation caches less.  Measured on MI355X on the Llama-70B 1/16 shard
+// (129 GB slab, same process, alternating): 6.44 against 6.38 TB/s; Llama-6.7B
+// (108 GB) +0.3%; on a 4.9 GB slab no gain.  The pair has the signature of a
+// torch pluggable allocator, so a torch memory pool can hand such memory out.
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+
+#include "../../include/zeroshard.h"
+
+extern "C" void* zs_device_alloc_contiguous(size_t bytes, int device, void* stream) {
+  (void)stream;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return nullptr;
+  if (device != prev && hipSetDevice(device) != hipSuccess) return nullptr;
+  void* p = nullptr;
+  if (hipExtMallocWithFlags(&p, bytes, hipDeviceMallocContiguous) != hipSuccess) {
+    (void)hipGetLastError();  // not available in one piece: ordinary device memory
+    p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      p = nullptr;
+    }
+  }
+  if (device != prev) (void)hipSetDevice(prev);
+  return p;
+}
+
+extern "C" void zs_device_free(void* ptr, size_t bytes, int device, void* stream) {
+  (void)bytes;
+  (void)stream;
+  if (!ptr) return;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return;
+  if (device != prev && hipSetDevice(device) != hipSuccess) return;
+  (void)hipFree(ptr);
+  if (device != prev) (void)hipSetDevice(prev);
+}

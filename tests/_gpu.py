@@ -70,14 +70,14 @@ def to_host(t) -> np.ndarray:
 class Shard:
     """A ZeroShard bound to a workload's synthetic inputs (geometry from the oracle layout)."""
 
-    def __init__(self, w: Workload, flags=0, device="cuda"):
+    def __init__(self, w: Workload, flags=0, device="cuda", contiguous=None):
         self.w = w
         self.lay = L.plan(w.numel, w.decay, w.world_size, w.rank, w.bucket_cap, w.align)
         # the slab placement bench.py times: state, contributions and workspace in one
         # allocation, staggered
         self.zs = ZeroShard(w.numel, w.decay, w.world_size, w.rank, w.M, device=device,
                             bucket_cap=w.bucket_cap, align=w.align, flags=flags,
-                            grad_buffers=True)
+                            grad_buffers=True, contiguous=contiguous)
         assert self.zs.shard_len == self.lay.shard_len
         self.S = self.lay.shard_len
         special = special_ranges(w, [(x.shard_off, x.length, x.tensor) for x in self.lay.segments])
@@ -108,9 +108,9 @@ class Shard:
         torch.cuda.empty_cache()
 
 
-def full_parity(w: Workload, steps: int, flags=0, exact=True):
+def full_parity(w: Workload, steps: int, flags=0, exact=True, contiguous=None):
     """Whole-shard parity for `steps` steps.  Returns the per-step stats."""
-    sh = Shard(w, flags)
+    sh = Shard(w, flags, contiguous=contiguous)
     S = sh.S
     hp = sh.hp()
     mask = sh.lay.decay_mask()
