@@ -446,10 +446,11 @@ const char *zero_shard_last_error(void);
 /*
  * For callers that want physically contiguous device memory for a large slab
  * (zs_slab_layout's); these are the library's only allocating calls, and no
- * other entry point uses them.  Contiguous memory lets the GPU map the slab
- * with large page fragments: on MI355X the step on the Llama-70B 1/16 shard
- * (a 129 GB slab) ran 6.44 against 6.38 TB/s on ordinary device memory, the
- * Llama-6.7B step (108 GB) 0.3% faster; a 4.9 GB slab gained nothing.
+ * other entry point uses them.  Measured on MI355X, the step on the Llama-70B
+ * 1/16 shard (a 129 GB slab) ran 6.44 against 6.37 TB/s on ordinary device
+ * memory as the first process on the device, but 6.15 against 6.25 after a
+ * 108 GB process had run: where the contiguous range lands matters more than
+ * its contiguity.  No default path uses it.
  *
  * zs_device_alloc_contiguous: `bytes` of device memory on `device`, physically
  * contiguous when the driver can provide it, else ordinary device memory (the

@@ -449,15 +449,14 @@ class ZeroShard:
     into one device slab placed by zs_slab_layout (array starts staggered by
     4 KiB past 2 MiB boundaries).  With grad_buffers=True the slab also holds the
     M gradient contribution buffers, exposed as `grads` (16-bit, shard_len each;
-    the caller fills them before each step)."""
+    the caller fills them before each step).  With contiguous=True the slab comes
+    from physically contiguous memory (zs_device_alloc_contiguous, through a
+    private torch memory pool released by close())."""
 
     _PERIOD = 1 << 21
-    # slabs from this size on come from physically contiguous memory by default
-    # (measured faster on 108 GB and 129 GB slabs, no gain on a 4.9 GB one)
-    CONTIGUOUS_FROM = 64 << 30
 
     def __init__(self, numel, decay, world_size=1, rank=0, M=1, device=None, bucket_cap=25_000_000,
-                 align=64, flags=0, stream=None, fp16=False, grad_buffers=False, contiguous=None):
+                 align=64, flags=0, stream=None, fp16=False, grad_buffers=False, contiguous=False):
         import torch
         self.device = torch.device(device if device is not None else "cuda")
         self.M = M
@@ -473,8 +472,6 @@ class ZeroShard:
         offs, total = zs_slab_layout(self.plan, M, flags, n_grads)
         self.ws_bytes = zs_workspace_bytes(self.plan, M, flags)
         # over-allocate one period so the slab can start on a 2 MiB boundary
-        if contiguous is None:
-            contiguous = total >= self.CONTIGUOUS_FROM
         self.contiguous = bool(contiguous)
         self._pool = None
         if self.contiguous:

@@ -2,10 +2,10 @@
 // arrays themselves.  No step, copy or plan call uses them.
 //
 // A physically contiguous allocation lets the GPU map a large slab with large
-// page fragments, so the twelve streams of a step at M = 8 miss the address
-// translation caches less.  Measured on MI355X on the Llama-70B 1/16 shard
-// (129 GB slab, same process, alternating): 6.44 against 6.38 TB/s; Llama-6.7B
-// (108 GB) +0.3%; on a 4.9 GB slab no gain.  The pair has the signature of a
+// page fragments.  Measured on MI355X on the Llama-70B 1/16 shard (129 GB slab,
+// same process, alternating with ordinary memory): 6.44 against 6.37 TB/s as
+// the first process on the device, 6.15 against 6.25 after a 108 GB process
+// had run, so it is an option, not a default.  The pair has the signature of a
 // torch pluggable allocator, so a torch memory pool can hand such memory out.
 #include <hip/hip_runtime_api.h>
 #include <stddef.h>

@@ -70,7 +70,7 @@ def to_host(t) -> np.ndarray:
 class Shard:
     """A ZeroShard bound to a workload's synthetic inputs (geometry from the oracle layout)."""
 
-    def __init__(self, w: Workload, flags=0, device="cuda", contiguous=None):
+    def __init__(self, w: Workload, flags=0, device="cuda", contiguous=False):
         self.w = w
         self.lay = L.plan(w.numel, w.decay, w.world_size, w.rank, w.bucket_cap, w.align)
         # the slab placement bench.py times: state, contributions and workspace in one
@@ -108,7 +108,7 @@ class Shard:
         torch.cuda.empty_cache()
 
 
-def full_parity(w: Workload, steps: int, flags=0, exact=True, contiguous=None):
+def full_parity(w: Workload, steps: int, flags=0, exact=True, contiguous=False):
     """Whole-shard parity for `steps` steps.  Returns the per-step stats."""
     sh = Shard(w, flags, contiguous=contiguous)
     S = sh.S
