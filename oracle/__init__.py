@@ -102,6 +102,9 @@ def _load(path: str):
     L.zo_step_f16.restype = i32
     L.zo_scaler_update.argtypes = [vp, vp, i32, f32, f32, i32]
     L.zo_scaler_update.restype = None
+    L.zo_amp_step.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, f32, f32, f32, f32, f32, f32,
+                              vp, vp, vp, f32, f32, i32, vp]
+    L.zo_amp_step.restype = i32
     return L
 
 
@@ -273,10 +276,14 @@ class Scaler:
     def __init__(self, scale=65536.0, growth_factor=2.0, backoff_factor=0.5, growth_interval=2000):
         self.scale = np.array([scale], np.float32)
         self.tracker = np.array([0], np.int32)
-        self.applied = 0
+        self._applied = np.array([0], np.int64)
         self.growth_factor = growth_factor
         self.backoff_factor = backoff_factor
         self.growth_interval = growth_interval
+
+    @property
+    def applied(self) -> int:
+        return int(self._applied[0])
 
     def update(self, found_inf: bool) -> None:
         lib().zo_scaler_update(self.scale.ctypes.data, self.tracker.ctypes.data,
@@ -286,18 +293,25 @@ class Scaler:
 
 def amp_step(grads, master, m, v, param, decay, scaler: Scaler, *, lr, beta1, beta2, eps,
              weight_decay, max_grad_norm=0.0):
-    """The whole fp16 step: unscale, found-inf (a non-finite sum of squares of the
-    unscaled average), optional clip on the unscaled norm, the update (at
-    t = applied + 1) unless found-inf, then the scale update.
-    Returns (found_inf, norm)."""
-    inv = inv_scale(float(scaler.scale[0]))
-    sumsq = grad_sumsq_f16(grads, inv)
-    found_inf = not np.isfinite(sumsq)
-    norm = float(np.sqrt(sumsq)) if np.isfinite(sumsq) else float("nan")
-    if not found_inf:
-        coef = coef_from_norm(norm, max_grad_norm) if max_grad_norm > 0 else None
-        step_f16(grads, master, m, v, param, decay, lr=lr, beta1=beta1, beta2=beta2, eps=eps,
-                 weight_decay=weight_decay, step=scaler.applied + 1, inv_scale=inv, coef=coef)
-        scaler.applied += 1
-    scaler.update(found_inf)
-    return found_inf, norm
+    """The whole fp16 step (zo_amp_step): unscale, found-inf (a non-finite sum of
+    squares of the unscaled average), optional clip on the unscaled norm, the
+    update (at t = applied + 1) unless found-inf, then the scale update.
+    Returns (found_inf, norm); norm is NaN when found-inf."""
+    gs, n = _grads_u16(grads)
+    for a in (master, m, v):
+        if a.dtype != np.float32 or not a.flags.c_contiguous or a.size != n:
+            raise ValueError("master/m/v must be contiguous float32 of the shard length")
+    if decay is not None:
+        decay = np.ascontiguousarray(decay, dtype=np.uint8)
+    norm = np.zeros(1, np.float64)
+    rc = lib().zo_amp_step(n, len(gs), _ptr_array(gs), master.ctypes.data, m.ctypes.data,
+                           v.ctypes.data, None if param is None else param.ctypes.data,
+                           None if decay is None else decay.ctypes.data, lr, beta1, beta2, eps,
+                           weight_decay, float(max_grad_norm), scaler.scale.ctypes.data,
+                           scaler.tracker.ctypes.data, scaler._applied.ctypes.data,
+                           scaler.growth_factor, scaler.backoff_factor, scaler.growth_interval,
+                           norm.ctypes.data)
+    if rc < 0:
+        raise ValueError("zo_amp_step rejected its arguments")
+    found_inf = rc == 1
+    return found_inf, float("nan") if found_inf else float(norm[0])

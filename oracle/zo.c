@@ -13,8 +13,8 @@
  *      reduce-scatter).  The accumulation identity is the gradient
  *      accumulation equation g = (1/M) sum_j grad l_j of Lecture04 notes,
  *      section "单卡 baseline 与 gradient accumulation 的隐藏假设"; the
- *      sum-then-divide form is the DDP loop of 第7讲 CS336 并行, §6.2
- *      (all_reduce, then p.grad /= world_size).  The contributions are bf16,
+ *      sum-then-divide form (add the contributions up, then divide by their
+ *      count) is the DDP loop of 第7讲 CS336 并行, §6.2.  The contributions are bf16,
  *      widened exactly to fp32 and summed in fp32 in the fixed order
  *      j = 0..M-1 (fp32 reduce: 大模型基础设施工程 06, §9.1 and §15.3).
  *   2. optionally g = g * coef, coef = min(1, max_norm / (||g||_2 + 1e-6)),
@@ -48,7 +48,8 @@
  * GradScaler: contributions of the loss scaled by `scale` are averaged in
  * fp32, multiplied by inv_scale = fp32(1/scale), and if any result is not
  * finite the step is skipped and scale *= backoff; otherwise the step runs
- * and, after growth_interval consecutive good steps, scale *= growth.
+ * and, after growth_interval consecutive good steps, scale *= growth when
+ * the grown scale is finite.  The clip, if any, uses the unscaled norm.
  */
 #include <math.h>
 #include <stdint.h>
@@ -475,7 +476,10 @@ int32_t zo_step_f16(int64_t n, int32_t M, const uint16_t *const *grads, float *m
 
 /* The loss-scale update after a step: found_inf -> scale *= backoff and the
  * growth count restarts; otherwise the count grows and, on reaching
- * growth_interval, scale *= growth and the count restarts. */
+ * growth_interval, the count restarts and scale *= growth -- unless the grown
+ * scale would not be finite, in which case the scale stays (torch's
+ * GradScaler: a scale that overflowed to Inf would zero every later unscaled
+ * gradient). */
 void zo_scaler_update(float *scale, int32_t *growth_tracker, int32_t found_inf,
                       float growth_factor, float backoff_factor, int32_t growth_interval)
 {
@@ -485,10 +489,47 @@ void zo_scaler_update(float *scale, int32_t *growth_tracker, int32_t found_inf,
     } else {
         int32_t good = *growth_tracker + 1;
         if (good == growth_interval) {
-            *scale = *scale * growth_factor;
+            float grown = *scale * growth_factor;
+            if (isfinite(grown))
+                *scale = grown;
             *growth_tracker = 0;
         } else {
             *growth_tracker = good;
         }
     }
+}
+
+/* One whole loss-scaled step, in the order torch's GradScaler drives an
+ * optimizer: unscale (inv_scale = fp32(1/scale)), found-inf = the fp64 sum of
+ * squares of the unscaled average is not finite, the optional clip on the
+ * unscaled norm, the update at t = applied + 1 unless found-inf (a skipped
+ * step does not advance t), then the scale update.  *norm_out (optional)
+ * receives sqrt of that sum of squares.  Returns 1 when the step was skipped,
+ * 0 when applied, -1 for bad arguments. */
+int32_t zo_amp_step(int64_t n, int32_t M, const uint16_t *const *grads, float *master, float *m,
+                    float *v, uint16_t *param_f16, const uint8_t *decay, float lr, float beta1,
+                    float beta2, float eps, float wd, float max_norm, float *scale,
+                    int32_t *growth_tracker, int64_t *applied, float growth_factor,
+                    float backoff_factor, int32_t growth_interval, double *norm_out)
+{
+    if (n < 0 || M < 1 || !grads || !master || !m || !v || !scale || !growth_tracker ||
+        !applied)
+        return -1;
+    float inv = zo_inv_scale(*scale);
+    double sumsq = zo_grad_sumsq_f16(n, M, grads, inv);
+    int32_t found_inf = !isfinite(sumsq);
+    double norm = sqrt(sumsq);
+    if (norm_out)
+        *norm_out = norm;
+    if (!found_inf) {
+        int32_t use_coef = max_norm > 0.0f;
+        float coef = use_coef ? zo_coef_from_norm(norm, max_norm) : 1.0f;
+        if (zo_step_f16(n, M, grads, master, m, v, param_f16, decay, lr, beta1, beta2, eps, wd,
+                        *applied + 1, inv, use_coef, coef) != 0)
+            return -1;
+        *applied += 1;
+    }
+    zo_scaler_update(scale, growth_tracker, found_inf, growth_factor, backoff_factor,
+                     growth_interval);
+    return found_inf;
 }

@@ -36,6 +36,11 @@ int32_t zo_step_f16(int64_t n, int32_t M, const uint16_t *const *grads, float *m
                     int32_t use_coef, float coef);
 void zo_scaler_update(float *scale, int32_t *growth_tracker, int32_t found_inf, float growth,
                       float backoff, int32_t interval);
+int32_t zo_amp_step(int64_t n, int32_t M, const uint16_t *const *grads, float *master, float *m,
+                    float *v, uint16_t *param_f16, const uint8_t *decay, float lr, float beta1,
+                    float beta2, float eps, float wd, float max_norm, float *scale,
+                    int32_t *growth_tracker, int64_t *applied, float growth_factor,
+                    float backoff_factor, int32_t growth_interval, double *norm_out);
 
 static uint64_t rng = 0x853C49E6748FEA9Bull;
 static uint32_t next_u32(void)
@@ -82,6 +87,17 @@ int main(void)
                 if (zo_step_f16(n, M, (const uint16_t *const *)g, p, m, v, b, dec, 1e-3f, 0.9f,
                                 0.95f, 1e-8f, 0.1f, t, zo_inv_scale(1024.0f), 0, 1.0f) != 0)
                     return 1;
+            }
+            {
+                float sc = 1024.0f;
+                int32_t tr = 0;
+                int64_t applied = 0;
+                double norm = 0.0;
+                for (int t = 1; t <= 3; t++)
+                    if (zo_amp_step(n, M, (const uint16_t *const *)g, p, m, v, b, dec, 1e-3f,
+                                    0.9f, 0.95f, 1e-8f, 0.1f, t == 2 ? 0.5f : 0.0f, &sc, &tr,
+                                    &applied, 2.0f, 0.5f, 1, t == 3 ? NULL : &norm) < 0)
+                        return 1;
             }
             zo_reduce_mean_f16(n, M, (const uint16_t *const *)g, zo_inv_scale(8.0f), avg);
             (void)zo_grad_sumsq_f16(n, M, (const uint16_t *const *)g, zo_inv_scale(8.0f));

@@ -53,6 +53,10 @@ PINS = [
     lambda: P.test_scale_update_matches_torch(),
     lambda: P.test_unscale_and_found_inf_match_torch(),
     lambda: P.test_amp_sequence_matches_torch_adamw_and_gradscaler(),
+    lambda: P.test_f16_sumsq_constant_gradient_closed_form(),
+    lambda: P.test_f16_sumsq_matches_clip_grad_norm_f64(),
+    lambda: P.test_scale_growth_keeps_finite_scale_near_flt_max(),
+    lambda: P.test_amp_clipped_sequence_matches_torch_gradscaler(),
 ]
 
 U, C = "zo_update.inc", "zo.c"
@@ -93,6 +97,20 @@ MUTANTS = [
      "float f = (float)mant * 1.1920928955078125e-7f;"),
     ("scaler-no-backoff", C, "*scale = *scale * backoff_factor;", "*scale = *scale;"),
     ("scaler-growth-late", C, "if (good == growth_interval) {", "if (good > growth_interval) {"),
+    ("scaler-grows-to-inf", C, "            if (isfinite(grown))\n                *scale = grown;",
+     "            *scale = grown;"),
+    ("f16-norm-not-squared", C,
+     "double g = (double)mean_f16_unscaled(grads, M, i, inv_scale);\n            acc += g * g;",
+     "double g = (double)mean_f16_unscaled(grads, M, i, inv_scale);\n            acc += g < 0 ? -g : g;"),
+    ("f16-norm-on-scaled-average", C,
+     "double g = (double)mean_f16_unscaled(grads, M, i, inv_scale);",
+     "double g = (double)mean_f16_unscaled(grads, M, i, 1.0f);"),
+    ("amp-coef-from-scaled-norm", C,
+     "float coef = use_coef ? zo_coef_from_norm(norm, max_norm) : 1.0f;",
+     "float coef = use_coef ? zo_coef_from_norm(norm * (double)*scale, max_norm) : 1.0f;"),
+    ("amp-clip-ignored", C, "int32_t use_coef = max_norm > 0.0f;", "int32_t use_coef = 0;"),
+    ("amp-skip-advances-t", C, "        *applied += 1;\n    }\n    zo_scaler_update(",
+     "    }\n    *applied += 1;\n    zo_scaler_update("),
     ("fma-contraction", None, None, None),
 ]
 
