@@ -107,7 +107,12 @@ typedef struct zs_amp_state {
 /*
  * Builds the layout of rank `rank` of `world_size` for tensors numel[0..n_tensors)
  * (element counts, forward order; 0 allowed) with weight-decay flags decay[]
- * (nonzero: decayed).  bucket_cap >= 1 elements; align a multiple of 8 (64 in
+ * (nonzero: decayed).  The layout is the flat gradient buckets of
+ * 大模型基础设施工程 06, §6.1 (buckets closed at a size cap, in forward
+ * order), kept as contiguous flat buffers (§11.3, contiguous_gradients), each
+ * bucket cut into world_size equal slices of which this rank owns slice
+ * `rank` -- the ZeRO partition of CS324 notes §3.4, where cutting flat buffers
+ * is legal because AdamW acts element by element.  bucket_cap >= 1 elements; align a multiple of 8 (64 in
  * the reference workloads: 128 B of bf16, 256 B of fp32).
  * On success *out owns a new plan.  Errors: ZS_EINVAL (bad sizes, flags array
  * missing, geometry), ZS_ENOMEM.
@@ -116,7 +121,8 @@ int zs_plan_create(const int64_t *numel, const uint8_t *decay, int64_t n_tensors
                    int32_t world_size, int32_t rank, int64_t bucket_cap, int32_t align,
                    zs_plan **out);
 
-/* Sizes of the plan.  Any output pointer may be NULL.
+/* Sizes of the plan (the partition of 大模型基础设施工程 06, §6.1 and §11.3, and
+ * CS324 notes §3.4, as built by zs_plan_create).  Any output pointer may be NULL.
  *   shard_len    elements of this rank's flat shard (a multiple of align)
  *   n_segments   maximal runs of one tensor, or of padding, in the shard
  *   n_runs       maximal stretches of one weight-decay flag (padding joins a
@@ -187,6 +193,10 @@ int zs_slab_layout(const zs_plan *plan, int32_t M, uint32_t flags, int32_t n_gra
 /* ------------------------------------------------------------ the step */
 
 /*
+ * The pages define no interface for creating or releasing this state (they
+ * describe the per-rank update, not an API); these two calls are this
+ * library's own.
+ *
  * Binds a context to one rank's device buffers (each shard_len elements):
  * param_bf16 (bf16, written by every step), master, exp_avg, exp_avg_sq
  * (fp32, read and written), and a workspace of zs_workspace_bytes(plan, M, flags)
@@ -198,10 +208,16 @@ int zs_slab_layout(const zs_plan *plan, int32_t M, uint32_t flags, int32_t n_gra
  * Uploads the run table on `stream` and waits for that copy.  The plan may
  * be destroyed afterwards.  Errors: ZS_EINVAL, ZS_ENOMEM, ZS_EHIP.
  *
- * Read from the environment at this call (zero_offload_init reads the second):
+ * The streaming kernels cap their resident workgroups per CU through an LDS
+ * reservation they never use.  Every reservation the context will launch
+ * with, plus the kernels' static LDS, is checked here against the current
+ * device's per-workgroup LDS limit (queried); ZS_EINVAL if one does not fit,
+ * so no launch ever asks for more.
+ *
+ * Read from the environment at this call (zero_offload_init reads both too):
  *   ZS_WAVES_PER_CU           resident waves per CU of the step kernels, 3..64,
  *                             or 0 for no cap; unset: a measured table by M and
- *                             shard size.
+ *                             shard size.  Any other value is ZS_EINVAL.
  *   ZS_MAX_GROUPS_PER_LAUNCH  work-groups per kernel launch, > 0.  A grid larger
  *                             than one dispatch carries (2^32 - 1 work-items,
  *                             reached by shards beyond 2^34 elements) is always
@@ -283,7 +299,8 @@ int zero_shard_import_state(zs_ctx *ctx, const float *canon_master, const float 
  *   otherwise:  [clip on the unscaled norm] the AdamW step at
  *               t = applied_steps + 1, param = fp16_rne(master);
  *               applied_steps += 1; after growth_interval such steps in a row
- *               scale *= growth_factor.
+ *               tracker = 0 and scale *= growth_factor, unless the grown
+ *               scale would be Inf (then the scale stays).
  * Everything, including the bias-correction constants for t, is decided on
  * the device: no host round trip per step.  zero_shard_amp_state_init enqueues
  * the initial state {init_scale, 0, 0}.  grad_norm_out (optional, waits)
@@ -399,6 +416,15 @@ int zero_offload_step_amp(zs_offload *ctx, const void *const *grads, float lr, f
                           int32_t growth_interval, double *grad_norm_out);
 
 /*
+ * Enqueues the initial scaler state {init_scale, 0, 0} into state_dev on the
+ * offload context's device stream, as zero_shard_amp_state_init does for a
+ * device context, so the first step on that stream reads it.
+ * Errors: ZS_EINVAL (NULL or unaligned state_dev, init_scale not finite and
+ * > 0), ZS_EHIP.
+ */
+int zero_offload_amp_state_init(zs_offload *ctx, zs_amp_state *state_dev, float init_scale);
+
+/*
  * The multi-rank split of the offloaded steps, as for the device steps
  * (zero_shard_grad_sumsq / zero_shard_step_global_norm and their _amp twins):
  * part 1 runs the device norm pass, which also stages the averages part 2
@@ -429,13 +455,18 @@ int zero_offload_set_stream(zs_offload *ctx, void *stream);
 /* Waits for the context's copies, stops its threads and frees it. */
 void zero_offload_destroy(zs_offload *ctx);
 
-/* The bf16 parameter shard (the all-gather send buffer) and its length. */
+/* The bf16 parameter shard and its length: after a step it holds the rank's
+ * updated parameters, the buffer ZeRO-1's all-gather sends so that every rank
+ * again holds the whole model (Lecture04 notes, "ZeRO-1"; CS336 第七讲
+ * summary, Q2).  Host call, enqueues nothing. */
 int zero_shard_params(zs_ctx *ctx, const void **param_bf16, int64_t *shard_len);
 
 /* Later calls enqueue on `stream`. */
 int zero_shard_set_stream(zs_ctx *ctx, void *stream);
 
-/* Releases the context (host memory only; device buffers stay the caller's). */
+/* Releases the context (host memory only; device buffers stay the caller's).
+ * Like zero_shard_init, the library's own call: the pages define no interface
+ * for it.  Work already enqueued is not waited for. */
 void zero_shard_destroy(zs_ctx *ctx);
 
 /* Message of the last failing call on this thread ("" if none). */

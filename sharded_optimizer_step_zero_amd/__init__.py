@@ -101,6 +101,7 @@ _sig("zero_offload_step_global_norm", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, 
 _sig("zero_offload_grad_sumsq_amp", ctypes.c_int, _vp, _vp, _vp, _vp)
 _sig("zero_offload_step_amp_global_norm", ctypes.c_int, _vp, _vp, _f32, _f32, _f32, _f32, _f32,
      _f32, _vp, _f32, _f32, _i32, _vp)
+_sig("zero_offload_amp_state_init", ctypes.c_int, _vp, _vp, _f32)
 _sig("zero_offload_set_stream", ctypes.c_int, _vp, _vp)
 _sig("zero_offload_destroy", None, _vp)
 _sig("zs_device_alloc_contiguous", _vp, ctypes.c_size_t, _i32, _vp)
@@ -108,17 +109,16 @@ _sig("zs_device_free", None, _vp, ctypes.c_size_t, _i32, _vp)
 
 EXPORTED = ["zs_plan_create", "zs_plan_query", "zs_plan_tensor_slice", "zs_plan_segment",
             "zs_plan_bucket", "zs_plan_run", "zs_plan_state_bytes", "zs_plan_destroy",
-            "zs_workspace_bytes", "zs_slab_layout", "zero_shard_init", "zero_shard_step", "zero_shard_grad_sumsq",
-            "zero_shard_step_global_norm", "zero_shard_amp_state_init", "zero_shard_step_amp",
-            "zero_shard_grad_sumsq_amp", "zero_shard_step_amp_global_norm",
-            "zero_shard_export_state", "zero_shard_import_state",
-            "zero_shard_params", "zero_shard_set_stream",
-            "zero_shard_destroy", "zero_shard_last_error", "zs_host_adamw",
-            "zs_offload_staging_bytes", "zero_offload_init", "zero_offload_step",
+            "zs_workspace_bytes", "zs_slab_layout", "zero_shard_init", "zero_shard_step",
+            "zero_shard_grad_sumsq", "zero_shard_step_global_norm", "zero_shard_amp_state_init",
+            "zero_shard_step_amp", "zero_shard_grad_sumsq_amp", "zero_shard_step_amp_global_norm",
+            "zero_shard_export_state", "zero_shard_import_state", "zero_shard_params",
+            "zero_shard_set_stream", "zero_shard_destroy", "zero_shard_last_error",
+            "zs_host_adamw", "zs_offload_staging_bytes", "zero_offload_init", "zero_offload_step",
             "zero_offload_step_amp", "zero_offload_grad_sumsq", "zero_offload_step_global_norm",
             "zero_offload_grad_sumsq_amp", "zero_offload_step_amp_global_norm",
-            "zero_offload_set_stream", "zero_offload_destroy", "zs_device_alloc_contiguous",
-            "zs_device_free"]
+            "zero_offload_amp_state_init", "zero_offload_set_stream", "zero_offload_destroy",
+            "zs_device_alloc_contiguous", "zs_device_free"]
 
 
 class ZeroShardError(RuntimeError):
@@ -143,6 +143,18 @@ def _int64_array(xs):
 
 def _ptr_array(ptrs):
     return (ctypes.c_void_p * max(1, len(ptrs)))(*[int(p) for p in ptrs])
+
+
+# M of every live context, by handle: the library reads exactly M gradient
+# pointers, so a shorter list would make it read past the pointer array
+_CTX_M = {}
+
+
+def _grad_array(ctx, grads):
+    M = _CTX_M.get(ctx)
+    if M is not None and len(grads) != M:
+        raise ValueError(f"the context takes exactly {M} gradient contributions, got {len(grads)}")
+    return _ptr_array(grads)
 
 
 # ------------------------------------------------------------------ plan
@@ -229,6 +241,7 @@ def zero_shard_init(plan: int, M: int, param_bf16: int, master: int, exp_avg: in
     out = ctypes.c_void_p()
     _check(_lib.zero_shard_init(ctypes.byref(out), plan, M, param_bf16, master, exp_avg,
                                 exp_avg_sq, workspace, workspace_bytes, stream or None, flags))
+    _CTX_M[out.value] = int(M)
     return out.value
 
 
@@ -238,7 +251,7 @@ def zero_shard_step(ctx: int, grads: Sequence[int], lr: float, beta1: float, bet
     """Enqueues one step.  Returns the fp64 grad norm when want_norm (the call then
     waits), else None; with return_code, returns (code, norm) -- code is ZS_OK or
     the warning ZS_NONFINITE.  Negative codes raise ZeroShardError."""
-    arr = _ptr_array(grads)
+    arr = _grad_array(ctx, grads)
     nrm = ctypes.c_double()
     rc = _check(_lib.zero_shard_step(ctx, arr, lr, beta1, beta2, eps, weight_decay, step,
                                      max_grad_norm, ctypes.byref(nrm) if want_norm else None))
@@ -247,13 +260,13 @@ def zero_shard_step(ctx: int, grads: Sequence[int], lr: float, beta1: float, bet
 
 
 def zero_shard_grad_sumsq(ctx: int, grads: Sequence[int], sumsq_dev: int) -> None:
-    _check(_lib.zero_shard_grad_sumsq(ctx, _ptr_array(grads), sumsq_dev))
+    _check(_lib.zero_shard_grad_sumsq(ctx, _grad_array(ctx, grads), sumsq_dev))
 
 
 def zero_shard_step_global_norm(ctx: int, grads: Sequence[int], lr: float, beta1: float,
                                 beta2: float, eps: float, weight_decay: float, step: int,
                                 max_grad_norm: float, global_sumsq_dev: int) -> None:
-    _check(_lib.zero_shard_step_global_norm(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
+    _check(_lib.zero_shard_step_global_norm(ctx, _grad_array(ctx, grads), lr, beta1, beta2, eps,
                                             weight_decay, step, max_grad_norm,
                                             global_sumsq_dev))
 
@@ -270,7 +283,7 @@ def zero_shard_step_amp(ctx: int, grads: Sequence[int], lr: float, beta1: float,
     """Enqueues one loss-scaled fp16 step (see zeroshard.h).  Returns the unscaled
     norm when want_norm (waits), else None; with return_code, (code, norm)."""
     nrm = ctypes.c_double()
-    rc = _check(_lib.zero_shard_step_amp(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
+    rc = _check(_lib.zero_shard_step_amp(ctx, _grad_array(ctx, grads), lr, beta1, beta2, eps,
                                          weight_decay, max_grad_norm, state_dev, growth_factor,
                                          backoff_factor, growth_interval,
                                          ctypes.byref(nrm) if want_norm else None))
@@ -282,7 +295,7 @@ def zero_shard_grad_sumsq_amp(ctx: int, grads: Sequence[int], state_dev: int,
                               sumsq_dev: int) -> None:
     """Multi-rank loss-scaled step, part 1: this shard's sum of squares of the
     unscaled average into the device double at sumsq_dev."""
-    _check(_lib.zero_shard_grad_sumsq_amp(ctx, _ptr_array(grads), state_dev, sumsq_dev))
+    _check(_lib.zero_shard_grad_sumsq_amp(ctx, _grad_array(ctx, grads), state_dev, sumsq_dev))
 
 
 def zero_shard_step_amp_global_norm(ctx: int, grads: Sequence[int], lr: float, beta1: float,
@@ -292,8 +305,8 @@ def zero_shard_step_amp_global_norm(ctx: int, grads: Sequence[int], lr: float, b
                                     growth_interval: int = 2000,
                                     global_sumsq_dev: int = 0) -> None:
     """Part 2: the loss-scaled step decided by the global sum of squares."""
-    _check(_lib.zero_shard_step_amp_global_norm(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
-                                                weight_decay, max_grad_norm, state_dev,
+    _check(_lib.zero_shard_step_amp_global_norm(ctx, _grad_array(ctx, grads), lr, beta1, beta2,
+                                                eps, weight_decay, max_grad_norm, state_dev,
                                                 growth_factor, backoff_factor, growth_interval,
                                                 global_sumsq_dev))
 
@@ -321,6 +334,7 @@ def zero_shard_set_stream(ctx: int, stream: int) -> None:
 
 
 def zero_shard_destroy(ctx: int) -> None:
+    _CTX_M.pop(ctx, None)
     _lib.zero_shard_destroy(ctx)
 
 
@@ -350,6 +364,7 @@ def zero_offload_init(plan: int, M: int, param_bf16: int, master: int, exp_avg: 
     _check(_lib.zero_offload_init(ctypes.byref(out), plan, M, param_bf16, master, exp_avg,
                                   exp_avg_sq, workspace, workspace_bytes, staging, staging_bytes,
                                   chunk_elems, n_threads, stream or None, flags))
+    _CTX_M[out.value] = int(M)
     return out.value
 
 
@@ -359,7 +374,7 @@ def zero_offload_step(ctx: int, grads: Sequence[int], lr: float, beta1: float, b
     """One offloaded step (returns once the host state is updated); results as
     zero_shard_step's."""
     nrm = ctypes.c_double()
-    rc = _check(_lib.zero_offload_step(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
+    rc = _check(_lib.zero_offload_step(ctx, _grad_array(ctx, grads), lr, beta1, beta2, eps,
                                        weight_decay, step, max_grad_norm,
                                        ctypes.byref(nrm) if want_norm else None))
     norm = nrm.value if want_norm else None
@@ -373,7 +388,7 @@ def zero_offload_step_amp(ctx: int, grads: Sequence[int], lr: float, beta1: floa
                           return_code: bool = False):
     """One offloaded loss-scaled step (see zeroshard.h); results as zero_shard_step_amp's."""
     nrm = ctypes.c_double()
-    rc = _check(_lib.zero_offload_step_amp(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
+    rc = _check(_lib.zero_offload_step_amp(ctx, _grad_array(ctx, grads), lr, beta1, beta2, eps,
                                            weight_decay, max_grad_norm, state_dev, growth_factor,
                                            backoff_factor, growth_interval,
                                            ctypes.byref(nrm) if want_norm else None))
@@ -382,20 +397,20 @@ def zero_offload_step_amp(ctx: int, grads: Sequence[int], lr: float, beta1: floa
 
 
 def zero_offload_grad_sumsq(ctx: int, grads: Sequence[int], sumsq_dev: int) -> None:
-    _check(_lib.zero_offload_grad_sumsq(ctx, _ptr_array(grads), sumsq_dev))
+    _check(_lib.zero_offload_grad_sumsq(ctx, _grad_array(ctx, grads), sumsq_dev))
 
 
 def zero_offload_step_global_norm(ctx: int, grads: Sequence[int], lr: float, beta1: float,
                                   beta2: float, eps: float, weight_decay: float, step: int,
                                   max_grad_norm: float, global_sumsq_dev: int) -> None:
-    _check(_lib.zero_offload_step_global_norm(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
-                                              weight_decay, step, max_grad_norm,
+    _check(_lib.zero_offload_step_global_norm(ctx, _grad_array(ctx, grads), lr, beta1, beta2,
+                                              eps, weight_decay, step, max_grad_norm,
                                               global_sumsq_dev))
 
 
 def zero_offload_grad_sumsq_amp(ctx: int, grads: Sequence[int], state_dev: int,
                                 sumsq_dev: int) -> None:
-    _check(_lib.zero_offload_grad_sumsq_amp(ctx, _ptr_array(grads), state_dev, sumsq_dev))
+    _check(_lib.zero_offload_grad_sumsq_amp(ctx, _grad_array(ctx, grads), state_dev, sumsq_dev))
 
 
 def zero_offload_step_amp_global_norm(ctx: int, grads: Sequence[int], lr: float, beta1: float,
@@ -404,10 +419,14 @@ def zero_offload_step_amp_global_norm(ctx: int, grads: Sequence[int], lr: float,
                                       growth_factor: float = 2.0, backoff_factor: float = 0.5,
                                       growth_interval: int = 2000,
                                       global_sumsq_dev: int = 0) -> None:
-    _check(_lib.zero_offload_step_amp_global_norm(ctx, _ptr_array(grads), lr, beta1, beta2, eps,
-                                                  weight_decay, max_grad_norm, state_dev,
+    _check(_lib.zero_offload_step_amp_global_norm(ctx, _grad_array(ctx, grads), lr, beta1, beta2,
+                                                  eps, weight_decay, max_grad_norm, state_dev,
                                                   growth_factor, backoff_factor,
                                                   growth_interval, global_sumsq_dev))
+
+
+def zero_offload_amp_state_init(ctx: int, state_dev: int, init_scale: float) -> None:
+    _check(_lib.zero_offload_amp_state_init(ctx, state_dev, init_scale))
 
 
 def zero_offload_set_stream(ctx: int, stream: int) -> None:
@@ -415,6 +434,7 @@ def zero_offload_set_stream(ctx: int, stream: int) -> None:
 
 
 def zero_offload_destroy(ctx: int) -> None:
+    _CTX_M.pop(ctx, None)
     _lib.zero_offload_destroy(ctx)
 
 
@@ -431,6 +451,31 @@ def zs_device_free(ptr: int, nbytes: int = 0, device: int = 0) -> None:
 
 
 _CONTIG = None
+
+
+def _resolve_device(device):
+    import torch
+    d = torch.device(device if device is not None else "cuda")
+    if d.type == "cuda" and d.index is None:
+        d = torch.device("cuda", torch.cuda.current_device())
+    return d
+
+
+def _check_tensors(ts, n, dtypes, device, what):
+    """Tensors the library will stream over: right dtype and device, contiguous,
+    at least n elements.  A plain int is a raw device address the caller vouches
+    for and is passed through unchecked."""
+    for i, t in enumerate(ts):
+        if isinstance(t, int):
+            continue
+        if t.dtype not in dtypes:
+            raise ValueError(f"{what}[{i}]: dtype {t.dtype}, expected one of {dtypes}")
+        if t.device != device:
+            raise ValueError(f"{what}[{i}]: on {t.device}, the context is on {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{what}[{i}]: not contiguous")
+        if t.numel() < n:
+            raise ValueError(f"{what}[{i}]: {t.numel()} elements, the call reads {n}")
 
 
 def _contiguous_allocator():
@@ -458,8 +503,9 @@ class ZeroShard:
     def __init__(self, numel, decay, world_size=1, rank=0, M=1, device=None, bucket_cap=25_000_000,
                  align=64, flags=0, stream=None, fp16=False, grad_buffers=False, contiguous=False):
         import torch
-        self.device = torch.device(device if device is not None else "cuda")
+        self.device = _resolve_device(device)
         self.M = M
+        self.total_params = int(sum(int(x) for x in numel))
         self.plan = zs_plan_create(numel, decay, world_size, rank, bucket_cap, align)
         q = zs_plan_query(self.plan)
         self.shard_len = q["shard_len"]
@@ -506,27 +552,52 @@ class ZeroShard:
 
     def set_stream(self, stream: int):
         zero_shard_set_stream(self.ctx, stream)
+        self._stream = stream
+
+    def _grad_ptrs(self, grads):
+        import torch
+        if len(grads) != self.M:
+            raise ValueError(f"expected {self.M} gradient contributions, got {len(grads)}")
+        # 16-bit patterns: the context's float type, or an integer view of them
+        half = torch.float16 if self.fp16 else torch.bfloat16
+        _check_tensors(grads, self.shard_len, (half, torch.int16, torch.uint16), self.device,
+                       "grads")
+        return [g if isinstance(g, int) else g.data_ptr() for g in grads]
+
+    def _canon_ptrs(self, ts):
+        import torch
+        _check_tensors(ts, self.total_params, (torch.float32,), self.device, "canonical state")
+        return [t if isinstance(t, int) else t.data_ptr() for t in ts]
 
     def step(self, grads, *, lr, beta1, beta2, eps, weight_decay, step, max_grad_norm=0.0,
              want_norm=False, return_code=False):
-        ptrs = [g if isinstance(g, int) else g.data_ptr() for g in grads]
-        if len(ptrs) != self.M:
-            raise ValueError(f"expected {self.M} gradient contributions")
+        ptrs = self._grad_ptrs(grads)
         return zero_shard_step(self.ctx, ptrs, lr, beta1, beta2, eps, weight_decay, step,
                                max_grad_norm, want_norm, return_code)
 
-    def amp_init(self, init_scale=65536.0):
-        """(Re)initialise the device loss-scaler state to {scale, 0, 0}.  The 16-byte
-        buffer is allocated once and keeps its address, so graphs captured with it
-        stay valid."""
+    def _amp_buffer(self):
+        """The 16-byte scaler state, allocated once (it keeps its address, so graphs
+        captured with it stay valid).  Allocated without a fill: the initialiser
+        writes all 16 bytes on the context's stream, where a fill kernel on torch's
+        current stream could land after it.  torch's current stream is drained once,
+        so no earlier work there still touches the recycled block."""
         import torch
         if self.amp_state is None:
-            self.amp_state = torch.zeros(2, dtype=torch.int64, device=self.device)
-        zero_shard_amp_state_init(self.ctx, self.amp_state.data_ptr(), init_scale)
+            self.amp_state = torch.empty(2, dtype=torch.int64, device=self.device)
+            torch.cuda.current_stream(self.device).synchronize()
+        return self.amp_state
+
+    def amp_init(self, init_scale=65536.0):
+        """(Re)initialise the device loss-scaler state to {scale, 0, 0}, enqueued on
+        the context's stream (zero_shard_amp_state_init)."""
+        zero_shard_amp_state_init(self.ctx, self._amp_buffer().data_ptr(), init_scale)
 
     def amp_read(self):
-        """(scale, growth_tracker, applied_steps) from the device state (waits)."""
+        """(scale, growth_tracker, applied_steps) from the device state (waits for the
+        device)."""
         import numpy as np
+        import torch
+        torch.cuda.synchronize(self.device)
         raw = self.amp_state.cpu().numpy()
         head = raw[:1].view(np.float32)
         return float(head[0]), int(raw[:1].view(np.int32)[1]), int(raw[1])
@@ -534,21 +605,19 @@ class ZeroShard:
     def step_amp(self, grads, *, lr, beta1, beta2, eps, weight_decay, max_grad_norm=0.0,
                  growth_factor=2.0, backoff_factor=0.5, growth_interval=2000, want_norm=False,
                  return_code=False):
-        ptrs = [g if isinstance(g, int) else g.data_ptr() for g in grads]
-        if len(ptrs) != self.M:
-            raise ValueError(f"expected {self.M} gradient contributions")
+        ptrs = self._grad_ptrs(grads)
         return zero_shard_step_amp(self.ctx, ptrs, lr, beta1, beta2, eps, weight_decay,
                                    max_grad_norm, self.amp_state.data_ptr(), growth_factor,
                                    backoff_factor, growth_interval, want_norm, return_code)
 
     def export_state(self, canon_master, canon_exp_avg, canon_exp_avg_sq):
         """Copy this rank's state into canonical device tensors (sum(numel) floats each)."""
-        zero_shard_export_state(self.ctx, canon_master.data_ptr(), canon_exp_avg.data_ptr(),
-                                canon_exp_avg_sq.data_ptr())
+        zero_shard_export_state(self.ctx, *self._canon_ptrs(
+            [canon_master, canon_exp_avg, canon_exp_avg_sq]))
 
     def import_state(self, canon_master, canon_exp_avg, canon_exp_avg_sq):
-        zero_shard_import_state(self.ctx, canon_master.data_ptr(), canon_exp_avg.data_ptr(),
-                                canon_exp_avg_sq.data_ptr())
+        zero_shard_import_state(self.ctx, *self._canon_ptrs(
+            [canon_master, canon_exp_avg, canon_exp_avg_sq]))
 
     def segments(self):
         n = zs_plan_query(self.plan)["n_segments"]
@@ -586,7 +655,7 @@ class ZeroOffload:
     def __init__(self, numel, decay, world_size=1, rank=0, M=1, device=None, bucket_cap=25_000_000,
                  align=64, flags=0, stream=None, chunk_elems=1 << 24, n_threads=0, fp16=False):
         import torch
-        self.device = torch.device(device if device is not None else "cuda")
+        self.device = _resolve_device(device)
         self.M = M
         self.plan = zs_plan_create(numel, decay, world_size, rank, bucket_cap, align)
         q = zs_plan_query(self.plan)
@@ -616,36 +685,26 @@ class ZeroOffload:
     def set_stream(self, stream: int):
         zero_offload_set_stream(self.ctx, stream)
 
+    _grad_ptrs = ZeroShard._grad_ptrs
+    _amp_buffer = ZeroShard._amp_buffer
+    amp_read = ZeroShard.amp_read
+
     def step(self, grads, *, lr, beta1, beta2, eps, weight_decay, step, max_grad_norm=0.0,
              want_norm=False, return_code=False):
-        ptrs = [g if isinstance(g, int) else g.data_ptr() for g in grads]
-        if len(ptrs) != self.M:
-            raise ValueError(f"expected {self.M} gradient contributions")
+        ptrs = self._grad_ptrs(grads)
         return zero_offload_step(self.ctx, ptrs, lr, beta1, beta2, eps, weight_decay, step,
                                  max_grad_norm, want_norm, return_code)
 
     def amp_init(self, init_scale=65536.0):
-        """(Re)initialise the device loss-scaler state (a stable 16-byte buffer);
-        the device-side initialiser runs on the context's device work stream."""
-        import torch
-        if self.amp_state is None:
-            self.amp_state = torch.zeros(2, dtype=torch.int64, device=self.device)
-        raw = self.amp_state.view(torch.float32)
-        raw.zero_()
-        raw[0] = float(init_scale)
-
-    def amp_read(self):
-        """(scale, growth_tracker, applied_steps) from the device state (waits)."""
-        import numpy as np
-        raw = self.amp_state.cpu().numpy()
-        return float(raw[:1].view(np.float32)[0]), int(raw[:1].view(np.int32)[1]), int(raw[1])
+        """(Re)initialise the device loss-scaler state to {scale, 0, 0} (a stable
+        16-byte buffer), enqueued on the context's device stream
+        (zero_offload_amp_state_init)."""
+        zero_offload_amp_state_init(self.ctx, self._amp_buffer().data_ptr(), init_scale)
 
     def step_amp(self, grads, *, lr, beta1, beta2, eps, weight_decay, max_grad_norm=0.0,
                  growth_factor=2.0, backoff_factor=0.5, growth_interval=2000, want_norm=False,
                  return_code=False):
-        ptrs = [g if isinstance(g, int) else g.data_ptr() for g in grads]
-        if len(ptrs) != self.M:
-            raise ValueError(f"expected {self.M} gradient contributions")
+        ptrs = self._grad_ptrs(grads)
         return zero_offload_step_amp(self.ctx, ptrs, lr, beta1, beta2, eps, weight_decay,
                                      max_grad_norm, self.amp_state.data_ptr(), growth_factor,
                                      backoff_factor, growth_interval, want_norm, return_code)

@@ -14,6 +14,7 @@
 #include "../../include/zeroshard.h"
 #include "abi_internal.h"
 #include "internal.h"
+#include "lds.h"
 
 namespace zs {
 
@@ -37,7 +38,7 @@ struct zs_ctx {
   bool stage = false;  // ZS_STAGE_AVERAGE
   int64_t shard_len = 0, n_pieces = 0, n_whole_pieces = 0, canon_len = 0;
   int32_t n_runs = 0;
-  int32_t waves_per_cu = 0, waves_per_cu_staged = 0;
+  zs::LdsPlan lds{};       // the dynamic LDS of every capped launch (lds.h)
   int64_t max_groups = 0;  // work-groups per launch slice (0: the dispatch limit)
   uint16_t* param = nullptr;
   float* master = nullptr;
@@ -81,7 +82,7 @@ zs::WorkspaceLayout workspace_layout(int64_t shard_len, int64_t n_runs, int64_t 
 namespace zs {
 
 WorkspaceLayout plan_workspace(const zs_plan* plan, uint32_t flags) {
-  return workspace_layout(plan->shard_len, (int64_t)plan->runs.size(),
+  return workspace_layout(plan->shard_len, (int64_t)plan->run_table.size() - 1,
                           (int64_t)plan->pieces.size(), zs::sumsq_partials(plan->shard_len),
                           (flags & ZS_STAGE_AVERAGE) ? plan->shard_len : 0);
 }
@@ -142,49 +143,49 @@ using zs::ehip;
 using zs::einval;
 using zs::plan_workspace;
 
+static_assert(zs::kCapTileElems == zs::kStepTileElems, "the caps count the step kernels' tiles");
+
+namespace zs {
+
+// The context's LDS reservations for M contributions over a shard, from the
+// current device's CU count and LDS sizes and ZS_WAVES_PER_CU (unset: the
+// measured table; 0: no cap; 3..64: that cap), each checked with the largest
+// static LDS of the kernels that take a reservation against the device's
+// per-workgroup limit.  ZS_OK, ZS_EINVAL (a bad override, or a reservation that
+// does not fit: nothing is launched) or ZS_EHIP (a failed device query).
+int make_lds_plan(int32_t M, int64_t shard_len, const char* who, LdsPlan* out) {
+  const std::string w(who);
+  int32_t override_waves;
+  if (!parse_waves_override(getenv("ZS_WAVES_PER_CU"), &override_waves))
+    return einval((w + ": ZS_WAVES_PER_CU must be 0 (no cap) or 3..64").c_str());
+  int dev = 0, n_cu = 0, per_cu = 0, per_wg = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+  if (e == hipSuccess)
+    e = hipDeviceGetAttribute(&per_wg, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return ehip((w + ": device query").c_str(), e);
+  const size_t lds_cu = per_cu > 0 ? (size_t)per_cu : kLdsPerCuDefault;
+  size_t static_lds = 0;
+  if ((e = reserved_kernels_static_lds(M, &static_lds)) != hipSuccess)
+    return ehip((w + ": kernel attributes").c_str(), e);
+  const LdsPlan p = lds_plan(M, shard_len, n_cu > 0 ? n_cu : 256, lds_cu, override_waves);
+  if (!lds_plan_fits(p, static_lds, per_wg > 0 ? (size_t)per_wg : 0, lds_cu))
+    return einval((w + ": an LDS reservation (step " + std::to_string(p.step) + ", staged step " +
+                   std::to_string(p.step_staged) + ", staged norm " +
+                   std::to_string(p.stage_norm) + ", copy " + std::to_string(p.copy) +
+                   " bytes, plus " + std::to_string(static_lds) +
+                   " static) exceeds the device's per-workgroup LDS limit of " +
+                   std::to_string(per_wg) + " bytes")
+                      .c_str());
+  *out = p;
+  return ZS_OK;
+}
+
+}  // namespace zs
+
 namespace {
-
-// Resident-wave cap of the step kernels per CU (0: no cap), by M and shard size.
-// Measured on MI355X with the device-scope non-temporal stores and the
-// staggered slab placement of zs_slab_layout: caps 5..12 swept for every M on
-// flat 164M-, 1G- and 4.3G-element shards, two rounds on the same buffers
-// (repeatable to 0.3%), and checked on the GPT, Llama and stress layouts.  Fewer
-// contributions leave each wave less in flight, so more waves pay off; from
-// M = 10 on, 7 waves are best everywhere (6 and 5 lose 3-20%).  Fresh
-// allocations move any of these figures by up to 3%, so only differences seen
-// on the same buffers count.  ZS_WAVES_PER_CU overrides the table.
-int32_t default_waves_per_cu(int32_t M, int64_t shard_len, int32_t n_cu) {
-  const char* env = getenv("ZS_WAVES_PER_CU");
-  if (env && *env) {
-    const long v = strtol(env, nullptr, 10);
-    if (v == 0 || (v >= 3 && v <= 64)) return (int32_t)v;
-  }
-  //                                   M: 0   1   2   3   4   5   6   7   8   9  10  11  12  13  14  15  16
-  static const int8_t kSmall[ZS_MAX_M + 1] = {0, 12, 11, 11, 10, 10, 9, 9, 9, 9, 7, 7, 7, 7, 7, 7, 7};
-  static const int8_t kLarge[ZS_MAX_M + 1] = {0, 11, 11, 10, 9, 9, 8, 8, 8, 8, 7, 7, 7, 7, 7, 7, 7};
-  static const int8_t kHuge[ZS_MAX_M + 1] = {0, 12, 10, 10, 8, 8, 9, 9, 7, 7, 7, 7, 7, 7, 7, 7, 7};
-  if (M < 1 || M > ZS_MAX_M) return 0;
-  int32_t cap;
-  if (shard_len <= (int64_t(1) << 28)) cap = kSmall[M];
-  else cap = shard_len <= (int64_t(1) << 31) ? kLarge[M] : kHuge[M];
-  // A grid that up to 16 waves per CU cover in one round runs as one round: at
-  // 1M elements (4,096 tiles) the table's cap leaves a partial second round,
-  // and cap 16 measured 0-14% faster there (M = 1..16); smaller grids keep the
-  // table's cap, which spreads their few waves over more CUs.
-  const int64_t tiles = (shard_len + zs::kStepTileElems - 1) / zs::kStepTileElems;
-  const int64_t one_round = (tiles + n_cu - 1) / n_cu;
-  if (one_round > cap && one_round <= 16) cap = (int32_t)one_round;
-  return cap;
-}
-
-// Compute units of the current device (256 on MI355X if the query fails).
-int32_t device_cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
-  return n;
-}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -226,25 +227,6 @@ zs::RunTable run_table(zs_ctx* ctx) {
                       : nullptr;
   rt.n_runs = ctx->n_runs;
   return rt;
-}
-
-// The tile-flag table of a run table (with its sentinel): per 256-element tile,
-// 2 bits -- the decay flag of a tile inside one run, or 2 for a tile that
-// straddles a run boundary.
-std::vector<uint32_t> tile_flags(const std::vector<zs::Run>& table, int64_t shard_len) {
-  const int64_t n_runs = (int64_t)table.size() - 1;
-  std::vector<uint32_t> w((size_t)zs::tile_flag_words(shard_len, n_runs), 0u);
-  if (w.empty()) return w;
-  const int64_t tiles = (shard_len + zs::kStepTileElems - 1) / zs::kStepTileElems;
-  size_t r = 0;  // the run holding the tile's first element
-  for (int64_t t = 0; t < tiles; t++) {
-    const int64_t lo = t * zs::kStepTileElems;
-    const int64_t hi = std::min(shard_len, lo + zs::kStepTileElems);
-    while (table[r + 1].start <= lo) r++;
-    const uint32_t f = table[r + 1].start < hi ? 2u : (uint32_t)(table[r].flags & 1);
-    w[(size_t)(t >> 4)] |= f << ((t & 15) * 2);
-  }
-  return w;
 }
 
 }  // namespace
@@ -302,17 +284,8 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   const zs::WorkspaceLayout lay = plan_workspace(plan, flags);
   if (workspace_bytes < lay.total)
     return einval("zero_shard_init: workspace smaller than zs_workspace_bytes(plan, M, flags)");
-  std::vector<zs::Run> table;
-  std::vector<uint32_t> tflags;
-  try {
-    table = plan->runs;
-    if (table.empty()) table.push_back({0, 0, 0});
-    table.push_back({plan->shard_len, 0, 0});  // sentinel: starts past every element
-    tflags = tile_flags(table, plan->shard_len);
-  } catch (const std::bad_alloc&) {
-    zs::set_error("zero_shard_init: out of host memory");
-    return ZS_ENOMEM;
-  }
+  const std::vector<zs::Run>& table = plan->run_table;  // runs + sentinel
+  const std::vector<uint32_t>& tflags = plan->tile_flags;
 
   zs_ctx* c = new (std::nothrow) zs_ctx;
   if (!c) {
@@ -328,10 +301,10 @@ extern "C" int zero_shard_init(zs_ctx** out, const zs_plan* plan, int32_t M, voi
   c->n_pieces = (int64_t)plan->pieces.size();
   c->n_whole_pieces = plan->n_whole_pieces;
   c->canon_len = plan->total_params;
-  const int32_t n_cu = device_cu_count();
-  c->waves_per_cu = default_waves_per_cu(M, plan->shard_len, n_cu);
-  // the staged step reads 16 B of gradient per lane, as many bytes as M = 2
-  c->waves_per_cu_staged = default_waves_per_cu(2, plan->shard_len, n_cu);
+  if (int rc = zs::make_lds_plan(M, plan->shard_len, "zero_shard_init", &c->lds)) {
+    delete c;
+    return rc;
+  }
   c->max_groups = zs::max_groups_from_env();
   c->param = static_cast<uint16_t*>(param_bf16);
   c->master = master;
@@ -371,8 +344,8 @@ int enqueue_step(zs_ctx* ctx, const zs::GradPtrs& g, const zs::StepConsts& k, bo
   float* stage = (need_norm && !external_sumsq) ? stage_area(ctx) : nullptr;
   if (need_norm) {
     if (!external_sumsq) {
-      e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), stage, ctx->max_groups,
-                           ctx->stream);
+      e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), stage, ctx->lds.stage_norm,
+                           ctx->max_groups, ctx->stream);
       if (e != hipSuccess) return ehip("zero_shard_step: norm pass", e);
     }
     e = zs::launch_finalize(final_partials(ctx), zs::final_partials(ctx->shard_len),
@@ -383,10 +356,10 @@ int enqueue_step(zs_ctx* ctx, const zs::GradPtrs& g, const zs::StepConsts& k, bo
   if (stage)
     e = zs::launch_step_staged(false, stage, ctx->master, ctx->m, ctx->v, ctx->param,
                                ctx->shard_len, run_table(ctx), sc, k, nullptr,
-                               ctx->waves_per_cu_staged, ctx->max_groups, ctx->stream);
+                               ctx->lds.step_staged, ctx->max_groups, ctx->stream);
   else
     e = zs::launch_step(ctx->M, need_norm, g, ctx->master, ctx->m, ctx->v, ctx->param,
-                        ctx->shard_len, run_table(ctx), sc, k, ctx->waves_per_cu,
+                        ctx->shard_len, run_table(ctx), sc, k, ctx->lds.step,
                         ctx->max_groups, ctx->stream);
   if (e != hipSuccess) return ehip("zero_shard_step: step kernel", e);
   return ZS_OK;
@@ -442,7 +415,7 @@ extern "C" int zero_shard_grad_sumsq(zs_ctx* ctx, const void* const* grads, doub
   const int32_t n_final = ctx->shard_len ? zs::final_partials(ctx->shard_len) : 0;
   hipError_t e = hipSuccess;
   if (n_final)
-    e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), nullptr, ctx->max_groups,
+    e = zs::launch_sumsq(ctx->M, g, ctx->shard_len, partials(ctx), nullptr, 0, ctx->max_groups,
                          ctx->stream);
   if (e == hipSuccess) e = zs::launch_sumsq_total(final_partials(ctx), n_final, sumsq_dev,
                                                   ctx->stream);
@@ -477,7 +450,7 @@ int state_copy(zs_ctx* ctx, bool do_export, float* cm, float* cmm, float* cv, co
   const hipError_t e = zs::launch_state_copy(
       do_export, ctx->fp16, reinterpret_cast<const zs::Piece*>(ctx->ws + ctx->lay.pieces_off),
       ctx->n_pieces, ctx->n_whole_pieces, ctx->master, ctx->m, ctx->v, ctx->param, cm, cmm, cv,
-      ctx->max_groups, ctx->stream);
+      ctx->lds.copy, ctx->max_groups, ctx->stream);
   return e == hipSuccess ? ZS_OK : ehip(who, e);
 }
 
@@ -537,11 +510,11 @@ int amp_finish(zs_ctx* ctx, const zs::GradPtrs& g, zs::AmpState* st, const zs::A
       e = zs::launch_step_staged(true, stage_area(ctx), ctx->master, ctx->m, ctx->v, ctx->param,
                                  ctx->shard_len, run_table(ctx), scalars(ctx),
                                  zs::StepConsts{}, device_consts(ctx),
-                                 ctx->waves_per_cu_staged, ctx->max_groups, ctx->stream);
+                                 ctx->lds.step_staged, ctx->max_groups, ctx->stream);
     else
       e = zs::launch_step_f16(ctx->M, g, ctx->master, ctx->m, ctx->v, ctx->param,
                               ctx->shard_len, run_table(ctx), scalars(ctx), device_consts(ctx),
-                              ctx->waves_per_cu, ctx->max_groups, ctx->stream);
+                              ctx->lds.step, ctx->max_groups, ctx->stream);
     if (e != hipSuccess) return ehip((w + ": step kernel").c_str(), e);
   }
   if (grad_norm_out) {
@@ -572,8 +545,9 @@ extern "C" int zero_shard_step_amp(zs_ctx* ctx, const void* const* grads, float 
   if ((rc = gather_grads(ctx, grads, &g))) return rc;
   zs::AmpState* st = reinterpret_cast<zs::AmpState*>(state_dev);
   if (ctx->shard_len > 0) {
-    const hipError_t e = zs::launch_sumsq_f16(ctx->M, g, ctx->shard_len, partials(ctx), st,
-                                              stage_area(ctx), ctx->max_groups, ctx->stream);
+    const hipError_t e =
+        zs::launch_sumsq_f16(ctx->M, g, ctx->shard_len, partials(ctx), st, stage_area(ctx),
+                             ctx->lds.stage_norm, ctx->max_groups, ctx->stream);
     if (e != hipSuccess) return ehip("zero_shard_step_amp: norm pass", e);
   }
   return amp_finish(ctx, g, st, p, nullptr, grad_norm_out, who);
@@ -596,7 +570,7 @@ extern "C" int zero_shard_grad_sumsq_amp(zs_ctx* ctx, const void* const* grads,
   if (n_final)
     e = zs::launch_sumsq_f16(ctx->M, g, ctx->shard_len, partials(ctx),
                              reinterpret_cast<const zs::AmpState*>(state_dev), stage_area(ctx),
-                             ctx->max_groups, ctx->stream);
+                             ctx->lds.stage_norm, ctx->max_groups, ctx->stream);
   if (e == hipSuccess)
     e = zs::launch_sumsq_total(final_partials(ctx), n_final, sumsq_dev, ctx->stream);
   return e == hipSuccess ? ZS_OK : ehip("zero_shard_grad_sumsq_amp", e);

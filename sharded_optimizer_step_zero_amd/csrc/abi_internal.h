@@ -9,6 +9,7 @@
 
 #include "../../include/zeroshard.h"
 #include "internal.h"
+#include "lds.h"
 
 namespace zs {
 
@@ -27,5 +28,8 @@ int check_amp_args(const char* who, float lr, float beta1, float beta2, float ep
                    float weight_decay, float max_grad_norm, const zs_amp_state* state_dev,
                    float growth_factor, float backoff_factor, int32_t growth_interval,
                    AmpParams* p);
+// The LDS reservations of a context on the current device (lds.h), checked
+// against its limits; ZS_OK, ZS_EINVAL or ZS_EHIP with the message set.
+int make_lds_plan(int32_t M, int64_t shard_len, const char* who, LdsPlan* out);
 
 }  // namespace zs

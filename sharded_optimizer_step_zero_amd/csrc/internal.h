@@ -157,13 +157,14 @@ int64_t max_groups_from_env();
 // one dispatch carries (2^32 - 1 work-items) goes out as consecutive slices;
 // max_groups > 0 caps the work-groups of each slice below that (a context takes
 // it from ZS_MAX_GROUPS_PER_LAUNCH at init; 0 leaves only the dispatch limit).
-// waves_per_cu > 0 caps the resident waves per CU of a step kernel (0: no cap).
+// lds / stage_lds: the dynamic LDS each work-group of a capped launch reserves
+// (lds.h; checked against the device's limits when the context is made).
 //
 // The norm pass over a non-empty shard: both partial levels into `partials`.
 // stage (nullable): also store the fp32 averages, shard_len floats, for
 // launch_step_staged.
 hipError_t launch_sumsq(int M, const GradPtrs& g, int64_t shard_len, double* partials,
-                        float* stage, int64_t max_groups, hipStream_t stream);
+                        float* stage, size_t stage_lds, int64_t max_groups, hipStream_t stream);
 // Reduces the partials (or takes *external_sumsq when non-null) into *out.
 hipError_t launch_finalize(const double* partials, int32_t n_partials,
                            const double* external_sumsq, float max_norm, int clip,
@@ -174,15 +175,15 @@ hipError_t launch_sumsq_total(const double* partials, int32_t n_partials, double
 // step that also computes the step constants on the device and updates the
 // scaler, the step kernel, and the scaler initialisation.
 hipError_t launch_sumsq_f16(int M, const GradPtrs& g, int64_t shard_len, double* partials,
-                            const AmpState* st, float* stage, int64_t max_groups,
-                            hipStream_t stream);
+                            const AmpState* st, float* stage, size_t stage_lds,
+                            int64_t max_groups, hipStream_t stream);
 // external (nullable): a global sum of squares used instead of the partials.
 hipError_t launch_amp_finalize(const double* partials, int32_t n_partials,
                                const double* external, AmpState* st, const AmpParams& p,
                                ClipScalars* out, StepConsts* kout, hipStream_t stream);
 hipError_t launch_step_f16(int M, const GradPtrs& g, float* master, float* m, float* v,
                            uint16_t* param, int64_t shard_len, const RunTable& rt,
-                           const ClipScalars* clip, const StepConsts* k, int32_t waves_per_cu,
+                           const ClipScalars* clip, const StepConsts* k, size_t lds,
                            int64_t max_groups, hipStream_t stream);
 hipError_t launch_amp_state_init(AmpState* st, float scale, hipStream_t stream);
 // The step on the averages a norm pass staged (amp: constants *kd and an fp16
@@ -190,21 +191,25 @@ hipError_t launch_amp_state_init(AmpState* st, float scale, hipStream_t stream);
 hipError_t launch_step_staged(bool amp, const float* stage, float* master, float* m, float* v,
                               uint16_t* param, int64_t shard_len, const RunTable& rt,
                               const ClipScalars* clip, const StepConsts& kh, const StepConsts* kd,
-                              int32_t waves_per_cu, int64_t max_groups, hipStream_t stream);
+                              size_t lds, int64_t max_groups, hipStream_t stream);
 
 // Copies fp32 master/m/v between the shard and the canonical order over the
 // piece table (export: shard -> canonical; import: canonical -> shard, which
 // also writes param = bf16_rne(master), or fp16 when param_f16, for the
 // imported elements).
 hipError_t launch_state_copy(bool do_export, bool param_f16, const Piece* pieces,
-                             int64_t n_pieces, int64_t n_whole, float* master, float* m, float* v, uint16_t* param,
-                             float* c_master, float* c_m, float* c_v, int64_t max_groups,
-                             hipStream_t stream);
+                             int64_t n_pieces, int64_t n_whole, float* master, float* m,
+                             float* v, uint16_t* param, float* c_master, float* c_m, float* c_v,
+                             size_t lds, int64_t max_groups, hipStream_t stream);
 // The fused bf16 step (use_clip: scale by the coefficient in *clip, or skip).
 hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, float* m,
                        float* v, uint16_t* param, int64_t shard_len, const RunTable& rt,
-                       const ClipScalars* clip, const StepConsts& k, int32_t waves_per_cu,
+                       const ClipScalars* clip, const StepConsts& k, size_t lds,
                        int64_t max_groups, hipStream_t stream);
+
+// The largest static LDS of the kernels that launch with a reservation, for M
+// contributions (hipFuncGetAttributes on the current device).
+hipError_t reserved_kernels_static_lds(int M, size_t* worst);
 
 }  // namespace zs
 
@@ -218,6 +223,8 @@ struct zs_plan {
   std::vector<int64_t> bucket_off, bucket_len;
   std::vector<zs::Segment> segments;
   std::vector<zs::Run> runs;
+  std::vector<zs::Run> run_table;     // runs (at least one) + a sentinel at shard_len
+  std::vector<uint32_t> tile_flags;   // 2 bits per step tile; empty with one run
   std::vector<zs::Piece> pieces;  // whole pieces first (n_whole_pieces), then parts
   int64_t n_whole_pieces = 0;
   int64_t shard_len = 0, padded_total = 0, total_params = 0;

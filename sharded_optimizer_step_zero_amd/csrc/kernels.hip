@@ -44,6 +44,7 @@
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
+#include "lds.h"
 
 namespace zs {
 namespace {
@@ -124,10 +125,6 @@ __device__ __forceinline__ uint32_t decay_flag(const RunTable& rt, int64_t tile,
   while (rt.runs[r + 1].start <= e) r++;
   return (uint32_t)rt.runs[r].flags & 1u;
 }
-
-// LDS per CU on gfx950; reserving lds_cu / waves_per_cu bytes per single-wave
-// workgroup lets at most waves_per_cu of them reside on a CU.
-constexpr size_t kLdsPerCu = 160 * 1024;
 
 constexpr int kStepLanes = 64;   // one wave64 per workgroup
 constexpr int kStepVec = 4;      // elements per lane
@@ -361,7 +358,6 @@ __global__ __launch_bounds__(kThreads) void sumsq_total_kernel(const double* __r
 // import 5.11 against 5.06.
 constexpr int kCopyLanes = 64;
 constexpr int32_t kCopySplit = (int32_t)(kPieceElems / kCopyPart);
-constexpr int kCopyWavesPerCu = 10;
 static_assert(kCopyPart == kCopyLanes * 4, "one 4-element group per lane");
 
 template <bool EXPORT, bool F16>
@@ -575,7 +571,10 @@ __global__ __launch_bounds__(kThreads) void amp_finalize_kernel(
     s.applied_steps += 1;
     const int32_t good = s.growth_tracker + 1;
     if (good == p.interval) {
-      s.scale = s.scale * p.growth;
+      // a grown scale that is not finite is dropped (torch's GradScaler): an
+      // Inf scale would unscale every later gradient to zero
+      const float grown = s.scale * p.growth;
+      if (__builtin_isfinite(grown)) s.scale = grown;
       s.growth_tracker = 0;
     } else {
       s.growth_tracker = good;
@@ -683,28 +682,6 @@ __global__ __launch_bounds__(kStepLanes) void step_staged_kernel(
   store_step(master, mom1, mom2, param, tile0, p4, m4, v4, pk);
 }
 
-// The LDS reservation that caps a single-wave step kernel at waves_per_cu
-// resident waves per CU (0: no cap).  Caps below 3 would reserve more than a
-// workgroup may hold, so they mean no cap as well.
-// Resident workgroups per CU of the staged norm pass (0: no cap), by M, applied
-// through an LDS reservation the kernel never uses.  The staged pass adds a
-// write stream to a read pass; the more contributions each workgroup reads, the
-// fewer of them stream best.  Measured on MI355X (GPT-1.3B-size shard, the
-// loss-scaled and the clipped bf16 step, same buffers): M = 2 uncapped; M = 4:
-// 6 (-2.1% step time); M = 8: 5 (-3.4%); M = 16: 4 (-2.6%).  The fused
-// (read-only) pass runs uncapped: caps measured neutral to slower there.
-constexpr int8_t kStageWgsPerCu[kMaxM + 1] = {0, 0, 0, 6, 6, 5, 5, 5, 5, 4, 4, 4, 4, 4, 4, 4, 4};
-
-size_t stage_lds(int M) {
-  const int w = kStageWgsPerCu[M];
-  return w ? (kLdsPerCu / (size_t)w) & ~(size_t)255 : 0;
-}
-
-size_t step_lds(int32_t waves_per_cu) {
-  if (waves_per_cu < 3) return 0;
-  return (kLdsPerCu / (size_t)waves_per_cu) & ~(size_t)255;
-}
-
 // A dispatch carries at most 2^32 - 1 work-items (its grid size is a 32-bit
 // count of work-items), which a step grid passes beyond 2^34 elements.  Larger
 // grids go out as consecutive slices of whole work-groups on the same stream;
@@ -724,12 +701,12 @@ hipError_t for_slices(int64_t groups, int block, int64_t max_groups, F&& launch)
 
 template <int M>
 hipError_t launch_sumsq_f16_m(const GradPtrs& g, int64_t shard_len, double* partials,
-                              const AmpState* st, float* stage, int64_t max_groups,
-                              hipStream_t stream) {
+                              const AmpState* st, float* stage, size_t stage_lds,
+                              int64_t max_groups, hipStream_t stream) {
   const int64_t p1 = (shard_len + kNormTile - 1) / kNormTile;
   const hipError_t e = for_slices(p1, kThreads, max_groups, [&](int64_t g0, unsigned n) {
     if (stage)
-      hipLaunchKernelGGL((sumsq_f16_kernel<M, true>), dim3(n), dim3(kThreads), stage_lds(M),
+      hipLaunchKernelGGL((sumsq_f16_kernel<M, true>), dim3(n), dim3(kThreads), stage_lds,
                          stream, g, shard_len, partials, st, stage, g0);
     else
       hipLaunchKernelGGL((sumsq_f16_kernel<M, false>), dim3(n), dim3(kThreads), 0, stream, g,
@@ -772,11 +749,11 @@ hipError_t launch_step_m(bool use_clip, const GradPtrs& g, float* master, float*
 
 template <int M>
 hipError_t launch_sumsq_m(const GradPtrs& g, int64_t shard_len, double* partials, float* stage,
-                          int64_t max_groups, hipStream_t stream) {
+                          size_t stage_lds, int64_t max_groups, hipStream_t stream) {
   const int64_t p1 = (shard_len + kNormTile - 1) / kNormTile;
   const hipError_t e = for_slices(p1, kThreads, max_groups, [&](int64_t g0, unsigned n) {
     if (stage)
-      hipLaunchKernelGGL((sumsq_kernel<M, true>), dim3(n), dim3(kThreads), stage_lds(M), stream,
+      hipLaunchKernelGGL((sumsq_kernel<M, true>), dim3(n), dim3(kThreads), stage_lds, stream,
                          g, shard_len, partials, stage, g0);
     else
       hipLaunchKernelGGL((sumsq_kernel<M, false>), dim3(n), dim3(kThreads), 0, stream, g,
@@ -836,11 +813,10 @@ static bool step_args_ok(const RunTable& rt) {
 
 hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, float* m,
                        float* v, uint16_t* param, int64_t shard_len, const RunTable& rt,
-                       const ClipScalars* clip, const StepConsts& k, int32_t waves_per_cu,
+                       const ClipScalars* clip, const StepConsts& k, size_t lds,
                        int64_t max_groups, hipStream_t stream) {
   if (shard_len <= 0) return hipSuccess;
   if (!step_args_ok(rt)) return hipErrorInvalidValue;
-  const size_t lds = step_lds(waves_per_cu);
 #define ZS_CALL_STEP(X) \
   launch_step_m<X>(use_clip, g, master, m, v, param, shard_len, rt, clip, k, lds, max_groups, \
                    stream)
@@ -849,9 +825,10 @@ hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, f
 }
 
 hipError_t launch_sumsq(int M, const GradPtrs& g, int64_t shard_len, double* partials,
-                        float* stage, int64_t max_groups, hipStream_t stream) {
+                        float* stage, size_t stage_lds, int64_t max_groups, hipStream_t stream) {
   if (shard_len <= 0 || level1_partials(shard_len) > 0x7fffffff) return hipErrorInvalidValue;
-#define ZS_CALL_SUMSQ(X) launch_sumsq_m<X>(g, shard_len, partials, stage, max_groups, stream)
+#define ZS_CALL_SUMSQ(X) \
+  launch_sumsq_m<X>(g, shard_len, partials, stage, stage_lds, max_groups, stream)
   ZS_DISPATCH_M(M, ZS_CALL_SUMSQ)
 #undef ZS_CALL_SUMSQ
 }
@@ -859,11 +836,10 @@ hipError_t launch_sumsq(int M, const GradPtrs& g, int64_t shard_len, double* par
 hipError_t launch_state_copy(bool do_export, bool param_f16, const Piece* pieces,
                              int64_t n_pieces, int64_t n_whole, float* master, float* m, float* v,
                              uint16_t* param, float* c_master, float* c_m, float* c_v,
-                             int64_t max_groups, hipStream_t stream) {
+                             size_t lds, int64_t max_groups, hipStream_t stream) {
   if (n_pieces <= 0) return hipSuccess;
   if (n_whole < 0 || n_whole > n_pieces) return hipErrorInvalidValue;
   const dim3 block(kCopyLanes);
-  const size_t lds = step_lds(kCopyWavesPerCu);
   const int64_t groups = n_whole * kCopySplit + (n_pieces - n_whole);
   return for_slices(groups, kCopyLanes, max_groups, [&](int64_t g0, unsigned n) {
     if (do_export)
@@ -879,11 +855,11 @@ hipError_t launch_state_copy(bool do_export, bool param_f16, const Piece* pieces
 }
 
 hipError_t launch_sumsq_f16(int M, const GradPtrs& g, int64_t shard_len, double* partials,
-                            const AmpState* st, float* stage, int64_t max_groups,
-                            hipStream_t stream) {
+                            const AmpState* st, float* stage, size_t stage_lds,
+                            int64_t max_groups, hipStream_t stream) {
   if (shard_len <= 0 || level1_partials(shard_len) > 0x7fffffff) return hipErrorInvalidValue;
 #define ZS_CALL_SUMSQ16(X) \
-  launch_sumsq_f16_m<X>(g, shard_len, partials, st, stage, max_groups, stream)
+  launch_sumsq_f16_m<X>(g, shard_len, partials, st, stage, stage_lds, max_groups, stream)
   ZS_DISPATCH_M(M, ZS_CALL_SUMSQ16)
 #undef ZS_CALL_SUMSQ16
 }
@@ -898,11 +874,10 @@ hipError_t launch_amp_finalize(const double* partials, int32_t n_partials,
 
 hipError_t launch_step_f16(int M, const GradPtrs& g, float* master, float* m, float* v,
                            uint16_t* param, int64_t shard_len, const RunTable& rt,
-                           const ClipScalars* clip, const StepConsts* k, int32_t waves_per_cu,
+                           const ClipScalars* clip, const StepConsts* k, size_t lds,
                            int64_t max_groups, hipStream_t stream) {
   if (shard_len <= 0) return hipSuccess;
   if (!step_args_ok(rt)) return hipErrorInvalidValue;
-  const size_t lds = step_lds(waves_per_cu);
 #define ZS_CALL_STEP16(X) \
   launch_step_f16_m<X>(g, master, m, v, param, shard_len, rt, clip, k, lds, max_groups, stream)
   ZS_DISPATCH_M(M, ZS_CALL_STEP16)
@@ -912,10 +887,9 @@ hipError_t launch_step_f16(int M, const GradPtrs& g, float* master, float* m, fl
 hipError_t launch_step_staged(bool amp, const float* stage, float* master, float* m, float* v,
                               uint16_t* param, int64_t shard_len, const RunTable& rt,
                               const ClipScalars* clip, const StepConsts& kh, const StepConsts* kd,
-                              int32_t waves_per_cu, int64_t max_groups, hipStream_t stream) {
+                              size_t lds, int64_t max_groups, hipStream_t stream) {
   if (shard_len <= 0) return hipSuccess;
   if (!step_args_ok(rt)) return hipErrorInvalidValue;
-  const size_t lds = step_lds(waves_per_cu);
   const int64_t tiles = (shard_len + kTile - 1) / kTile;
   return for_slices(tiles, kStepLanes, max_groups, [&](int64_t g0, unsigned nt) {
     if (amp)
@@ -945,6 +919,43 @@ hipError_t launch_sumsq_total(const double* partials, int32_t n_partials, double
   hipLaunchKernelGGL(sumsq_total_kernel, dim3(1), dim3(kThreads), 0, stream, partials,
                      n_partials, out);
   return hipGetLastError();
+}
+
+namespace {
+
+hipError_t static_lds_of(const void* kernel, size_t* worst) {
+  hipFuncAttributes a{};
+  const hipError_t e = hipFuncGetAttributes(&a, kernel);
+  if (e == hipSuccess && a.sharedSizeBytes > *worst) *worst = a.sharedSizeBytes;
+  return e;
+}
+
+template <int M>
+hipError_t static_lds_m(size_t* worst) {
+  const void* k[] = {reinterpret_cast<const void*>(&step_kernel<M, false>),
+                     reinterpret_cast<const void*>(&step_kernel<M, true>),
+                     reinterpret_cast<const void*>(&step_f16_kernel<M>),
+                     reinterpret_cast<const void*>(&sumsq_kernel<M, true>),
+                     reinterpret_cast<const void*>(&sumsq_f16_kernel<M, true>),
+                     reinterpret_cast<const void*>(&step_staged_kernel<false>),
+                     reinterpret_cast<const void*>(&step_staged_kernel<true>),
+                     reinterpret_cast<const void*>(&state_copy_kernel<true, false>),
+                     reinterpret_cast<const void*>(&state_copy_kernel<false, false>),
+                     reinterpret_cast<const void*>(&state_copy_kernel<false, true>)};
+  for (const void* f : k) {
+    const hipError_t e = static_lds_of(f, worst);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t reserved_kernels_static_lds(int M, size_t* worst) {
+  *worst = 0;
+#define ZS_CALL_STATIC(X) static_lds_m<X>(worst)
+  ZS_DISPATCH_M(M, ZS_CALL_STATIC)
+#undef ZS_CALL_STATIC
 }
 
 }  // namespace zs

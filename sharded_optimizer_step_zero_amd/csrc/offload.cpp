@@ -114,6 +114,7 @@ struct zs_offload {
   bool fp16 = false;  // ZS_FP16: fp16 gradients and param, zero_offload_step_amp
   int64_t shard_len = 0, chunk = 0;
   int64_t max_groups = 0;  // work-groups per launch slice (0: the dispatch limit)
+  zs::LdsPlan lds{};       // the dynamic LDS of every capped launch (lds.h)
   std::vector<zs::HostRun> runs;
   std::vector<std::pair<int64_t, int64_t>> chunks;
   uint16_t* param = nullptr;
@@ -184,6 +185,7 @@ extern "C" int zero_offload_init(zs_offload** out, const zs_plan* plan, int32_t 
   if (!c) return enomem("zero_offload_init: out of host memory");
   c->M = M;
   c->max_groups = zs::max_groups_from_env();
+  if (int rc = zs::make_lds_plan(M, plan->shard_len, "zero_offload_init", &c->lds)) return rc;
   c->flags = flags;
   c->fp16 = (flags & ZS_FP16) != 0;
   c->shard_len = plan->shard_len;
@@ -275,7 +277,8 @@ int pipeline(zs_offload* c, const zs::HostConsts* k_host, bool out_f16, double* 
       const int64_t off = c->chunks[ci].first, len = c->chunks[ci].second;
       zs::GradPtrs g = *per_chunk;
       for (int j = 0; j < c->M; j++) g.p[j] += off;
-      e = zs::launch_sumsq(c->M, g, len, partials, stage + off, c->max_groups, c->stream);
+      e = zs::launch_sumsq(c->M, g, len, partials, stage + off, c->lds.stage_norm, c->max_groups,
+                           c->stream);
       if (e == hipSuccess) e = hipEventRecord(c->chunk_done[ci], c->stream);
     }
   } else {
@@ -373,7 +376,8 @@ extern "C" int zero_offload_step(zs_offload* c, const void* const* grads, float 
   double* partials = reinterpret_cast<double*>(c->ws + c->lay.partials_off);
   zs::ClipScalars* sc_dev = reinterpret_cast<zs::ClipScalars*>(c->ws + c->lay.scalars_off);
   // the device part: reduce, stage the averages, norm and clip scalars
-  hipError_t e = zs::launch_sumsq(c->M, g, S, partials, stage, c->max_groups, c->stream);
+  hipError_t e =
+      zs::launch_sumsq(c->M, g, S, partials, stage, c->lds.stage_norm, c->max_groups, c->stream);
   if (e == hipSuccess)
     e = zs::launch_finalize(partials + zs::level1_partials(S), zs::final_partials(S), nullptr,
                             max_grad_norm, max_grad_norm > 0.0f ? 1 : 0,
@@ -406,7 +410,8 @@ extern "C" int zero_offload_step_amp(zs_offload* c, const void* const* grads, fl
   // runs the finalize, so its scaler advances like every other rank's
   hipError_t e = hipSuccess;
   if (S > 0)
-    e = zs::launch_sumsq_f16(c->M, g, S, partials, st, stage, c->max_groups, c->stream);
+    e = zs::launch_sumsq_f16(c->M, g, S, partials, st, stage, c->lds.stage_norm, c->max_groups,
+                             c->stream);
   if (e == hipSuccess)
     e = zs::launch_amp_finalize(partials + zs::level1_partials(S),
                                 S ? zs::final_partials(S) : 0, nullptr, st, p,
@@ -437,8 +442,9 @@ int offload_sumsq(zs_offload* c, const void* const* grads, const zs_amp_state* s
   if (n_final)
     e = state_dev ? zs::launch_sumsq_f16(c->M, g, S, partials,
                                          reinterpret_cast<const zs::AmpState*>(state_dev),
-                                         stage, c->max_groups, c->stream)
-                  : zs::launch_sumsq(c->M, g, S, partials, stage, c->max_groups, c->stream);
+                                         stage, c->lds.stage_norm, c->max_groups, c->stream)
+                  : zs::launch_sumsq(c->M, g, S, partials, stage, c->lds.stage_norm,
+                                     c->max_groups, c->stream);
   if (e == hipSuccess)
     e = zs::launch_sumsq_total(partials + zs::level1_partials(S), n_final, sumsq_dev, c->stream);
   return e == hipSuccess ? ZS_OK : zs::ehip(who, e);
@@ -518,6 +524,19 @@ extern "C" int zero_offload_step_amp_global_norm(zs_offload* c, const void* cons
       c->stream);
   if (e != hipSuccess) return zs::ehip("zero_offload_step_amp_global_norm: finalize", e);
   return pipeline(c, nullptr, true, nullptr, who);
+}
+
+extern "C" int zero_offload_amp_state_init(zs_offload* c, zs_amp_state* state_dev,
+                                           float init_scale) {
+  if (!c) return zs::einval("zero_offload_amp_state_init: ctx is NULL");
+  if (!state_dev || !aligned(state_dev, 16))
+    return zs::einval(
+        "zero_offload_amp_state_init: state_dev must be a 16-byte-aligned device pointer");
+  if (!(init_scale > 0.0f) || isinf(init_scale))
+    return zs::einval("zero_offload_amp_state_init: init_scale must be finite and > 0");
+  const hipError_t e = zs::launch_amp_state_init(reinterpret_cast<zs::AmpState*>(state_dev),
+                                                 init_scale, c->stream);
+  return e == hipSuccess ? ZS_OK : zs::ehip("zero_offload_amp_state_init", e);
 }
 
 extern "C" int zero_offload_set_stream(zs_offload* c, void* stream) {

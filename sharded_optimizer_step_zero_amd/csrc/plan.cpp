@@ -69,6 +69,28 @@ void build_runs(zs_plan& p) {
   }
 }
 
+// The run table as the step kernels read it (the runs, at least one, then a
+// sentinel starting past the shard) and, with more than one run, the tile-flag
+// table: per 256-element tile, 2 bits -- the decay flag of a tile inside one
+// run, or 2 for a tile that straddles a run boundary.
+void build_step_tables(zs_plan& p) {
+  p.run_table = p.runs;
+  if (p.run_table.empty()) p.run_table.push_back({0, 0, 0});
+  p.run_table.push_back({p.shard_len, 0, 0});
+  const int64_t n_runs = (int64_t)p.run_table.size() - 1;
+  p.tile_flags.assign((size_t)zs::tile_flag_words(p.shard_len, n_runs), 0u);
+  if (p.tile_flags.empty()) return;
+  const int64_t tiles = (p.shard_len + zs::kStepTileElems - 1) / zs::kStepTileElems;
+  size_t r = 0;  // the run holding the tile's first element
+  for (int64_t t = 0; t < tiles; t++) {
+    const int64_t lo = t * zs::kStepTileElems;
+    const int64_t hi = std::min(p.shard_len, lo + zs::kStepTileElems);
+    while (p.run_table[r + 1].start <= lo) r++;
+    const uint32_t f = p.run_table[r + 1].start < hi ? 2u : (uint32_t)(p.run_table[r].flags & 1);
+    p.tile_flags[(size_t)(t >> 4)] |= f << ((t & 15) * 2);
+  }
+}
+
 }  // namespace
 
 extern "C" int zs_plan_create(const int64_t* numel, const uint8_t* decay, int64_t n_tensors,
@@ -172,8 +194,9 @@ extern "C" int zs_plan_create(const int64_t* numel, const uint8_t* decay, int64_
     }
     p->shard_len = shard;
 
-    // 5. weight-decay runs
+    // 5. weight-decay runs, and the step kernels' run and tile-flag tables
     build_runs(*p);
+    build_step_tables(*p);
 
     // 6. pieces for state export/import, with their offsets in the canonical
     //    order: the whole kPieceElems-element pieces of every tensor segment,

@@ -19,7 +19,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 37
+    assert len(names) == 38
     lib = ctypes.CDLL(zs.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -96,6 +96,26 @@ def test_init_and_step_argument_errors_before_any_device_call():
     assert zs.zero_shard_last_error()
 
 
+@pytest.mark.parametrize("value", ["1", "2", "65", "-4", "eight"])
+def test_bad_waves_override_refused_before_any_device_call(monkeypatch, value):
+    """A ZS_WAVES_PER_CU value other than 0 or 3..64 makes context creation fail
+    with ZS_EINVAL before the library touches the device."""
+    monkeypatch.setenv("ZS_WAVES_PER_CU", value)
+    p = zs.zs_plan_create([1000], [1], 1, 0)
+    ws = zs.zs_workspace_bytes(p, 4)
+    try:
+        with pytest.raises(zs.ZeroShardError) as e:
+            zs.zero_shard_init(p, 4, 16, 16, 16, 16, 256, ws)
+        assert e.value.code == zs.ZS_EINVAL and "ZS_WAVES_PER_CU" in str(e.value)
+        sb = zs.zs_offload_staging_bytes(1024)
+        wso = zs.zs_workspace_bytes(p, 4, zs.ZS_STAGE_AVERAGE)
+        with pytest.raises(zs.ZeroShardError) as e:
+            zs.zero_offload_init(p, 4, 16, 16, 16, 16, 256, wso, 256, sb, 1024, n_threads=1)
+        assert e.value.code == zs.ZS_EINVAL and "ZS_WAVES_PER_CU" in str(e.value)
+    finally:
+        zs.zs_plan_destroy(p)
+
+
 def test_empty_plan():
     p = zs.zs_plan_create([], [], 4, 3)
     try:
@@ -156,3 +176,28 @@ def test_slab_layout_argument_errors():
     total = ctypes.c_size_t(7)
     assert lib.zs_slab_layout(None, 4, 0, 0, out, ctypes.byref(total)) == zs.ZS_EINVAL
     assert total.value == 7
+
+
+def test_binding_checks_tensors_and_contribution_count():
+    """The binding rejects, before any library call, tensors the kernels would
+    stream past (wrong dtype, device, layout or length) and a gradient list whose
+    length differs from the context's M (the library reads exactly M pointers)."""
+    import torch
+    dev = torch.device("cpu")
+    ok = torch.zeros(1024, dtype=torch.bfloat16)
+    zs._check_tensors([ok, 1234], 1024, (torch.bfloat16,), dev, "grads")   # ints pass through
+    for bad, what in ((torch.zeros(1024, dtype=torch.float32), "dtype"),
+                      (torch.zeros(1000, dtype=torch.bfloat16), "elements"),
+                      (torch.zeros(2048, dtype=torch.bfloat16)[::2], "contiguous")):
+        with pytest.raises(ValueError, match=what):
+            zs._check_tensors([ok, bad], 1024, (torch.bfloat16,), dev, "grads")
+    with pytest.raises(ValueError, match="on cpu"):
+        zs._check_tensors([ok], 1024, (torch.bfloat16,), torch.device("cuda", 0), "grads")
+    fake = 0x1000
+    zs._CTX_M[fake] = 3
+    try:
+        with pytest.raises(ValueError, match="exactly 3"):
+            zs._grad_array(fake, [1, 2])
+        assert len(zs._grad_array(fake, [1, 2, 3])) == 3
+    finally:
+        zs._CTX_M.pop(fake)

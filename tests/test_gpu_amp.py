@@ -130,7 +130,7 @@ def test_amp_rejects_wrong_context():
     z = ZeroShard([1000], [1], 1, 0, 1)          # bf16 context
     z.amp_state = torch.zeros(2, dtype=torch.int64, device="cuda")
     with pytest.raises(zsm.ZeroShardError) as e:
-        z.step_amp([torch.zeros(1000, dtype=torch.int16, device="cuda")], **HP)
+        z.step_amp([torch.zeros(1024, dtype=torch.int16, device="cuda")], **HP)
     assert e.value.code == zsm.ZS_ESTATE
     gt = torch.zeros(1024, dtype=torch.int16, device="cuda")
     g = [gt.data_ptr()]
@@ -146,7 +146,7 @@ def test_amp_rejects_wrong_context():
     z.close()
     y = ZeroShard([1000], [1], 1, 0, 1, fp16=True)
     with pytest.raises(zsm.ZeroShardError) as e:
-        y.step([torch.zeros(1000, dtype=torch.int16, device="cuda")], step=1, **HP)
+        y.step([torch.zeros(1024, dtype=torch.int16, device="cuda")], step=1, **HP)
     assert e.value.code == zsm.ZS_ESTATE
     y.amp_init(1024.0)
     st = y.amp_state.data_ptr()
@@ -223,4 +223,41 @@ def test_amp_empty_shard_keeps_the_scaler_in_step():
                                             state_dev=z.amp_state.data_ptr(), growth_interval=2,
                                             global_sumsq_dev=d.data_ptr(), **HP)
         assert z.amp_read() == want
+    z.close()
+
+
+@pytest.mark.parametrize("start", [float(np.finfo(np.float32).max), 2.0 ** 127])
+def test_amp_scale_growth_stays_finite(start):
+    """Growth every step from next to the largest finite fp32 scale: a grown scale
+    that would be Inf is dropped and the growth count restarts, on the device as
+    in the oracle (torch's GradScaler).  Zero gradients keep the steps applied;
+    one contribution that overflowed fp16 (Inf) makes a step skip and back the
+    scale off."""
+    log(f"test_amp_scale_growth_stays_finite start={start}")
+    numel, decay = [5000, 64, 3], [1, 0, 1]
+    lay = L.plan(numel, decay, 1, 0, 25_000_000, 64)
+    z = ZeroShard(numel, decay, 1, 0, 2, fp16=True)
+    S = z.shard_len
+    master = synth.host_normal_f32(S, synth.key(78, 0), 0.02)
+    for o, n in lay.padding_ranges():
+        master[o:o + n] = 0
+    z.master[:S].copy_(torch.from_numpy(master))
+    z.amp_init(start)
+    sc = oracle.Scaler(scale=start, growth_interval=1)
+    p, m, v = master.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32)
+    pf = np.zeros(S, np.uint16)
+    mask = lay.decay_mask()
+    for s in range(7):
+        gs = [np.zeros(S, np.uint16) for _ in range(2)]
+        if s == 3:
+            gs[1][17] = 0x7C00        # an overflowed (Inf) fp16 contribution
+        z.step_amp([_u16(g) for g in gs], growth_interval=1, **HP)
+        fi, _ = oracle.amp_step(gs, p, m, v, pf, mask, sc, **HP)
+        assert fi == (s == 3)
+        got = _state(z)
+        for a, b in zip(got, (p, m, v, pf)):
+            assert _eq(a, b), s
+        scale, tracker, applied = z.amp_read()
+        assert np.isfinite(scale), s
+        assert (scale, tracker, applied) == (float(sc.scale[0]), int(sc.tracker[0]), sc.applied), s
     z.close()
