@@ -6,6 +6,12 @@ the GPU's pre-step state of the checked elements is fed to the oracle, and the
 oracle's result is compared with the GPU's post-step state, so earlier
 rounding differences do not accumulate into the per-step figure.  A separate
 free-running oracle trajectory gives the drift report.
+
+A clipped step is checked against the oracle's own clip coefficient (from the
+oracle's fp64 norm of the whole shard), never the one the device derived: the
+tolerance (1e-6 relative, 1 bf16 ulp) always applies, and bit-exactness is
+required on the steps where the coefficient the device's norm implies equals
+the oracle's.  The free-running trajectory uses the oracle's coefficient too.
 """
 from __future__ import annotations
 
@@ -59,6 +65,23 @@ def bf16_ulps(a: np.ndarray, b: np.ndarray) -> int:
     if (~bn).sum() == 0:
         return 0
     return int(np.abs(ordered(a[~bn]) - ordered(b[~bn])).max())
+
+
+def coef_ulps(a, b) -> int:
+    """Distance of two positive fp32 coefficients in ulps."""
+    return abs(int(np.float32(a).view(np.int32)) - int(np.float32(b).view(np.int32)))
+
+
+def bf16_ulp_hist(a: np.ndarray, b: np.ndarray) -> dict:
+    """{ulps: count} of the bf16 param against the oracle's (NaN pairs count as 0)."""
+    def ordered(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    d = np.abs(ordered(a) - ordered(b))
+    nan = ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+    d[nan] = 0
+    vals, counts = np.unique(np.minimum(d, 2), return_counts=True)
+    return {int(v): int(c) for v, c in zip(vals, counts)}
 
 
 def to_host(t) -> np.ndarray:
@@ -122,43 +145,72 @@ def full_parity(w: Workload, steps: int, flags=0, exact=True, contiguous=False):
     fr_m = np.zeros(S, np.float32)
     fr_v = np.zeros(S, np.float32)
     fr_b = np.zeros(S, np.uint16)
+    t_last = time.time()
     for s in range(steps):
+        if time.time() - t_last > 20:
+            log(f"  [{w.name}] step {s + 1}/{steps}")
+            t_last = time.time()
         pre = [to_host(x)[:S].copy() for x in (sh.zs.master, sh.zs.exp_avg, sh.zs.exp_avg_sq)]
         g = sh.case.host_grads(s)
-        coef = coef_gpu = None
+        coef = None
         if w.max_grad_norm > 0:
-            want_norm = float(np.sqrt(oracle.grad_sumsq(g)))
-            coef = oracle.coef_from_norm(want_norm, w.max_grad_norm)
+            # the oracle's own coefficient, from its own fp64 norm of the whole shard
+            sumsq = oracle.grad_sumsq(g)
+            want_norm = float(np.sqrt(sumsq))
+            coef = oracle.clip_coef(sumsq, w.max_grad_norm)
         norm = sh.step(s, want_norm=w.max_grad_norm > 0)
         torch.cuda.synchronize()
-        if coef is not None:
-            # the norm is checked against the oracle's below; the step is then checked
-            # with the coefficient the device derived from its own norm
-            coef_gpu = oracle.coef_from_norm(norm, w.max_grad_norm)
         p, m, v = pre
         b = np.zeros(S, np.uint16)
-        oracle.step_f32(g, p, m, v, b, mask, step=s + 1, coef=coef_gpu, **hp)
+        oracle.step_f32(g, p, m, v, b, mask, step=s + 1, coef=coef, **hp)
         got = [to_host(x)[:S] for x in (sh.zs.master, sh.zs.exp_avg, sh.zs.exp_avg_sq, sh.zs.param)]
-        st = dict(step=s + 1, rel_master=rel_err(got[0], p), rel_m=rel_err(got[1], m),
-                  rel_v=rel_err(got[2], v), bf16_ulps=bf16_ulps(got[3], b),
-                  exact=bool(np.array_equal(got[0].view(np.uint32), p.view(np.uint32))
-                             and np.array_equal(got[1].view(np.uint32), m.view(np.uint32))
-                             and np.array_equal(got[2].view(np.uint32), v.view(np.uint32))
-                             and np.array_equal(got[3], b)))
+        st = _step_stats(s, got, (p, m, v, b))
+        same_coef = True
         if coef is not None:
             st["norm_rel"] = abs(norm - want_norm) / max(want_norm, 1e-300)
-            st["coef_ulps"] = abs(int(np.float32(coef_gpu).view(np.int32))
-                                  - int(np.float32(coef).view(np.int32)))
+            st["coef_ulps"] = coef_ulps(oracle.coef_from_norm(norm, w.max_grad_norm), coef)
+            same_coef = st["coef_ulps"] == 0
             assert st["norm_rel"] <= 1e-12 and st["coef_ulps"] <= 1, st
         oracle.step_f32(g, fr_p, fr_m, fr_v, fr_b, mask, step=s + 1, coef=coef, **hp)
         st["drift_master"] = rel_err(got[0], fr_p)
+        st["drift_m"] = rel_err(got[1], fr_m)
+        st["drift_v"] = rel_err(got[2], fr_v)
+        st["drift_bf16_ulps"] = bf16_ulps(got[3], fr_b)
         stats.append(st)
-        assert st["rel_master"] <= TOL_REL and st["rel_m"] <= TOL_REL and st["rel_v"] <= TOL_REL, st
-        assert st["bf16_ulps"] <= 1, st
-        if exact:
-            assert st["exact"], st
+        _assert_step(st, exact and same_coef)
     sh.close()
     return stats
+
+
+def _step_stats(s, got, want) -> dict:
+    """Per-step figures of the device state `got` against the oracle's `want`
+    (master, m, v, bf16 param)."""
+    p, m, v, b = want
+    return dict(step=s + 1, n=int(p.size), rel_master=rel_err(got[0], p),
+                rel_m=rel_err(got[1], m), rel_v=rel_err(got[2], v),
+                bf16_ulps=bf16_ulps(got[3], b), bf16_hist=bf16_ulp_hist(got[3], b),
+                exact=bool(np.array_equal(got[0].view(np.uint32), p.view(np.uint32))
+                           and np.array_equal(got[1].view(np.uint32), m.view(np.uint32))
+                           and np.array_equal(got[2].view(np.uint32), v.view(np.uint32))
+                           and np.array_equal(got[3], b)))
+
+
+def assert_within_tolerance(step, got, want):
+    """The stated bar on a free-running comparison: master, m, v (got[0:3]) within
+    1e-6 relative of the oracle's, the bf16 param (got[3]) within 1 ulp."""
+    for k in range(3):
+        e = rel_err(got[k], want[k])
+        assert e <= TOL_REL, (step, k, e)
+    u = bf16_ulps(got[3], want[3])
+    assert u <= 1, (step, u)
+
+
+def _assert_step(st, exact):
+    """The stated bar always; bit-exactness where asked for."""
+    assert st["rel_master"] <= TOL_REL and st["rel_m"] <= TOL_REL and st["rel_v"] <= TOL_REL, st
+    assert st["bf16_ulps"] <= 1, st
+    if exact:
+        assert st["exact"], st
 
 
 class Gather:
@@ -240,38 +292,35 @@ def sampled_parity(w: Workload, steps: int, idx=None, check_steps=None, exact=Tr
             cached_g[gs_key] = sh.case.host_grads(s, idx)
         g = cached_g[gs_key]
         coef = None
-        coef_gpu = None
+        same_coef = True
         if w.max_grad_norm > 0:
+            # the oracle's own coefficient, from its fp64 norm of the whole shard
             gs = w.grad_step_index(s)
             if gs not in cached_coef:
                 sumsq = full_norm(s)
                 cached_coef[gs] = (oracle.clip_coef(sumsq, w.max_grad_norm), float(np.sqrt(sumsq)))
             coef, want_norm = cached_coef[gs]
-            coef_gpu = oracle.coef_from_norm(norm, w.max_grad_norm)
+            ulps = coef_ulps(oracle.coef_from_norm(norm, w.max_grad_norm), coef)
+            same_coef = ulps == 0
             assert abs(norm - want_norm) <= 1e-12 * want_norm, (norm, want_norm)
-            assert abs(int(coef_gpu.view(np.int32)) - int(np.float32(coef).view(np.int32))) <= 1
-        oracle.step_f32(g, fr_p, fr_m, fr_v, fr_b, dec, step=s + 1, coef=coef_gpu, **hp)
+            assert ulps <= 1, (s, ulps)
+        oracle.step_f32(g, fr_p, fr_m, fr_v, fr_b, dec, step=s + 1, coef=coef, **hp)
         if not check:
             continue
         torch.cuda.synchronize()
         p, m, v = pre
         b = np.zeros(idx.size, np.uint16)
-        oracle.step_f32(g, p, m, v, b, dec, step=s + 1, coef=coef_gpu, **hp)
+        oracle.step_f32(g, p, m, v, b, dec, step=s + 1, coef=coef, **hp)
         got = [gat(x) for x in (sh.zs.master, sh.zs.exp_avg, sh.zs.exp_avg_sq, sh.zs.param)]
-        st = dict(step=s + 1, n=int(idx.size), rel_master=rel_err(got[0], p),
-                  rel_m=rel_err(got[1], m), rel_v=rel_err(got[2], v),
-                  bf16_ulps=bf16_ulps(got[3], b), drift_master=rel_err(got[0], fr_p),
-                  exact=bool(np.array_equal(got[0].view(np.uint32), p.view(np.uint32))
-                             and np.array_equal(got[1].view(np.uint32), m.view(np.uint32))
-                             and np.array_equal(got[2].view(np.uint32), v.view(np.uint32))
-                             and np.array_equal(got[3], b)))
+        st = _step_stats(s, got, (p, m, v, b))
+        st["drift_master"] = rel_err(got[0], fr_p)
+        st["drift_m"] = rel_err(got[1], fr_m)
+        st["drift_v"] = rel_err(got[2], fr_v)
+        st["drift_bf16_ulps"] = bf16_ulps(got[3], fr_b)
         if coef is not None:
             st["norm_rel"] = abs(norm - want_norm) / want_norm
-            st["coef_ulps"] = abs(int(coef_gpu.view(np.int32)) - int(np.float32(coef).view(np.int32)))
+            st["coef_ulps"] = ulps
         st_all.append(st)
-        assert st["rel_master"] <= TOL_REL and st["rel_m"] <= TOL_REL and st["rel_v"] <= TOL_REL, st
-        assert st["bf16_ulps"] <= 1, st
-        if exact:
-            assert st["exact"], st
+        _assert_step(st, exact and same_coef)
     sh.close()
     return st_all

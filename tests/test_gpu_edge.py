@@ -68,7 +68,8 @@ def test_nonfinite_gradient(skip, bad, clip):
             assert np.array_equal(_bits(a), _bits(b))   # left untouched
     else:
         g = [to_host(x)[:S].copy() for x in grads]
-        coef = oracle.coef_from_norm(norm, clip) if clip > 0 else None
+        # the oracle's own coefficient (NaN or 0 here, as the device's)
+        coef = oracle.clip_coef(oracle.grad_sumsq(g), clip) if clip > 0 else None
         p, m, v, _ = [x.copy() for x in pre]
         b = np.zeros(S, np.uint16)
         oracle.step_f32(g, p, m, v, b, sh.lay.decay_mask(), step=2, coef=coef, **sh.hp())

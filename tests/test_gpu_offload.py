@@ -15,7 +15,7 @@ from sharded_optimizer_step_zero_amd import ZeroOffload, ZeroShard
 from synth.device_case import DeviceCase
 from synth.workloads import scaled, workload
 
-from _gpu import log, to_host
+from _gpu import assert_within_tolerance, coef_ulps, log, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -52,17 +52,27 @@ def _run_vs_oracle(w, steps, chunk, n_threads=0):
     p, m, v, b = o.case.host_master(), np.zeros(S, np.float32), np.zeros(S, np.float32), \
         np.zeros(S, np.uint16)
     mask = o.lay.decay_mask()
+    same = True      # the device's coefficient has equalled the oracle's on every step so far
     for s in range(steps):
         grads = o.case.fill_grads(s)
         norm = o.z.step(grads, step=s + 1, max_grad_norm=w.max_grad_norm, want_norm=True,
                         **o.hp())
         g = o.case.host_grads(s)
-        want = float(np.sqrt(oracle.grad_sumsq(g)))
+        sumsq = oracle.grad_sumsq(g)
+        want = float(np.sqrt(sumsq))
         assert abs(norm - want) <= 1e-12 * max(want, 1e-300)
-        coef = oracle.coef_from_norm(norm, w.max_grad_norm) if w.max_grad_norm > 0 else None
+        coef = None
+        if w.max_grad_norm > 0:
+            coef = oracle.clip_coef(sumsq, w.max_grad_norm)    # the oracle's own
+            ulps = coef_ulps(oracle.coef_from_norm(norm, w.max_grad_norm), coef)
+            assert ulps <= 1
+            same = same and ulps == 0
         oracle.step_f32(g, p, m, v, b, mask, step=s + 1, coef=coef, **o.hp())
-        for x, y in zip(o.state(), (p, m, v, b)):
-            assert np.array_equal(_bits(x), _bits(y)), s
+        got = o.state()
+        assert_within_tolerance(s, got, (p, m, v, b))
+        if same:
+            for x, y in zip(got, (p, m, v, b)):
+                assert np.array_equal(_bits(x), _bits(y)), s
     o.z.close()
 
 

@@ -9,6 +9,9 @@ with ragged tails; the 6.7B, 70B-shard and stress workloads run at full size
 and are checked on sampled elements (seeded windows, the first/last 64
 elements of every segment, every padding element).
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -23,17 +26,48 @@ pytestmark = pytest.mark.gpu
 
 
 def _report(name, stats):
-    worst = max(max(s["rel_master"], s["rel_m"], s["rel_v"]) for s in stats)
+    """Logs the parity summary of a run; with ZS_PARITY_REPORT set to a directory it
+    also writes it there as <name>.json (per-field worst per-step error, the bf16
+    ulp histogram over every checked element and step, and the drift of the
+    free-running oracle trajectory at steps 1, 10, 100, 1000 and the last)."""
+    worst = {k: max(s[k] for s in stats) for k in ("rel_master", "rel_m", "rel_v")}
     exact = sum(s["exact"] for s in stats)
-    drift = {s["step"]: s.get("drift_master") for s in stats if s["step"] in (1, 10, 100, 1000)}
-    log(f"  [{name}] steps checked {len(stats)}, exact {exact}, worst rel {worst:.2e}, "
-        f"max bf16 ulps {max(s['bf16_ulps'] for s in stats)}, drift {drift}")
+    hist = {}
+    for s in stats:
+        for k, c in s["bf16_hist"].items():
+            hist[k] = hist.get(k, 0) + c
+    last = stats[-1]["step"]
+    drift = {s["step"]: {k: s[k] for k in ("drift_master", "drift_m", "drift_v",
+                                           "drift_bf16_ulps")}
+             for s in stats if s["step"] in (1, 10, 100, 1000, last)}
+    coef = [s["coef_ulps"] for s in stats if "coef_ulps" in s]
+    log(f"  [{name}] steps checked {len(stats)}, exact {exact}, worst rel {worst}, "
+        f"bf16 ulp histogram {hist}, coef ulps {sorted(set(coef))}, drift {drift}")
+    out = os.environ.get("ZS_PARITY_REPORT")
+    if out:
+        os.makedirs(out, exist_ok=True)
+        rec = dict(name=name, steps_checked=len(stats), elements=stats[0]["n"],
+                   exact_steps=exact, worst=worst, bf16_ulp_hist=hist,
+                   coef_ulps=sorted(set(coef)),
+                   norm_rel_max=max((s["norm_rel"] for s in stats if "norm_rel" in s),
+                                    default=None),
+                   drift=drift)
+        with open(os.path.join(out, f"{name}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
 
 
 def test_tiny_flat_full():
     w = workload(1)
     log(f"test_tiny_flat_full: S={w.total_params} M={w.M} steps={w.steps}")
     _report(w.name, full_parity(w, w.steps))
+
+
+def test_tiny_flat_drift_1000_steps():
+    """The tiny workload run for 1000 steps, every element checked every step, and
+    the drift of the device trajectory against a free-running oracle reported."""
+    w = workload(1)
+    log(f"test_tiny_flat_drift_1000_steps: S={w.total_params} M={w.M} steps=1000")
+    _report(w.name + "-1000steps", full_parity(w, 1000))
 
 
 SMALL = [
