@@ -14,11 +14,13 @@ using the algorithmic bytes 2M+12 read + 14 written per parameter;
     python bench.py [--steps K] [--warmup W] [--workload 1..5] [--no-cpu-baseline]
                     [--checkpoint] [--amp] [--offload] [--cold] [--no-extras]
 
-On the default workload the line also carries the checkpoint export/import, the
-loss-scaled fp16 step (fused and staged) and the offloaded step on host cores
-("checkpoint", "amp_fp16", "amp_fp16_staged", "offload", "offload_fp16") and the
-timed steps replayed from one HIP graph ("graph"), each timed after the headline
-step; --no-extras leaves them out.
+The default workload is the largest one a single GPU holds: the unsharded
+Llama-shaped 6.7B parameter list (M = 1, 108 GB of state resident).  With
+--workload 2 (the GPT-1.3B 1/8 shard) the line also carries the checkpoint
+export/import, the loss-scaled fp16 step (fused and staged) and the offloaded
+step on host cores ("checkpoint", "amp_fp16", "amp_fp16_staged", "offload",
+"offload_fp16") and the timed steps replayed from one HIP graph ("graph"), each
+timed after the headline step; --no-extras leaves them out.
 """
 from __future__ import annotations
 
@@ -369,13 +371,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2,
-                    help="1 tiny, 2 GPT-1.3B 1/8 shard (default), 3 Llama-6.7B, "
-                         "4 Llama-70B 1/16 shard, 5 stress with clip")
+    ap.add_argument("--workload", type=int, default=3,
+                    help="1 tiny, 2 GPT-1.3B 1/8 shard, 3 Llama-6.7B unsharded (default: the "
+                         "largest workload one GPU holds), 4 Llama-70B 1/16 shard, 5 stress "
+                         "with clip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the headline step: skip the checkpoint, loss-scaled and "
-                         "offload legs that the default run adds on the GPT shard")
+                         "offload legs that a run on the GPT shard (--workload 2) adds")
     ap.add_argument("--checkpoint", action="store_true",
                     help="also time the state export/import used for checkpoints and resharding")
     ap.add_argument("--amp", action="store_true",
@@ -534,7 +537,7 @@ def main():
     if args.graph or w.name.startswith("tiny") or (not args.no_extras and args.workload == 2):
         out["graph"] = time_graph(zs, grads, w, hp, args.steps,
                                   args.warmup + args.steps + n_spread + 1)
-    # the default run on the GPT shard adds the follow-on paths' legs
+    # a run on the GPT shard adds the follow-on paths' legs
     extras = not args.no_extras and args.workload == 2
     if args.checkpoint or extras:
         out["checkpoint"] = time_checkpoint(zs, w, stream)
