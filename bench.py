@@ -393,6 +393,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the steps replayed from one HIP graph (default for the tiny "
                          "workload, which is launch-bound)")
+    ap.add_argument("--contiguous", action="store_true",
+                    help="take the shard's slab from physically contiguous device memory "
+                         "(ZeroShard(contiguous=True))")
     ap.add_argument("--cpu-slab", type=int, default=1 << 25)
     ap.add_argument("--calibrate-copy-gib", type=float, default=1.0,
                     help="size of the plain copy run once before timing (counter calibration)")
@@ -416,7 +419,8 @@ def main():
     w = workload(args.workload)
     t_setup = time.time()
     zs = ZeroShard(w.numel, w.decay, w.world_size, w.rank, w.M, device=dev,
-                   bucket_cap=w.bucket_cap, align=w.align, grad_buffers=True)
+                   bucket_cap=w.bucket_cap, align=w.align, grad_buffers=True,
+                   contiguous=args.contiguous)
     segs = zs.segments()
     pad = [(o, n) for o, n, t, _, _ in segs if t < 0]
     special = special_ranges(w, [(o, n, t) for o, n, t, _, _ in segs])
@@ -506,6 +510,7 @@ def main():
         "config": {
             "workload": w.name,
             "description": w.description,
+            "slab": "physically contiguous" if args.contiguous else "ordinary device memory",
             "shard_params": S,
             "M": w.M,
             "world_size": w.world_size,
