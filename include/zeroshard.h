@@ -455,6 +455,38 @@ int zero_offload_set_stream(zs_offload *ctx, void *stream);
 /* Waits for the context's copies, stops its threads and frees it. */
 void zero_offload_destroy(zs_offload *ctx);
 
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: one bf16
+ * step of zero_shard_step's arithmetic (same kernels, same bits) on one rank's
+ * buffers, with no context and no caller workspace.  The plan's run and
+ * tile-flag tables, and for a clipped step the norm partials and the clip
+ * scalars, go to a static device scratch of ZS_STATIC_SCRATCH_BYTES that
+ * every GPU the library runs on holds until the process ends; the call
+ * allocates nothing.  The scratch takes 16 B per decay run, 1 B per 1,024
+ * elements when there is more than one run and, clipped, 1 B per 256 elements
+ * of norm partials: a call that needs more (a clipped step beyond about 1.7G
+ * elements, 2.1G with one run; an unclipped one beyond about 8.5G elements
+ * with several runs) is refused with ZS_EINVAL and a message; use
+ * zero_shard_init with a workspace then.
+ *   plan        the layout (host); it must outlive the call's table upload,
+ *               which copies from it on `stream`
+ *   M, buffers  as zero_shard_init / zero_shard_step (device pointers, 16-byte
+ *               aligned, shard_len elements each); grads[0..M) bf16
+ *   step, hyper-parameters, max_grad_norm: as zero_shard_step (no norm out)
+ * Enqueues on `stream` and returns.  Every call on a GPU shares that GPU's
+ * scratch (each call re-uploads its tables and writes every partial it reads,
+ * so nothing needs clearing): calls that overlap on one GPU -- other threads,
+ * other streams -- race and must be ordered by the caller; calls on one stream
+ * are ordered already.  Errors: ZS_EINVAL (found before any device call),
+ * ZS_EHIP.
+ */
+#define ZS_STATIC_SCRATCH_BYTES (8u << 20)
+int zero_shard_step_static(const zs_plan *plan, int32_t M, void *param_bf16, float *master,
+                           float *exp_avg, float *exp_avg_sq, const void *const *grads,
+                           float lr, float beta1, float beta2, float eps, float weight_decay,
+                           int64_t step, float max_grad_norm, void *stream);
+
 /* The bf16 parameter shard and its length: after a step it holds the rank's
  * updated parameters, the buffer ZeRO-1's all-gather sends so that every rank
  * again holds the whole model (Lecture04 notes, "ZeRO-1"; CS336 第七讲

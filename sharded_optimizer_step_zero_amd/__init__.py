@@ -29,6 +29,7 @@ ZS_SKIP_NONFINITE = 1
 ZS_FP16 = 2
 ZS_STAGE_AVERAGE = 4
 ZS_MAX_M = 16
+ZS_STATIC_SCRATCH_BYTES = 8 << 20
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
@@ -85,6 +86,8 @@ _sig("zero_shard_import_state", ctypes.c_int, _vp, _vp, _vp, _vp)
 _sig("zero_shard_params", ctypes.c_int, _vp, _P(_vp), _P(_i64))
 _sig("zero_shard_set_stream", ctypes.c_int, _vp, _vp)
 _sig("zero_shard_destroy", None, _vp)
+_sig("zero_shard_step_static", ctypes.c_int, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _f32, _f32, _f32,
+     _f32, _f32, _i64, _f32, _vp)
 _sig("zero_shard_last_error", ctypes.c_char_p)
 _sig("zs_host_adamw", ctypes.c_int, _vp, _i64, _i64, _vp, _f32, _vp, _vp, _vp, _vp, _f32, _f32,
      _f32, _f32, _f32, _i64, _i32, _u32)
@@ -114,8 +117,9 @@ EXPORTED = ["zs_plan_create", "zs_plan_query", "zs_plan_tensor_slice", "zs_plan_
             "zero_shard_step_amp", "zero_shard_grad_sumsq_amp", "zero_shard_step_amp_global_norm",
             "zero_shard_export_state", "zero_shard_import_state", "zero_shard_params",
             "zero_shard_set_stream", "zero_shard_destroy", "zero_shard_last_error",
-            "zs_host_adamw", "zs_offload_staging_bytes", "zero_offload_init", "zero_offload_step",
-            "zero_offload_step_amp", "zero_offload_grad_sumsq", "zero_offload_step_global_norm",
+            "zero_shard_step_static", "zs_host_adamw", "zs_offload_staging_bytes",
+            "zero_offload_init", "zero_offload_step", "zero_offload_step_amp",
+            "zero_offload_grad_sumsq", "zero_offload_step_global_norm",
             "zero_offload_grad_sumsq_amp", "zero_offload_step_amp_global_norm",
             "zero_offload_amp_state_init", "zero_offload_set_stream", "zero_offload_destroy",
             "zs_device_alloc_contiguous", "zs_device_free"]
@@ -336,6 +340,20 @@ def zero_shard_set_stream(ctx: int, stream: int) -> None:
 def zero_shard_destroy(ctx: int) -> None:
     _CTX_M.pop(ctx, None)
     _lib.zero_shard_destroy(ctx)
+
+
+def zero_shard_step_static(plan: int, M: int, param_bf16: int, master: int, exp_avg: int,
+                           exp_avg_sq: int, grads: Sequence[int], lr: float, beta1: float,
+                           beta2: float, eps: float, weight_decay: float, step: int,
+                           max_grad_norm: float = 0.0, stream: int = 0) -> None:
+    """Enqueues one bf16 step without a context or workspace: the library's static
+    device scratch holds the tables and partials (see zeroshard.h).  Pointers are
+    device addresses."""
+    if len(grads) != M:
+        raise ValueError(f"expected {M} gradient contributions, got {len(grads)}")
+    _check(_lib.zero_shard_step_static(plan, M, param_bf16, master, exp_avg, exp_avg_sq,
+                                       _ptr_array(grads), lr, beta1, beta2, eps, weight_decay,
+                                       step, max_grad_norm, stream or None))
 
 
 # ------------------------------------------------- the step on host cores

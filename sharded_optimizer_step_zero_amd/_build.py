@@ -8,7 +8,8 @@ import tempfile
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(_HERE, "libzeroshard.so")
 SOURCES = [os.path.join(_HERE, "csrc", f)
-           for f in ("kernels.hip", "plan.cpp", "abi.cpp", "offload.cpp", "alloc.cpp")]
+           for f in ("kernels.hip", "plan.cpp", "abi.cpp", "offload.cpp", "alloc.cpp",
+                     "static_step.hip")]
 # host-compiled part: the offloaded update (vector clones picked at load time)
 HOST_SOURCES = [os.path.join(_HERE, "csrc", "host_step.cpp")]
 GXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-math-errno", "-pthread",

@@ -19,7 +19,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 38
+    assert len(names) == 39
     lib = ctypes.CDLL(zs.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -201,3 +201,31 @@ def test_binding_checks_tensors_and_contribution_count():
         assert len(zs._grad_array(fake, [1, 2, 3])) == 3
     finally:
         zs._CTX_M.pop(fake)
+
+
+def test_static_step_refuses_what_its_scratch_cannot_hold():
+    """zero_shard_step_static refuses, before any device call, a shard whose tables
+    and partials need more than the static scratch: a clipped step over 2^31
+    elements (8.4 MB of norm partials), and a layout with 2^20 alternating decay
+    runs (16 MB of run table) even unclipped."""
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+    p = zs.zs_plan_create([1 << 31], [1], 1, 0)
+    try:
+        with pytest.raises(zs.ZeroShardError) as e:
+            zs.zero_shard_step_static(p, 2, 256, 256, 256, 256, [256, 256], max_grad_norm=1.0,
+                                      **hp)
+        assert e.value.code == zs.ZS_EINVAL and "scratch" in str(e.value)
+    finally:
+        zs.zs_plan_destroy(p)
+    n = 1 << 20
+    p = zs.zs_plan_create([8] * n, [1, 0] * (n // 2), 1, 0, align=8)
+    try:
+        assert zs.zs_plan_query(p)["n_runs"] == n
+        with pytest.raises(zs.ZeroShardError) as e:
+            zs.zero_shard_step_static(p, 1, 256, 256, 256, 256, [256], **hp)
+        assert e.value.code == zs.ZS_EINVAL and "scratch" in str(e.value)
+        with pytest.raises(zs.ZeroShardError) as e:                 # argument errors first
+            zs.zero_shard_step_static(p, 1, 256, 256, 256, 8, [256], **hp)
+        assert e.value.code == zs.ZS_EINVAL and "aligned" in str(e.value)
+    finally:
+        zs.zs_plan_destroy(p)
