@@ -184,6 +184,53 @@ def percentiles(xs) -> dict:
             "p90": float(np.percentile(a, 90))}
 
 
+def sweep_caps(zs, grads, w, hp, stream, caps, rounds: int, steps: int) -> dict:
+    """The step kernel's wave cap swept on the same buffers: one context per cap
+    (ZS_WAVES_PER_CU set while it is created; 0 = no cap), all bound to this shard's
+    arrays, timed in alternating rounds so that placement does not mix into the
+    comparison.  Returns GB/s per cap and round at the algorithmic bytes."""
+    import torch
+
+    import sharded_optimizer_step_zero_amd as zsm
+    ctxs, keep = {}, []
+    old = os.environ.get("ZS_WAVES_PER_CU")
+    try:
+        for c in caps:
+            os.environ["ZS_WAVES_PER_CU"] = str(c)
+            ws = torch.zeros(zs.ws_bytes + 256, dtype=torch.uint8, device=zs.device)
+            keep.append(ws)
+            ctxs[c] = zsm.zero_shard_init(zs.plan, w.M, zs.param.data_ptr(), zs.master.data_ptr(),
+                                          zs.exp_avg.data_ptr(), zs.exp_avg_sq.data_ptr(),
+                                          ws.data_ptr() + (-ws.data_ptr()) % 256, zs.ws_bytes,
+                                          stream.cuda_stream, 0)
+    finally:
+        if old is None:
+            os.environ.pop("ZS_WAVES_PER_CU", None)
+        else:
+            os.environ["ZS_WAVES_PER_CU"] = old
+    ptrs = [g if isinstance(g, int) else g.data_ptr() for g in grads]
+    by = zs.shard_len * (2 * w.M + 26)
+    out = {c: [] for c in caps}
+    try:
+        for c in caps:                            # one untimed step per context
+            zsm.zero_shard_step(ctxs[c], ptrs, step=1, max_grad_norm=0.0, **hp)
+        for _ in range(rounds):
+            for c in caps:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for s in range(steps):
+                    zsm.zero_shard_step(ctxs[c], ptrs, step=2 + s, max_grad_norm=0.0, **hp)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                out[c].append(by / (e0.elapsed_time(e1) / steps * 1e-3) / 1e9)
+    finally:
+        for ctx in ctxs.values():
+            zsm.zero_shard_destroy(ctx)
+    return {"gbs_per_round": {str(c): v for c, v in out.items()}, "rounds": rounds,
+            "steps_per_round": steps, "note": "same buffers, one context per cap, no clip"}
+
+
 def time_cold(zs, grads, w, hp, stream, step0: int, reps: int) -> dict:
     """Per-step time with the 256 MB Infinity Cache evicted before each step (a
     1 GiB buffer is overwritten between steps, outside the timed events)."""
@@ -396,6 +443,10 @@ def main():
     ap.add_argument("--contiguous", action="store_true",
                     help="take the shard's slab from physically contiguous device memory "
                          "(ZeroShard(contiguous=True))")
+    ap.add_argument("--sweep-caps", default="",
+                    help="comma-separated step-kernel wave caps (0 = no cap) to time on the "
+                         "same buffers after the headline (adds a 'cap_sweep' object)")
+    ap.add_argument("--sweep-rounds", type=int, default=3)
     ap.add_argument("--cpu-slab", type=int, default=1 << 25)
     ap.add_argument("--calibrate-copy-gib", type=float, default=1.0,
                     help="size of the plain copy run once before timing (counter calibration)")
@@ -426,7 +477,9 @@ def main():
     special = special_ranges(w, [(o, n, t) for o, n, t, _, _ in segs])
     case = DeviceCase(w, zs.shard_len, pad, dev, special, grads=zs.grads)
     case.fill_master(zs.master)
-    grads = case.fill_grads(0)
+    # checked once, then passed as plain device addresses: the timed loop measures the
+    # library call, not the binding's per-call tensor checks
+    grads = zs.grad_pointers(case.fill_grads(0))
     stream = torch.cuda.current_stream(dev)
     zs.set_stream(stream.cuda_stream)
 
@@ -539,6 +592,10 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.sweep_caps:
+        out["cap_sweep"] = sweep_caps(zs, grads, w, hp, stream,
+                                      [int(c) for c in args.sweep_caps.split(",")],
+                                      args.sweep_rounds, max(args.steps // 2, 3))
     if args.graph or w.name.startswith("tiny") or (not args.no_extras and args.workload == 2):
         out["graph"] = time_graph(zs, grads, w, hp, args.steps,
                                   args.warmup + args.steps + n_spread + 1)

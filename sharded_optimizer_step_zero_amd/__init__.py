@@ -582,6 +582,12 @@ class ZeroShard:
                        "grads")
         return [g if isinstance(g, int) else g.data_ptr() for g in grads]
 
+    def grad_pointers(self, grads):
+        """The contributions' device addresses after the same checks a step makes; a
+        loop that steps many times on the same buffers can pass these plain ints and
+        skip the per-call Python checks (as a C caller does)."""
+        return self._grad_ptrs(grads)
+
     def _canon_ptrs(self, ts):
         import torch
         _check_tensors(ts, self.total_params, (torch.float32,), self.device, "canonical state")
