@@ -36,9 +36,9 @@ constexpr int32_t kMaxWavesPerCu = 64;
 // Llama and stress layouts.  Fewer contributions leave each wave less in
 // flight, so more waves pay off; from M = 10 on, 7 waves are best everywhere (6
 // and 5 lose 3-20%).  Re-measured on the Llama-70B 1/16 shard (M = 8, above
-// 2^31), caps 5-12 on the same buffers: 7, 8 and 9 equal on an ordinary slab
-// (6.34 TB/s), 8 and 9 ahead of 7 on a physically contiguous one (6.44 against
-// 6.39), so that entry is 8.
+// 2^31), caps 5-12 on the same buffers in four allocations on two boxes: 8 and
+// 9 tied 7 or led it by up to 1.3% in three, trailed by 0.6% in one, so that
+// entry is 8.
 //                                                 M: 0   1   2   3   4   5  6  7  8  9 10 11 12 13 14 15 16
 constexpr int8_t kStepWavesSmall[kCapMaxM + 1] = {0, 12, 11, 11, 10, 10, 9, 9, 9, 9, 7, 7, 7, 7, 7, 7, 7};
 constexpr int8_t kStepWavesLarge[kCapMaxM + 1] = {0, 11, 11, 10, 9, 9, 8, 8, 8, 8, 7, 7, 7, 7, 7, 7, 7};
