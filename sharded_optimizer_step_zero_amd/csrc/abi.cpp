@@ -171,13 +171,14 @@ int make_lds_plan(int32_t M, int64_t shard_len, const char* who, LdsPlan* out) {
   if ((e = reserved_kernels_static_lds(M, &static_lds)) != hipSuccess)
     return ehip((w + ": kernel attributes").c_str(), e);
   const LdsPlan p = lds_plan(M, shard_len, n_cu > 0 ? n_cu : 256, lds_cu, override_waves);
-  if (!lds_plan_fits(p, static_lds, per_wg > 0 ? (size_t)per_wg : 0, lds_cu))
+  const size_t wg_limit = per_wg > 0 ? (size_t)per_wg : kLdsPerWorkgroupFallback;
+  if (!lds_plan_fits(p, static_lds, wg_limit, lds_cu))
     return einval((w + ": an LDS reservation (step " + std::to_string(p.step) + ", staged step " +
                    std::to_string(p.step_staged) + ", staged norm " +
                    std::to_string(p.stage_norm) + ", copy " + std::to_string(p.copy) +
                    " bytes, plus " + std::to_string(static_lds) +
                    " static) exceeds the device's per-workgroup LDS limit of " +
-                   std::to_string(per_wg) + " bytes")
+                   std::to_string(wg_limit) + " bytes")
                       .c_str());
   *out = p;
   return ZS_OK;

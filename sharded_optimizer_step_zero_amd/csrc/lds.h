@@ -21,6 +21,9 @@ namespace zs {
 
 // LDS per CU on gfx950 (used when the device query fails).
 constexpr size_t kLdsPerCuDefault = 160 * 1024;
+// Per-workgroup LDS limit assumed when the device reports none: the smallest
+// among CDNA parts (MI355X reports 160 KiB).
+constexpr size_t kLdsPerWorkgroupFallback = 64 * 1024;
 constexpr int kCapMaxM = 16;
 // The smallest cap that can be asked for: below 3 resident waves per CU the
 // reservation would exceed what one workgroup may hold on CDNA parts with a

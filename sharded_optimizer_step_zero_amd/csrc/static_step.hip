@@ -56,7 +56,8 @@ int device_setup(DeviceSetup* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return zs::ehip(who, e);
-  if (dev < 0 || dev >= kMaxDevices) return zs::einval("zero_shard_step_static: device index beyond 63");
+  if (dev < 0 || dev >= kMaxDevices)
+    return zs::einval("zero_shard_step_static: device index beyond 63");
   std::lock_guard<std::mutex> lock(g_setup_mu);
   DeviceSetup& d = g_setup[dev];
   if (!d.ready) {
@@ -74,7 +75,7 @@ int device_setup(DeviceSetup* out) {
     if (e != hipSuccess) return zs::ehip("zero_shard_step_static: device query", e);
     n.n_cu = cu > 0 ? cu : 256;
     n.lds_cu = per_cu > 0 ? (size_t)per_cu : zs::kLdsPerCuDefault;
-    n.per_wg = per_wg > 0 ? (size_t)per_wg : 0;
+    n.per_wg = per_wg > 0 ? (size_t)per_wg : zs::kLdsPerWorkgroupFallback;
     for (int M = 1; M <= ZS_MAX_M; M++) {
       size_t s = 0;
       if ((e = zs::reserved_kernels_static_lds(M, &s)) != hipSuccess)
@@ -147,14 +148,14 @@ extern "C" int zero_shard_step_static(const zs_plan* plan, int32_t M, void* para
                    std::to_string(kScratchBytes) +
                    " the static scratch holds; use zero_shard_init with a workspace")
                       .c_str());
+  int32_t override_waves;
+  if (!zs::parse_waves_override(getenv("ZS_WAVES_PER_CU"), &override_waves))
+    return einval("zero_shard_step_static: ZS_WAVES_PER_CU must be 0 (no cap) or 3..64");
   const int64_t S = plan->shard_len;
   if (S == 0) return ZS_OK;
 
   DeviceSetup d;
   if (int rc = device_setup(&d)) return rc;
-  int32_t override_waves;
-  if (!zs::parse_waves_override(getenv("ZS_WAVES_PER_CU"), &override_waves))
-    return einval("zero_shard_step_static: ZS_WAVES_PER_CU must be 0 (no cap) or 3..64");
   const zs::LdsPlan lds = zs::lds_plan(M, S, d.n_cu, d.lds_cu, override_waves);
   if (!zs::lds_plan_fits(lds, d.static_lds, d.per_wg, d.lds_cu))
     return einval("zero_shard_step_static: an LDS reservation exceeds the device's "

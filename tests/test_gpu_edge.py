@@ -187,3 +187,30 @@ def test_two_contexts_on_two_streams_concurrently():
         b.close()
     for x, y in zip(runs[False][0] + runs[False][1], runs[True][0] + runs[True][1]):
         assert np.array_equal(_bits(x), _bits(y))
+
+
+@pytest.mark.parametrize("cap", ["3", "64", "0"])
+def test_wave_cap_override_keeps_results(monkeypatch, cap):
+    """ZS_WAVES_PER_CU at its extremes -- 3 (the largest LDS reservation any launch
+    makes, 54,528 B per workgroup), 64 and 0 (no cap) -- passes the context's LDS check
+    and changes only how many waves reside, never a result: clipped steps on the
+    fused and the staged context stay bit-identical to the oracle."""
+    monkeypatch.setenv("ZS_WAVES_PER_CU", cap)
+    log(f"test_wave_cap_override_keeps_results cap={cap}")
+    for flags in (0, zsm.ZS_STAGE_AVERAGE):
+        w = _small(M=5)
+        w.max_grad_norm = 0.3
+        sh = Shard(w, flags=flags)
+        S = sh.S
+        mask = sh.lay.decay_mask()
+        p, m, v = sh.case.host_master(), np.zeros(S, np.float32), np.zeros(S, np.float32)
+        b = np.zeros(S, np.uint16)
+        for s in range(2):
+            sh.step(s)
+            g = sh.case.host_grads(s)
+            coef = oracle.clip_coef(oracle.grad_sumsq(g), w.max_grad_norm)
+            oracle.step_f32(g, p, m, v, b, mask, step=s + 1, coef=coef, **sh.hp())
+        torch.cuda.synchronize()
+        for a, want in zip(_state(sh.zs), (p, m, v, b)):
+            assert np.array_equal(_bits(a), _bits(want)), (cap, flags)
+        sh.close()
