@@ -469,8 +469,10 @@ void zero_offload_destroy(zs_offload *ctx);
  * elements, 2.1G with one run; an unclipped one beyond about 8.5G elements
  * with several runs) is refused with ZS_EINVAL and a message; use
  * zero_shard_init with a workspace then.
- *   plan        the layout (host); it must outlive the call's table upload,
- *               which copies from it on `stream`
+ *   plan        the layout (host), read during the call only: its run table
+ *               travels to the scratch in kernel arguments and the tile flags
+ *               are built from it on the device, so the call enqueues kernels
+ *               only (no copy, no memset) and can be captured in a HIP graph
  *   M, buffers  as zero_shard_init / zero_shard_step (device pointers, 16-byte
  *               aligned, shard_len elements each); grads[0..M) bf16
  *   step, hyper-parameters, max_grad_norm: as zero_shard_step (no norm out)
@@ -478,8 +480,9 @@ void zero_offload_destroy(zs_offload *ctx);
  * scratch (each call re-uploads its tables and writes every partial it reads,
  * so nothing needs clearing): calls that overlap on one GPU -- other threads,
  * other streams -- race and must be ordered by the caller; calls on one stream
- * are ordered already.  Errors: ZS_EINVAL (found before any device call),
- * ZS_EHIP.
+ * are ordered already.  The first call on a device resolves the scratch's
+ * address and queries the device: make it outside any graph capture.
+ * Errors: ZS_EINVAL (found before any device call), ZS_EHIP.
  */
 #define ZS_STATIC_SCRATCH_BYTES (8u << 20)
 int zero_shard_step_static(const zs_plan *plan, int32_t M, void *param_bf16, float *master,

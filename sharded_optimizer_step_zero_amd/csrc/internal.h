@@ -207,6 +207,16 @@ hipError_t launch_step(int M, bool use_clip, const GradPtrs& g, float* master, f
                        const ClipScalars* clip, const StepConsts& k, size_t lds,
                        int64_t max_groups, hipStream_t stream);
 
+// n_words 32-bit words from host memory to device memory through kernel
+// arguments (launches of at most 512 words; the host data is read before the
+// call returns).  No copy engine, no allocation: capturable in a graph.
+hipError_t launch_store_words(const uint32_t* host_words, int64_t n_words, uint32_t* dst,
+                              hipStream_t stream);
+// The tile-flag table (tile_flag_words(shard_len, n_runs) words) from a device
+// run table with its sentinel, as the planner computes it on the host.
+hipError_t launch_tile_flags(const Run* runs, int32_t n_runs, int64_t shard_len, uint32_t* flags,
+                             hipStream_t stream);
+
 // The largest static LDS of the kernels that launch with a reservation, for M
 // contributions (hipFuncGetAttributes on the current device).
 hipError_t reserved_kernels_static_lds(int M, size_t* worst);

@@ -766,7 +766,70 @@ hipError_t launch_sumsq_m(const GradPtrs& g, int64_t shard_len, double* partials
   return hipGetLastError();
 }
 
+// Small host tables handed to the device through kernel arguments: each
+// launch carries up to kArgWords 32-bit words by value and one workgroup
+// stores them.  No host memory is read once the launch call has returned,
+// nothing is allocated, and the launches can be captured in a graph.
+constexpr int kArgWords = 512;  // 2 KiB of payload, well inside the kernel-argument limit
+struct ArgWords {
+  uint32_t w[kArgWords];
+};
+
+__global__ __launch_bounds__(kThreads) void store_words_kernel(ArgWords a,
+                                                               uint32_t* __restrict__ dst,
+                                                               int32_t n) {
+  for (int32_t i = threadIdx.x; i < n; i += kThreads) dst[i] = a.w[i];
+}
+
+// The tile-flag table from a run table on the device (the same 2 bits per
+// step tile the planner computes on the host): thread w builds word w, tiles
+// 16w .. 16w + 15.  runs[n_runs] is the sentinel (start = shard_len), and
+// runs[0].start == 0, so every tile's first element lies in some run.
+__global__ __launch_bounds__(kThreads) void tile_flags_kernel(const Run* __restrict__ runs,
+                                                              int32_t n_runs, int64_t shard_len,
+                                                              uint32_t* __restrict__ flags,
+                                                              int64_t words) {
+  const int64_t wi = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (wi >= words) return;
+  const int64_t tiles = (shard_len + kTile - 1) / kTile;
+  uint32_t out = 0;
+  for (int k = 0; k < 16; k++) {
+    const int64_t t = wi * 16 + k;
+    if (t >= tiles) break;
+    const int64_t lo = t * kTile;
+    const int64_t hi = lo + kTile < shard_len ? lo + kTile : shard_len;
+    const int32_t r = find_run(runs, n_runs, lo);
+    const uint32_t f = runs[r + 1].start < hi ? 2u : ((uint32_t)runs[r].flags & 1u);
+    out |= f << (k * 2);
+  }
+  flags[wi] = out;
+}
+
 }  // namespace
+
+hipError_t launch_store_words(const uint32_t* host_words, int64_t n_words, uint32_t* dst,
+                              hipStream_t stream) {
+  for (int64_t off = 0; off < n_words; off += kArgWords) {
+    ArgWords a;
+    const int32_t m = (int32_t)(n_words - off < kArgWords ? n_words - off : kArgWords);
+    for (int32_t i = 0; i < kArgWords; i++) a.w[i] = i < m ? host_words[off + i] : 0u;
+    hipLaunchKernelGGL(store_words_kernel, dim3(1), dim3(kThreads), 0, stream, a, dst + off, m);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_tile_flags(const Run* runs, int32_t n_runs, int64_t shard_len, uint32_t* flags,
+                             hipStream_t stream) {
+  const int64_t words = tile_flag_words(shard_len, n_runs);
+  if (words <= 0) return hipSuccess;
+  const int64_t blocks = (words + kThreads - 1) / kThreads;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tile_flags_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, runs,
+                     n_runs, shard_len, flags, words);
+  return hipGetLastError();
+}
 
 // Level-1 plus level-2 partials of the norm pass; the level-2 ones (at most a few
 // thousand) start at offset level1_partials(shard_len) and feed the finalize step.

@@ -14,9 +14,11 @@
 // same arithmetic, so both entry points give the same bits.
 //
 // Every call on a GPU shares that GPU's scratch and leaves its contents there:
-// each call first uploads the plan's tables into it, and every partial sum and
-// scalar a kernel reads is written earlier in the same call, so nothing has to
-// start at zero.  Calls that overlap on one GPU (other host threads, other
+// each call first writes the plan's tables into it (the run table through
+// kernel arguments, the tile flags computed from it on the device, so a call
+// enqueues kernels only and can be captured in a graph), and every partial sum
+// and scalar a kernel reads is written earlier in the same call, so nothing
+// has to start at zero.  Calls that overlap on one GPU (other host threads, other
 // streams) race on the scratch; calls ordered on one stream do not.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -163,17 +165,21 @@ extern "C" int zero_shard_step_static(const zs_plan* plan, int32_t M, void* para
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   unsigned char* base = d.ptr;  // the scratch's device address, never the symbol
-  hipError_t e = hipMemcpyAsync(base + lay.runs_off, plan->run_table.data(), lay.runs_bytes,
-                                hipMemcpyHostToDevice, st);
+  const int32_t n_runs = (int32_t)(plan->run_table.size() - 1);
+  zs::Run* runs_dev = reinterpret_cast<zs::Run*>(base + lay.runs_off);
+  uint32_t* tflags_dev = reinterpret_cast<uint32_t*>(base + lay.tflags_off);
+  // the run table travels in kernel arguments; the tile flags are built from it
+  // on the device: the call enqueues kernels only
+  hipError_t e = zs::launch_store_words(reinterpret_cast<const uint32_t*>(plan->run_table.data()),
+                                        (int64_t)(lay.runs_bytes / sizeof(uint32_t)),
+                                        reinterpret_cast<uint32_t*>(runs_dev), st);
   if (e == hipSuccess && lay.tflags_bytes)
-    e = hipMemcpyAsync(base + lay.tflags_off, plan->tile_flags.data(), lay.tflags_bytes,
-                       hipMemcpyHostToDevice, st);
+    e = zs::launch_tile_flags(runs_dev, n_runs, S, tflags_dev, st);
   if (e != hipSuccess) return zs::ehip("zero_shard_step_static: table upload", e);
   zs::RunTable rt;
-  rt.runs = reinterpret_cast<const zs::Run*>(base + lay.runs_off);
-  rt.tile_flags = lay.tflags_bytes ? reinterpret_cast<const uint32_t*>(base + lay.tflags_off)
-                                   : nullptr;
-  rt.n_runs = (int32_t)(plan->run_table.size() - 1);
+  rt.runs = runs_dev;
+  rt.tile_flags = lay.tflags_bytes ? tflags_dev : nullptr;
+  rt.n_runs = n_runs;
   zs::ClipScalars* sc = reinterpret_cast<zs::ClipScalars*>(base + lay.scalars_off);
   const int64_t max_groups = zs::max_groups_from_env();
   if (clip) {

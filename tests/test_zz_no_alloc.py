@@ -1,8 +1,10 @@
 """The allocation-free step (zero_shard_step_static) against the context step
 (zero_shard_step) through the C ABI: the same seeded inputs through both entry
 points give the same bits for master, m, v and the bf16 param, on two calls in
-a row (two steps each), the second with a smaller shard, clipped and not.  The
-second call reuses the static scratch the first left behind."""
+a row (two steps each), each shard smaller than the one before, clipped and not;
+every call reuses the static scratch the one before left behind.  The same step
+captured in a HIP graph and replayed, with eager work and synchronisations
+between the replays, matches the eager context step after every replay."""
 import numpy as np
 import pytest
 import torch
@@ -18,10 +20,13 @@ pytestmark = pytest.mark.gpu
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
 
 CASES = [
-    # (numel, decay, N, rank, M, max_grad_norm): a larger shard with several decay
-    # runs and a ragged end, clipped; then a smaller one, unclipped
-    ([70_001, 64, 5, 2 ** 17 + 8, 333], [1, 0, 0, 1, 0], 2, 1, 5, 0.05),
-    ([3000, 64, 7], [1, 0, 1], 1, 0, 3, 0.0),
+    # (numel, decay, N, rank, M, max_grad_norm, align): a larger shard with several
+    # decay runs and a ragged end, clipped; 320 small tensors alternating decay (321
+    # runs: a run table of three kernel-argument launches, runs starting inside
+    # tiles); then a smaller shard, unclipped
+    ([70_001, 64, 5, 2 ** 17 + 8, 333], [1, 0, 0, 1, 0], 2, 1, 5, 0.05, 64),
+    ([3, 9, 1, 17, 2, 40, 5, 8] * 40, [1, 0] * 160, 1, 0, 2, 0.3, 8),
+    ([3000, 64, 7], [1, 0, 1], 1, 0, 3, 0.0, 64),
 ]
 
 
@@ -36,12 +41,12 @@ def _state(z):
 
 
 def test_static_step_equals_context_step():
-    for case, (numel, decay, N, rank, M, clip) in enumerate(CASES):
+    for case, (numel, decay, N, rank, M, clip, align) in enumerate(CASES):
         log(f"test_static_step_equals_context_step case {case}: tensors={len(numel)} N={N} "
-            f"r={rank} M={M} clip={clip}")
-        lay = L.plan(numel, decay, N, rank, 25_000_000, 64)
-        ref = ZeroShard(numel, decay, N, rank, M, grad_buffers=True)   # the context step
-        sta = ZeroShard(numel, decay, N, rank, M)                      # buffers for the static one
+            f"r={rank} M={M} clip={clip} align={align}")
+        lay = L.plan(numel, decay, N, rank, 25_000_000, align)
+        ref = ZeroShard(numel, decay, N, rank, M, align=align, grad_buffers=True)  # context step
+        sta = ZeroShard(numel, decay, N, rank, M, align=align)  # buffers for the static one
         S = ref.shard_len
         assert S == sta.shard_len == lay.shard_len
         master = synth.host_normal_f32(S, synth.key(91, case), 0.02)
@@ -69,3 +74,56 @@ def test_static_step_equals_context_step():
         log(f"  case {case}: S={S:,}, 2 steps bit-identical to zero_shard_step")
         ref.close()
         sta.close()
+
+
+def test_static_step_replayed_from_a_graph():
+    """Two static steps captured once in a HIP graph (torch's graph API on a side
+    stream) and replayed four times, with eager work and a synchronisation between
+    replays: after every replay master, m, v and the param equal those of a context
+    that took the same two steps eagerly each time."""
+    numel, decay, N, rank, M, clip = [5000, 64, 70_001, 7], [1, 0, 1, 0], 2, 1, 3, 0.4
+    log("test_static_step_replayed_from_a_graph")
+    lay = L.plan(numel, decay, N, rank, 25_000_000, 64)
+    ref = ZeroShard(numel, decay, N, rank, M, grad_buffers=True)
+    sta = ZeroShard(numel, decay, N, rank, M)
+    S = ref.shard_len
+    master = synth.host_normal_f32(S, synth.key(94, 0), 0.02)
+    for o, n in lay.padding_ranges():
+        master[o:o + n] = 0
+    for z in (ref, sta):
+        z.master[:S].copy_(torch.from_numpy(master))
+    for j in range(M):
+        g = synth.host_grad_bf16(S, synth.key(95, j), synth.key(96, j), 1e-3)
+        for o, n in lay.padding_ranges():
+            g[o:o + n] = 0
+        ref.grads[j][:S].copy_(torch.from_numpy(g.view(np.int16)).view(torch.bfloat16))
+    ptrs = [g.data_ptr() for g in ref.grads]
+    # the first call on a device resolves the scratch and queries the device: make it
+    # outside the capture (an eager step on a throwaway shard)
+    w0 = ZeroShard([256], [1], 1, 0, 1, grad_buffers=True)
+    zsm.zero_shard_step_static(w0.plan, 1, w0.param.data_ptr(), w0.master.data_ptr(),
+                               w0.exp_avg.data_ptr(), w0.exp_avg_sq.data_ptr(),
+                               [w0.grads[0].data_ptr()], step=1, **HP)
+    torch.cuda.synchronize()
+    w0.close()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        s = torch.cuda.current_stream().cuda_stream
+        for step in (1, 2):
+            zsm.zero_shard_step_static(sta.plan, M, sta.param.data_ptr(), sta.master.data_ptr(),
+                                       sta.exp_avg.data_ptr(), sta.exp_avg_sq.data_ptr(), ptrs,
+                                       step=step, max_grad_norm=clip, stream=s, **HP)
+    other = torch.ones(1 << 20, device="cuda")
+    for replay in range(4):
+        graph.replay()
+        for step in (1, 2):
+            ref.step(ref.grads, step=step, max_grad_norm=clip, **HP)
+        other.mul_(1.5).add_(0.25)          # the program's own eager work between replays
+        torch.cuda.synchronize()
+        for a, b, name in zip(_state(sta), _state(ref), ("master", "m", "v", "param")):
+            assert np.array_equal(_bits(a), _bits(b)), (replay, name)
+    log("  4 replays, each bit-identical to the eager context steps")
+    ref.close()
+    sta.close()
