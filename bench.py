@@ -231,6 +231,32 @@ def sweep_caps(zs, grads, w, hp, stream, caps, rounds: int, steps: int) -> dict:
             "steps_per_round": steps, "note": "same buffers, one context per cap, no clip"}
 
 
+def time_static(zs, grads, w, hp, stream, steps: int, step0: int) -> dict:
+    """The allocation-free entry point (zero_shard_step_static) on the same buffers:
+    no context, its tables and partials in the library's static device scratch."""
+    import torch
+
+    import sharded_optimizer_step_zero_amd as zsm
+    ptrs = [g if isinstance(g, int) else g.data_ptr() for g in grads]
+
+    def one(step):
+        zsm.zero_shard_step_static(zs.plan, w.M, zs.param.data_ptr(), zs.master.data_ptr(),
+                                   zs.exp_avg.data_ptr(), zs.exp_avg_sq.data_ptr(), ptrs,
+                                   step=step, max_grad_norm=w.max_grad_norm,
+                                   stream=stream.cuda_stream, **hp)
+    one(step0)                                    # the first call resolves the scratch
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(steps):
+        one(step0 + 1 + s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms_per_step": ms, "params_per_s": zs.shard_len / (ms * 1e-3), "steps": steps}
+
+
 def time_cold(zs, grads, w, hp, stream, step0: int, reps: int) -> dict:
     """Per-step time with the 256 MB Infinity Cache evicted before each step (a
     1 GiB buffer is overwritten between steps, outside the timed events)."""
@@ -443,6 +469,9 @@ def main():
     ap.add_argument("--contiguous", action="store_true",
                     help="take the shard's slab from physically contiguous device memory "
                          "(ZeroShard(contiguous=True))")
+    ap.add_argument("--static-step", action="store_true",
+                    help="also time the allocation-free entry point (zero_shard_step_static) on "
+                         "the same buffers (adds a 'static_step' object)")
     ap.add_argument("--sweep-caps", default="",
                     help="comma-separated step-kernel wave caps (0 = no cap) to time on the "
                          "same buffers after the headline (adds a 'cap_sweep' object)")
@@ -592,6 +621,9 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.static_step:
+        out["static_step"] = time_static(zs, grads, w, hp, stream, args.steps,
+                                         args.warmup + args.steps + n_spread + 1)
     if args.sweep_caps:
         out["cap_sweep"] = sweep_caps(zs, grads, w, hp, stream,
                                       [int(c) for c in args.sweep_caps.split(",")],
