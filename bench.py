@@ -13,6 +13,7 @@ using the algorithmic bytes 2M+12 read + 14 written per parameter;
 
     python bench.py [--steps K] [--warmup W] [--workload 1..5] [--no-cpu-baseline]
                     [--checkpoint] [--amp] [--offload] [--cold] [--no-extras]
+                    [--graph] [--static-step] [--sweep-caps 8,9,...] [--ceiling]
 
 The default workload is the largest one a single GPU holds: the unsharded
 Llama-shaped 6.7B parameter list (M = 1, 108 GB of state resident).  With
@@ -257,6 +258,41 @@ def time_static(zs, grads, w, hp, stream, steps: int, step0: int) -> dict:
     return {"ms_per_step": ms, "params_per_s": zs.shard_len / (ms * 1e-3), "steps": steps}
 
 
+def time_ceiling(zs, stream, reps: int) -> dict:
+    """What the library-side copies reach on the shard's own slab (same placement as
+    the step): torch's device-to-device copy_ (hipMemcpyAsync) and a plain 16-byte
+    copy kernel from master into exp_avg (one read and one write stream, as the
+    step's mix), a fill of exp_avg_sq (writes only) and a sum of master (reads
+    only).  Overwrites the optimizer state, so it runs after every other step leg."""
+    import torch
+
+    import synth
+    S = zs.shard_len
+    src, dst, fill = zs.master[:S], zs.exp_avg[:S], zs.exp_avg_sq[:S]
+    acc = torch.empty((), dtype=torch.float32, device=zs.device)
+    legs = {
+        "memcpy_d2d": (lambda: dst.copy_(src), 8 * S),
+        "copy_kernel_16B": (lambda: synth.dev_copy(dst, src, stream.cuda_stream), 8 * S),
+        "fill": (lambda: fill.fill_(1.0), 4 * S),
+        "sum": (lambda: torch.sum(src, (0,), out=acc), 4 * S),
+    }
+    out = {}
+    for name, (fn, nbytes) in legs.items():
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": ms, "bytes": nbytes, "gbs": gbs, "frac": gbs / PEAK_HBM_GBS}
+    return out
+
+
 def time_cold(zs, grads, w, hp, stream, step0: int, reps: int) -> dict:
     """Per-step time with the 256 MB Infinity Cache evicted before each step (a
     1 GiB buffer is overwritten between steps, outside the timed events)."""
@@ -476,6 +512,10 @@ def main():
                     help="comma-separated step-kernel wave caps (0 = no cap) to time on the "
                          "same buffers after the headline (adds a 'cap_sweep' object)")
     ap.add_argument("--sweep-rounds", type=int, default=3)
+    ap.add_argument("--ceiling", action="store_true",
+                    help="last, time torch's device copy, a plain copy kernel, a fill and a "
+                         "sum on the shard's own slab (adds a 'ceiling' object; overwrites "
+                         "the optimizer state)")
     ap.add_argument("--cpu-slab", type=int, default=1 << 25)
     ap.add_argument("--calibrate-copy-gib", type=float, default=1.0,
                     help="size of the plain copy run once before timing (counter calibration)")
@@ -643,6 +683,8 @@ def main():
                                       args.offload_chunk)
         out["offload_fp16"] = time_offload(w, pad, dev, stream, max(3, args.steps // 20), 2,
                                            args.offload_chunk, fp16=True)
+    if args.ceiling:
+        out["ceiling"] = time_ceiling(zs, stream, max(args.steps, 5))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_slab, S))
     print(json.dumps(out), flush=True)
