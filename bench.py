@@ -262,20 +262,28 @@ def time_ceiling(zs, stream, reps: int) -> dict:
     """What the library-side copies reach on the shard's own slab (same placement as
     the step): torch's device-to-device copy_ (hipMemcpyAsync) and a plain 16-byte
     copy kernel from master into exp_avg (one read and one write stream, as the
-    step's mix), a fill of exp_avg_sq (writes only) and a sum of master (reads
-    only).  Overwrites the optimizer state, so it runs after every other step leg."""
+    step's mix), a fill of exp_avg_sq (writes only; again over its first S rounded
+    down to a multiple of 2^20 elements) and a sum of master (reads only).
+    Overwrites the optimizer state, so it runs after every other step leg."""
     import torch
 
     import synth
     S = zs.shard_len
     src, dst, fill = zs.master[:S], zs.exp_avg[:S], zs.exp_avg_sq[:S]
     acc = torch.empty((), dtype=torch.float32, device=zs.device)
+    S20 = S >> 20 << 20
+    fill20 = zs.exp_avg_sq[:S20]
     legs = {
         "memcpy_d2d": (lambda: dst.copy_(src), 8 * S),
         "copy_kernel_16B": (lambda: synth.dev_copy(dst, src, stream.cuda_stream), 8 * S),
         "fill": (lambda: fill.fill_(1.0), 4 * S),
+        # torch's fill is slower at some element counts: the same array, cut down to a
+        # multiple of 2^20 elements
+        "fill_2pow20_multiple": (lambda: fill20.fill_(1.0), 4 * S20),
         "sum": (lambda: torch.sum(src, (0,), out=acc), 4 * S),
     }
+    if S20 == 0:
+        del legs["fill_2pow20_multiple"]
     out = {}
     for name, (fn, nbytes) in legs.items():
         fn()
