@@ -2,8 +2,11 @@
  * abi_check.c -- the C ABI used from plain C with the HIP runtime alone (no
  * Python, no torch): one hipMalloc'ed slab placed by zs_slab_layout, a plan, a
  * context, three steps (the second clipped), checked bit for bit against the CPU oracle
- * (oracle/libzo.so, test infrastructure) on the same inputs.  Exit status 0 on
- * agreement.
+ * (oracle/libzo.so, test infrastructure) on the same inputs.  Then the
+ * allocation-free step (zero_shard_step_static) continues the same state: once
+ * eagerly, then two steps (one clipped) captured into a HIP graph and replayed
+ * twice, with an eager context step between the replays; every replay is
+ * checked bit for bit against the oracle.  Exit status 0 on agreement.
  */
 #include <hip/hip_runtime_api.h>
 #include <math.h>
@@ -52,6 +55,26 @@ static uint16_t bf16_trunc(float x)
     uint32_t u;
     memcpy(&u, &x, 4);
     return (uint16_t)(u >> 16);
+}
+
+/* device state against the oracle's host state, bit for bit */
+static int same_as_oracle(const char *what, int64_t S, hipStream_t stream, const float *d_master,
+                          const float *d_m, const float *d_v, const void *d_param,
+                          const float *master, const float *m, const float *v,
+                          const uint16_t *param, float *got_master, float *got_m, float *got_v,
+                          uint16_t *got_param)
+{
+    CHECK_HIP(hipStreamSynchronize(stream));
+    CHECK_HIP(hipMemcpy(got_master, d_master, S * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(got_m, d_m, S * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(got_v, d_v, S * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(got_param, d_param, S * 2, hipMemcpyDeviceToHost));
+    if (memcmp(got_master, master, S * 4) || memcmp(got_m, m, S * 4) ||
+        memcmp(got_v, v, S * 4) || memcmp(got_param, param, S * 2)) {
+        fprintf(stderr, "%s: device state differs from the oracle\n", what);
+        return 1;
+    }
+    return 0;
 }
 
 int main(void)
@@ -137,17 +160,65 @@ int main(void)
         if (zo_step_f32(S, M, gp, master, m, v, param, mask, 1e-3f, 0.9f, 0.95f, 1e-8f, 0.1f, t,
                         use_coef, coef) != 0)
             return 2;
-        CHECK_HIP(hipStreamSynchronize(stream));
-        CHECK_HIP(hipMemcpy(got_master, d_master, S * 4, hipMemcpyDeviceToHost));
-        CHECK_HIP(hipMemcpy(got_m, d_m, S * 4, hipMemcpyDeviceToHost));
-        CHECK_HIP(hipMemcpy(got_v, d_v, S * 4, hipMemcpyDeviceToHost));
-        CHECK_HIP(hipMemcpy(got_param, d_param, S * 2, hipMemcpyDeviceToHost));
-        if (memcmp(got_master, master, S * 4) || memcmp(got_m, m, S * 4) ||
-            memcmp(got_v, v, S * 4) || memcmp(got_param, param, S * 2)) {
-            fprintf(stderr, "step %d: device state differs from the oracle\n", t);
+        char what[32];
+        snprintf(what, sizeof what, "step %d", t);
+        if (same_as_oracle(what, S, stream, d_master, d_m, d_v, d_param, master, m, v, param,
+                           got_master, got_m, got_v, got_param))
             return 1;
+    }
+
+    /* the allocation-free step on the same state: its first call on the device runs
+       eagerly (it resolves the static scratch there), the next two are captured */
+    const double norm_oracle = sqrt(zo_grad_sumsq(S, M, gp));
+    const float coef_oracle = zo_coef_from_norm(norm_oracle, 0.05f);
+    CHECK_ZS(zero_shard_step_static(plan, M, d_param, d_master, d_m, d_v,
+                                    (const void *const *)d_grads, 1e-3f, 0.9f, 0.95f, 1e-8f, 0.1f,
+                                    4, 0.0f, stream));
+    if (zo_step_f32(S, M, gp, master, m, v, param, mask, 1e-3f, 0.9f, 0.95f, 1e-8f, 0.1f, 4, 0,
+                    1.0f) != 0)
+        return 2;
+    if (same_as_oracle("static step 4", S, stream, d_master, d_m, d_v, d_param, master, m, v,
+                       param, got_master, got_m, got_v, got_param))
+        return 1;
+    hipGraph_t graph = NULL;
+    hipGraphExec_t exec = NULL;
+    CHECK_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal));
+    int rc5 = zero_shard_step_static(plan, M, d_param, d_master, d_m, d_v,
+                                     (const void *const *)d_grads, 1e-3f, 0.9f, 0.95f, 1e-8f,
+                                     0.1f, 5, 0.05f, stream);
+    int rc6 = zero_shard_step_static(plan, M, d_param, d_master, d_m, d_v,
+                                     (const void *const *)d_grads, 1e-3f, 0.9f, 0.95f, 1e-8f,
+                                     0.1f, 6, 0.0f, stream);
+    CHECK_HIP(hipStreamEndCapture(stream, &graph));
+    CHECK_ZS(rc5);
+    CHECK_ZS(rc6);
+    CHECK_HIP(hipGraphInstantiate(&exec, graph, NULL, NULL, 0));
+    for (int replay = 1; replay <= 2; replay++) {
+        CHECK_HIP(hipGraphLaunch(exec, stream));
+        if (zo_step_f32(S, M, gp, master, m, v, param, mask, 1e-3f, 0.9f, 0.95f, 1e-8f, 0.1f, 5,
+                        1, coef_oracle) != 0 ||
+            zo_step_f32(S, M, gp, master, m, v, param, mask, 1e-3f, 0.9f, 0.95f, 1e-8f, 0.1f, 6,
+                        0, 1.0f) != 0)
+            return 2;
+        char what[48];
+        snprintf(what, sizeof what, "graph replay %d (static steps 5, 6)", replay);
+        if (same_as_oracle(what, S, stream, d_master, d_m, d_v, d_param, master, m, v, param,
+                           got_master, got_m, got_v, got_param))
+            return 1;
+        if (replay == 1) {
+            /* eager work of the program's own between the replays */
+            CHECK_ZS(zero_shard_step(ctx, (const void *const *)d_grads, 1e-3f, 0.9f, 0.95f,
+                                     1e-8f, 0.1f, 7, 0.0f, NULL));
+            if (zo_step_f32(S, M, gp, master, m, v, param, mask, 1e-3f, 0.9f, 0.95f, 1e-8f,
+                            0.1f, 7, 0, 1.0f) != 0)
+                return 2;
+            if (same_as_oracle("context step 7", S, stream, d_master, d_m, d_v, d_param, master,
+                               m, v, param, got_master, got_m, got_v, got_param))
+                return 1;
         }
     }
+    CHECK_HIP(hipGraphExecDestroy(exec));
+    CHECK_HIP(hipGraphDestroy(graph));
     const void *pp = NULL;
     int64_t plen = 0;
     CHECK_ZS(zero_shard_params(ctx, &pp, &plen));
@@ -162,7 +233,8 @@ int main(void)
     CHECK_HIP(hipFree(slab));
     free(master), free(m), free(v), free(got_master), free(got_m), free(got_v);
     free(param), free(got_param), free(mask);
-    printf("c-abi check ok: S=%lld, M=%d, 3 steps (one clipped), bit-identical to the oracle\n",
+    printf("c-abi check ok: S=%lld, M=%d, 3 context steps (one clipped), the allocation-free "
+           "step eagerly and from a HIP graph replayed twice, bit-identical to the oracle\n",
            (long long)S, M);
     return 0;
 }

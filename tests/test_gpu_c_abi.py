@@ -1,5 +1,6 @@
 """The C ABI from plain C with the HIP runtime alone (tests/c_abi/abi_check.c): no
-Python binding and no torch in that process; bit-identical to the oracle."""
+Python binding and no torch in that process; bit-identical to the oracle, including
+the allocation-free step captured into a HIP graph and replayed."""
 import os
 import subprocess
 
