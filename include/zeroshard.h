@@ -475,7 +475,9 @@ void zero_offload_destroy(zs_offload *ctx);
  *               only (no copy, no memset) and can be captured in a HIP graph
  *   M, buffers  as zero_shard_init / zero_shard_step (device pointers, 16-byte
  *               aligned, shard_len elements each); grads[0..M) bf16
- *   step, hyper-parameters, max_grad_norm: as zero_shard_step (no norm out)
+ *   step, hyper-parameters, max_grad_norm: as zero_shard_step on a context
+ *               made with flags 0 (bf16, no staged average, and a non-finite
+ *               norm is not skipped); no norm output
  * Enqueues on `stream` and returns.  Every call on a GPU shares that GPU's
  * scratch (each call re-uploads its tables and writes every partial it reads,
  * so nothing needs clearing): calls that overlap on one GPU -- other threads,
