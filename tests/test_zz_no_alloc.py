@@ -4,7 +4,8 @@ points give the same bits for master, m, v and the bf16 param, on two calls in
 a row (two steps each), each shard smaller than the one before, clipped and not;
 every call reuses the static scratch the one before left behind.  The same step
 captured in a HIP graph and replayed, with eager work and synchronisations
-between the replays, matches the eager context step after every replay."""
+between the replays, matches the eager context step after every replay, and on
+non-finite contributions the static step does what a flags-0 context does."""
 import numpy as np
 import pytest
 import torch
@@ -125,5 +126,46 @@ def test_static_step_replayed_from_a_graph():
         for a, b, name in zip(_state(sta), _state(ref), ("master", "m", "v", "param")):
             assert np.array_equal(_bits(a), _bits(b)), (replay, name)
     log("  4 replays, each bit-identical to the eager context steps")
+    ref.close()
+    sta.close()
+
+
+def test_static_step_with_nonfinite_gradient_matches_flags0_context():
+    """A clipped step whose contributions hold an Inf and a NaN: the static step does
+    what a context made with flags 0 does (the non-finite norm is not skipped), bit
+    for bit, including the non-finite results."""
+    numel, decay, N, rank, M, clip = [4097, 64, 9000], [1, 0, 1], 1, 0, 2, 1.0
+    log("test_static_step_with_nonfinite_gradient_matches_flags0_context")
+    lay = L.plan(numel, decay, N, rank, 25_000_000, 64)
+    ref = ZeroShard(numel, decay, N, rank, M, grad_buffers=True)
+    sta = ZeroShard(numel, decay, N, rank, M)
+    S = ref.shard_len
+    master = synth.host_normal_f32(S, synth.key(97, 0), 0.02)
+    for o, n in lay.padding_ranges():
+        master[o:o + n] = 0
+    for z in (ref, sta):
+        z.master[:S].copy_(torch.from_numpy(master))
+    for j in range(M):
+        g = synth.host_grad_bf16(S, synth.key(98, j), synth.key(99, j), 1e-3)
+        for o, n in lay.padding_ranges():
+            g[o:o + n] = 0
+        if j == 1:
+            g[5] = 0x7F80                    # +Inf in the first tensor
+            g[4224 + 100] = 0x7FC1           # a quiet NaN in the third (which starts at 4224)
+        ref.grads[j][:S].copy_(torch.from_numpy(g.view(np.int16)).view(torch.bfloat16))
+    torch.cuda.synchronize()
+    ptrs = [g.data_ptr() for g in ref.grads]
+    for step in (1, 2):
+        ref.step(ref.grads, step=step, max_grad_norm=clip, **HP)
+        zsm.zero_shard_step_static(sta.plan, M, sta.param.data_ptr(), sta.master.data_ptr(),
+                                   sta.exp_avg.data_ptr(), sta.exp_avg_sq.data_ptr(), ptrs,
+                                   step=step, max_grad_norm=clip,
+                                   stream=torch.cuda.current_stream().cuda_stream, **HP)
+        torch.cuda.synchronize()
+        st = _state(sta)
+        assert not np.isfinite(st[0]).all()  # the non-finite norm reached the state
+        for a, b, name in zip(st, _state(ref), ("master", "m", "v", "param")):
+            assert np.array_equal(_bits(a), _bits(b)), (step, name)
+    log(f"  S={S:,}: 2 clipped steps on non-finite contributions, bit-identical")
     ref.close()
     sta.close()
