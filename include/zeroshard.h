@@ -483,8 +483,10 @@ void zero_offload_destroy(zs_offload *ctx);
  * so nothing needs clearing): calls that overlap on one GPU -- other threads,
  * other streams -- race and must be ordered by the caller; calls on one stream
  * are ordered already.  The first call on a device resolves the scratch's
- * address and queries the device: make it outside any graph capture.
- * Errors: ZS_EINVAL (found before any device call), ZS_EHIP.
+ * address and queries the device: make it outside any graph capture (made
+ * while `stream` is capturing, it is refused with ZS_EINVAL and leaves the
+ * capture untouched).
+ * Errors: ZS_EINVAL (found before anything is enqueued), ZS_EHIP.
  */
 #define ZS_STATIC_SCRATCH_BYTES (8u << 20)
 int zero_shard_step_static(const zs_plan *plan, int32_t M, void *param_bf16, float *master,

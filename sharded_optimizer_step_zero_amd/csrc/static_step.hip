@@ -53,7 +53,7 @@ struct DeviceSetup {
 std::mutex g_setup_mu;
 DeviceSetup g_setup[kMaxDevices];
 
-int device_setup(DeviceSetup* out) {
+int device_setup(hipStream_t stream, DeviceSetup* out) {
   const char* who = "zero_shard_step_static";
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -63,6 +63,14 @@ int device_setup(DeviceSetup* out) {
   std::lock_guard<std::mutex> lock(g_setup_mu);
   DeviceSetup& d = g_setup[dev];
   if (!d.ready) {
+    // the set-up queries below are not stream work and would break a capture in
+    // progress: refuse before making any of them
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return zs::ehip("zero_shard_step_static: capture status", e);
+    if (cs != hipStreamCaptureStatusNone)
+      return zs::einval("zero_shard_step_static: the first call on a device must run outside "
+                        "graph capture (it resolves the static scratch and queries the device)");
     DeviceSetup n;
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
@@ -156,14 +164,14 @@ extern "C" int zero_shard_step_static(const zs_plan* plan, int32_t M, void* para
   const int64_t S = plan->shard_len;
   if (S == 0) return ZS_OK;
 
+  hipStream_t st = static_cast<hipStream_t>(stream);
   DeviceSetup d;
-  if (int rc = device_setup(&d)) return rc;
+  if (int rc = device_setup(st, &d)) return rc;
   const zs::LdsPlan lds = zs::lds_plan(M, S, d.n_cu, d.lds_cu, override_waves);
   if (!zs::lds_plan_fits(lds, d.static_lds, d.per_wg, d.lds_cu))
     return einval("zero_shard_step_static: an LDS reservation exceeds the device's "
                   "per-workgroup limit");
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
   unsigned char* base = d.ptr;  // the scratch's device address, never the symbol
   const int32_t n_runs = (int32_t)(plan->run_table.size() - 1);
   zs::Run* runs_dev = reinterpret_cast<zs::Run*>(base + lay.runs_off);

@@ -3,7 +3,8 @@
  * Python, no torch): one hipMalloc'ed slab placed by zs_slab_layout, a plan, a
  * context, three steps (the second clipped), checked bit for bit against the CPU oracle
  * (oracle/libzo.so, test infrastructure) on the same inputs.  Then the
- * allocation-free step (zero_shard_step_static) continues the same state: once
+ * allocation-free step (zero_shard_step_static) continues the same state: a
+ * first call made under capture is refused, then it runs once
  * eagerly, then two steps (one clipped) captured into a HIP graph and replayed
  * twice, with an eager context step between the replays; every replay is
  * checked bit for bit against the oracle.  Exit status 0 on agreement.
@@ -171,6 +172,22 @@ int main(void)
        eagerly (it resolves the static scratch there), the next two are captured */
     const double norm_oracle = sqrt(zo_grad_sumsq(S, M, gp));
     const float coef_oracle = zo_coef_from_norm(norm_oracle, 0.05f);
+    {
+        /* made while the stream captures, that first call is refused and leaves the
+           capture intact */
+        hipGraph_t empty = NULL;
+        CHECK_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal));
+        const int rc = zero_shard_step_static(plan, M, d_param, d_master, d_m, d_v,
+                                              (const void *const *)d_grads, 1e-3f, 0.9f, 0.95f,
+                                              1e-8f, 0.1f, 4, 0.0f, stream);
+        CHECK_HIP(hipStreamEndCapture(stream, &empty));
+        CHECK_HIP(hipGraphDestroy(empty));
+        if (rc != ZS_EINVAL || !strstr(zero_shard_last_error(), "outside graph capture")) {
+            fprintf(stderr, "first static call under capture returned %d: %s\n", rc,
+                    zero_shard_last_error());
+            return 1;
+        }
+    }
     CHECK_ZS(zero_shard_step_static(plan, M, d_param, d_master, d_m, d_v,
                                     (const void *const *)d_grads, 1e-3f, 0.9f, 0.95f, 1e-8f, 0.1f,
                                     4, 0.0f, stream));
