@@ -4,8 +4,10 @@ points give the same bits for master, m, v and the bf16 param, on two calls in
 a row (two steps each), each shard smaller than the one before, clipped and not;
 every call reuses the static scratch the one before left behind.  The same step
 captured in a HIP graph and replayed, with eager work and synchronisations
-between the replays, matches the eager context step after every replay, and on
-non-finite contributions the static step does what a flags-0 context does."""
+between the replays, matches the eager context step after every replay; on
+non-finite contributions the static step does what a flags-0 context does; and at
+the largest clipped shard the scratch holds it still matches, while one tile more
+is refused."""
 import numpy as np
 import pytest
 import torch
@@ -169,3 +171,49 @@ def test_static_step_with_nonfinite_gradient_matches_flags0_context():
     log(f"  S={S:,}: 2 clipped steps on non-finite contributions, bit-identical")
     ref.close()
     sta.close()
+
+
+# The largest clipped single-run shard whose norm partials fit the static scratch:
+# 2^20 - 192 tiles of 2,048 elements (one fp64 partial per tile, plus one per 8,192 of
+# those, plus the 256-byte run table and 256 bytes of clip scalars: 8 MiB exactly).
+S_MAX_CLIPPED = ((1 << 20) - 192) * 2048
+
+
+def test_static_step_at_the_largest_clipped_shard_its_scratch_holds():
+    """At 2,147,090,432 elements a clipped static step fills the 8 MiB scratch exactly
+    and equals the context step bit for bit; one 2,048-element tile more is refused with
+    ZS_EINVAL before anything is enqueued (the buffers passed there are large enough for
+    that shard anyway)."""
+    S = S_MAX_CLIPPED
+    assert zsm.ZS_STATIC_SCRATCH_BYTES == 8 << 20
+    log(f"test_static_step_at_the_largest_clipped_shard_its_scratch_holds: S={S:,} M=1 clip=1.0")
+    ref = ZeroShard([S], [1], 1, 0, 1, grad_buffers=True)
+    big = ZeroShard([S + 2048], [1], 1, 0, 1)        # the static step's buffers
+    assert ref.shard_len == S and big.shard_len == S + 2048
+    synth.dev_normal_f32(ref.master[:S], synth.key(101, 0), 0.02)
+    synth.dev_grad_bf16(ref.grads[0][:S], synth.key(102, 0), synth.key(103, 0), 1e-3)
+    big.master[:S].copy_(ref.master[:S])
+    torch.cuda.synchronize()
+    g = [ref.grads[0].data_ptr()]
+    s = torch.cuda.current_stream().cuda_stream
+    for step in (1, 2):
+        ref.step(ref.grads, step=step, max_grad_norm=1.0, **HP)
+        zsm.zero_shard_step_static(ref.plan, 1, big.param.data_ptr(), big.master.data_ptr(),
+                                   big.exp_avg.data_ptr(), big.exp_avg_sq.data_ptr(), g,
+                                   step=step, max_grad_norm=1.0, stream=s, **HP)
+        torch.cuda.synchronize()
+        for a, b, name in ((big.master, ref.master, "master"), (big.exp_avg, ref.exp_avg, "m"),
+                           (big.exp_avg_sq, ref.exp_avg_sq, "v"), (big.param, ref.param, "param")):
+            ia = a[:S].view(torch.int32 if a.element_size() == 4 else torch.int16)
+            ib = b[:S].view(torch.int32 if b.element_size() == 4 else torch.int16)
+            assert torch.equal(ia, ib), (step, name)
+    with pytest.raises(zsm.ZeroShardError) as e:
+        zsm.zero_shard_step_static(big.plan, 1, big.param.data_ptr(), big.master.data_ptr(),
+                                   big.exp_avg.data_ptr(), big.exp_avg_sq.data_ptr(),
+                                   [big.master.data_ptr()], step=3, max_grad_norm=1.0,
+                                   stream=s, **HP)
+    assert e.value.code == zsm.ZS_EINVAL and "scratch" in str(e.value)
+    torch.cuda.synchronize()
+    log("  2 clipped steps bit-identical at the limit; one tile more refused")
+    ref.close()
+    big.close()
